@@ -1,0 +1,149 @@
+"""fp64 CPU oracle for softmax attention (ctypes binding of attn_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may use it.  The GPU library never imports it, and this
+package never imports the GPU library.
+
+The definition it computes, with the page citations, is in attn_oracle.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB = os.path.join(_HERE, "libattn_oracle.so")
+
+BF16, F32, F64 = 0, 1, 2
+DOT, RBF = 0, 1
+
+_default = None
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle C source with gcc (-O2 -fopenmp, no fast-math)."""
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                        "-Wall", "-Wextra", "-I", _HERE, "-o", tmp, src, "-lm"], check=True)
+        os.replace(tmp, out)
+    return out
+
+
+def bind(path: str):
+    """Load an oracle shared library built by build(); returns a handle for attn(lib=...)."""
+    return _bind(path)
+
+
+def _bind(path: str):
+    lib = ctypes.CDLL(path)
+    vp, dp, llp = ctypes.c_void_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong)
+    lib.oracle_attn_rows.restype = ctypes.c_int
+    lib.oracle_attn_rows.argtypes = [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        vp, vp, vp, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, dp,
+        ctypes.c_longlong, llp, dp, dp, dp, ctypes.c_int]
+    lib.oracle_visible.restype = ctypes.c_int
+    lib.oracle_visible.argtypes = [ctypes.c_int] * 7
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = [ctypes.c_int]
+    return lib
+
+
+def _load():
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        _default = _bind(_LIB)
+    return _default
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.float64:
+        return F64
+    raise TypeError(f"oracle: unsupported element type {a.dtype}")
+
+
+def visible(L: int, S: int, causal: bool, window: int, n_reg: int, i: int, j: int, lib=None) -> bool:
+    return bool((lib or _load()).oracle_visible(L, S, int(causal), window, n_reg, i, j))
+
+
+def num_threads(threads: int = 0, lib=None) -> int:
+    return (lib or _load()).oracle_num_threads(threads)
+
+
+def attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, mode: str = "dot", scale: Optional[float] = None,
+         gamma: float = 0.0, causal: bool = False, window: int = 0, n_reg: int = 0,
+         sink: Optional[np.ndarray] = None, rows: Optional[Sequence[int]] = None,
+         want_p: bool = False, threads: int = 0, lib=None):
+    """Attention rows in fp64.
+
+    q (N,Hq,L,E), k and v (N,Hkv,S,E): uint16 (bf16 bits), float32 or float64,
+    all the same type.  rows: flat indices (n*Hq+h)*L+i, or None for all rows.
+    Returns (o, lse[, p]): o has shape (N,Hq,L,E) when rows is None, else
+    (len(rows), E); lse matches without E; p has S columns.
+    lib: a handle from bind() to use instead of the default build.
+    """
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    dt = _dtype_code(q)
+    if _dtype_code(k) != dt or _dtype_code(v) != dt:
+        raise TypeError("oracle: q, k, v must share one element type")
+    N, Hq, L, E = q.shape
+    Nk, Hkv, S, Ek = k.shape
+    if v.shape != k.shape or Nk != N or Ek != E:
+        raise ValueError("oracle: shape mismatch")
+    if scale is None:
+        scale = 1.0 / np.sqrt(E)
+    md = {"dot": DOT, "rbf": RBF}[mode]
+    sk = None
+    if sink is not None:
+        sk = np.ascontiguousarray(np.asarray(sink, dtype=np.float64).reshape(-1))
+        if sk.shape[0] != Hq:
+            raise ValueError("oracle: sink must hold Hq values")
+    if rows is None:
+        nrows = N * Hq * L
+        rptr = None
+        out_shape = (N, Hq, L)
+    else:
+        rr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+        nrows = rr.shape[0]
+        rptr = rr.ctypes.data_as(ctypes.POINTER(ctypes.c_longlong))
+        out_shape = (nrows,)
+    o = np.empty((nrows, E), dtype=np.float64)
+    lse = np.empty(nrows, dtype=np.float64)
+    p = np.empty((nrows, S), dtype=np.float64) if want_p else None
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = (lib or _load()).oracle_attn_rows(
+        dt, N, Hq, Hkv, L, S, E,
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, md, float(scale), float(gamma),
+        int(bool(causal)), int(window), int(n_reg),
+        sk.ctypes.data_as(dp) if sk is not None else None,
+        nrows, rptr, o.ctypes.data_as(dp), lse.ctypes.data_as(dp),
+        p.ctypes.data_as(dp) if p is not None else None, int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_rows failed with code {rc}")
+    o = o.reshape(out_shape + (E,))
+    lse = lse.reshape(out_shape)
+    if want_p:
+        return o, lse, p.reshape(out_shape + (S,))
+    return o, lse
+
+
+def attn_workload(inp, rows: Optional[Sequence[int]] = None, want_p: bool = False, threads: int = 0):
+    """Run the oracle on a workloads.gen.Inputs bundle (same flags as its workload)."""
+    w = inp.workload
+    return attn(inp.q, inp.k, inp.v, mode=w.mode, scale=w.scale, gamma=w.gamma, causal=w.causal,
+                window=w.window, n_reg=w.n_reg, sink=inp.sink, rows=rows, want_p=want_p, threads=threads)

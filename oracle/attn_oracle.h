@@ -1,0 +1,79 @@
+/*
+ * attn_oracle.h -- fp64 CPU oracle for softmax attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the slow, plain reference that the GPU
+ * library is checked against.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load it; the GPU library never includes,
+ * links or calls anything here, and nothing here includes the GPU library.
+ *
+ * What it computes (per output row, all in double precision):
+ *
+ *   logits   dot: l_ij = scale * sum_e q_ie k_je
+ *                 ("SDPA란 무엇인가?" section 1, the Attention equation with
+ *                 scale in place of 1/sqrt(E); "어텐션 메커니즘" section 2)
+ *            rbf: l_ij = -gamma * sum_e (q_ie - k_je)^2
+ *                 (RBF-attention digest, section details paragraph 2: the
+ *                 Euclidean distance form, written out before any folding)
+ *   bias     z_ij = l_ij if the pair is visible, else -inf
+ *                 (SDPA page section 1: B holds 0 or -inf; "어텐션 메커니즘"
+ *                 section 5: causal masking adds -inf above the diagonal)
+ *   softmax  M_i = max(max_j z_ij, s_h if a sink is given)
+ *            D_i = sum_j exp(z_ij - M_i) + [sink] exp(s_h - M_i)
+ *            p_ij = exp(z_ij - M_i) / D_i,  O_i = sum_j p_ij v_j,
+ *            LSE_i = M_i + ln D_i
+ *                 ("어텐션 메커니즘" section 2: row-wise softmax, outputs are
+ *                 convex combinations of V; "Attention Sink" section 4.2: the
+ *                 per-head sink logit sits in the denominator and its mass
+ *                 takes no part in the value sum)
+ *   empty    a row with no visible key and no sink gives O_i = 0 and
+ *            LSE_i = -inf (SDPA page section 4: the math backend returns 0,
+ *            not NaN, for a fully masked row)
+ *
+ * Visibility of key j for query i, with off = S - n_reg - L:
+ *   j < n_reg (register token, RBF digest paragraph 4)      -> visible
+ *   otherwise r = j - n_reg, i' = i + off (bottom-right alignment, SDPA page
+ *   section 4 pitfall 3), visible iff (!causal || r <= i') and
+ *   (window <= 0 || i' - r < window).
+ *
+ * GQA: query head h reads key/value head h / (Hq / Hkv) (SDPA page section 5:
+ * several query heads share one key/value head, in contiguous groups).
+ *
+ * Layouts: q (N,Hq,L,E), k and v (N,Hkv,S,E), row-major, E innermost.
+ * Element type given by `dtype`: bf16 bit patterns (uint16), float32 or
+ * float64; every element is widened exactly to double before use.
+ */
+#ifndef ATTN_ORACLE_H
+#define ATTN_ORACLE_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORACLE_BF16 = 0, ORACLE_F32 = 1, ORACLE_F64 = 2 };
+enum { ORACLE_DOT = 0, ORACLE_RBF = 1 };
+
+/* Returns 1 if key j is visible to query i under the rule above, else 0. */
+int oracle_visible(int L, int S, int causal, int window, int n_reg, int i, int j);
+
+/*
+ * Computes `nrows` output rows.  rows[r] is the flat row index
+ * (n*Hq + h)*L + i; rows == NULL means every row, in order (nrows must then
+ * equal N*Hq*L).  Outputs: o[r*E + e], lse[r]; p (may be NULL) receives the
+ * attention weights p[r*S + j].  sink (may be NULL) holds Hq logits.
+ * threads <= 0 uses the OpenMP default.  Returns 0, or a negative value for
+ * an invalid argument (nothing is written then).
+ */
+int oracle_attn_rows(int dtype, int N, int Hq, int Hkv, int L, int S, int E,
+                     const void* q, const void* k, const void* v,
+                     int mode, double scale, double gamma,
+                     int causal, int window, int n_reg, const double* sink,
+                     long long nrows, const long long* rows,
+                     double* o, double* lse, double* p, int threads);
+
+/* Number of OpenMP threads oracle_attn_rows uses for a given `threads`. */
+int oracle_num_threads(int threads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

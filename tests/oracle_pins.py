@@ -1,0 +1,444 @@
+"""Pins for the fp64 oracle: checks against what the pages and the mathematics fix.
+
+Every pin takes an oracle library handle (``lib``) and raises AssertionError if
+the oracle disagrees.  test_oracle_pins.py runs them on the real oracle;
+test_oracle_mutants.py runs them on copies of the oracle with planted mistakes
+and requires each mistake to be caught by at least one pin.
+
+Independent references used here: torch.nn.functional.scaled_dot_product_attention
+in float64 with an explicit bottom-right boolean mask (the library routine the
+SDPA page compares against, its section 1 and section 4 pitfall 3), torch.cdist
+for the RBF distance (RBF digest, paragraph 2), closed forms, invariants and two
+values printed on the pages (tests/golden/).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _qkv(seed, N, Hq, Hkv, L, S, E, dtype=np.float64):
+    r = _rng(seed)
+    q = r.standard_normal((N, Hq, L, E)).astype(dtype)
+    k = r.standard_normal((N, Hkv, S, E)).astype(dtype)
+    v = r.standard_normal((N, Hkv, S, E)).astype(dtype)
+    return q, k, v
+
+
+def _torch_mask(L, S, causal, window):
+    """Bottom-right causal / window band built from torch.tril / torch.triu (True = attend)."""
+    m = torch.ones(L, S, dtype=torch.bool)
+    if causal:
+        m = torch.tril(m, diagonal=S - L)
+    if window > 0:
+        m = m & torch.triu(torch.ones(L, S, dtype=torch.bool), diagonal=S - L - window + 1)
+    return m
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    err = np.where(both_inf, 0.0, np.abs(a - b))
+    assert np.all(np.isfinite(err)), f"{what}: non-finite mismatch"
+    m = float(err.max()) if err.size else 0.0
+    assert m <= tol, f"{what}: max abs err {m:.3e} > {tol:.1e}"
+
+
+def _bitwise(a, b, what):
+    assert np.array_equal(np.asarray(a).view(np.uint64), np.asarray(b).view(np.uint64)), f"{what}: not bitwise equal"
+
+
+# --------------------------------------------------------------------------- dot mode vs library
+
+
+DOT_CASES = [
+    # N, Hq, Hkv, L, S, E, causal, window
+    (2, 3, 3, 5, 5, 8, False, 0),
+    (1, 4, 2, 7, 11, 16, True, 0),
+    (2, 2, 1, 9, 9, 4, True, 0),
+    (1, 2, 2, 6, 13, 8, True, 4),
+    (1, 6, 3, 1, 10, 8, True, 0),
+]
+
+
+def pin_dot_matches_torch_sdpa(lib):
+    for c, (N, Hq, Hkv, L, S, E, causal, window) in enumerate(DOT_CASES):
+        q, k, v = _qkv(100 + c, N, Hq, Hkv, L, S, E)
+        scale = 0.7 / math.sqrt(E)
+        o, lse = oracle.attn(q, k, v, scale=scale, causal=causal, window=window, lib=lib)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        mask = _torch_mask(L, S, causal, window)
+        ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale,
+                                             enable_gqa=(Hq != Hkv)).numpy()
+        _close(o, ref, 1e-12, f"dot case {c} O")
+        kr = tk.repeat_interleave(Hq // Hkv, dim=1)
+        logits = (tq @ kr.transpose(-1, -2)) * scale
+        lref = torch.logsumexp(logits.masked_fill(~mask, float("-inf")), dim=-1).numpy()
+        _close(lse, lref, 1e-12, f"dot case {c} LSE")
+
+
+def pin_causal_lower_right_library_mask(lib):
+    """The bottom-right rule equals torch's causal_lower_right bias, named on the SDPA page."""
+    from torch.nn.attention.bias import causal_lower_right
+    for (L, S) in [(1, 6), (3, 5), (4, 4), (2, 9)]:
+        dense = causal_lower_right(L, S)._materialize().numpy()
+        mine = np.array([[oracle.visible(L, S, True, 0, 0, i, j, lib=lib) for j in range(S)] for i in range(L)])
+        assert np.array_equal(dense, mine), f"visibility L={L} S={S} differs from causal_lower_right"
+
+
+# --------------------------------------------------------------------------- rbf mode
+
+
+RBF_CASES = [
+    (1, 2, 2, 6, 6, 8, True, 0, 0),
+    (2, 4, 2, 5, 9, 4, True, 0, 2),
+    (1, 3, 1, 7, 7, 16, False, 0, 1),
+    (1, 2, 2, 8, 12, 8, True, 3, 2),
+]
+
+
+def pin_rbf_matches_cdist(lib):
+    gamma = 0.3
+    for c, (N, Hq, Hkv, L, S, E, causal, window, n_reg) in enumerate(RBF_CASES):
+        q, k, v = _qkv(200 + c, N, Hq, Hkv, L, S, E)
+        o, lse = oracle.attn(q, k, v, mode="rbf", gamma=gamma, causal=causal, window=window,
+                             n_reg=n_reg, lib=lib)
+        tq = torch.from_numpy(q)
+        tk = torch.from_numpy(k).repeat_interleave(Hq // Hkv, dim=1)
+        tv = torch.from_numpy(v).repeat_interleave(Hq // Hkv, dim=1)
+        d2 = torch.cdist(tq, tk, compute_mode="donot_use_mm_for_euclid_dist") ** 2
+        mask = torch.ones(L, S, dtype=torch.bool)
+        mask[:, n_reg:] = _torch_mask(L, S - n_reg, causal, window)
+        z = (-gamma * d2).masked_fill(~mask, float("-inf"))
+        ref = (torch.softmax(z, dim=-1) @ tv).numpy()
+        _close(o, ref, 1e-12, f"rbf case {c} O")
+        _close(lse, torch.logsumexp(z, dim=-1).numpy(), 1e-11, f"rbf case {c} LSE")
+
+
+def pin_rbf_tiny_loops(lib):
+    """Brute force in plain Python loops on a 2-query, 3-key, E=2 problem."""
+    q = np.array([[[[0.5, -1.0], [2.0, 0.25]]]])
+    k = np.array([[[[1.0, 0.0], [-0.5, 0.5], [0.0, 2.0]]]])
+    v = np.array([[[[1.0, 2.0], [3.0, -1.0], [0.5, 0.5]]]])
+    g = 0.7
+    o, lse = oracle.attn(q, k, v, mode="rbf", gamma=g, lib=lib)
+    for i in range(2):
+        w = []
+        for j in range(3):
+            d = sum((q[0, 0, i, e] - k[0, 0, j, e]) ** 2 for e in range(2))
+            w.append(math.exp(-g * d))
+        tot = sum(w)
+        for e in range(2):
+            ref = sum(w[j] * v[0, 0, j, e] for j in range(3)) / tot
+            assert abs(o[0, 0, i, e] - ref) < 1e-14, "rbf tiny O"
+        assert abs(lse[0, 0, i] - math.log(tot)) < 1e-14, "rbf tiny LSE"
+
+
+def pin_rbf_fold_identity(lib):
+    """Folded logits gamma*(2 q.k - |k|^2) give the same O; LSE differs by exactly gamma*|q|^2."""
+    gamma = 0.25
+    N, H, L, S, E = 1, 2, 6, 6, 8
+    q, k, v = _qkv(300, N, H, H, L, S, E)
+    o, lse = oracle.attn(q, k, v, mode="rbf", gamma=gamma, causal=True, lib=lib)
+    zf = gamma * (2.0 * np.einsum("nhie,nhje->nhij", q, k) - np.sum(k * k, -1)[:, :, None, :])
+    mask = np.tril(np.ones((L, S), bool))
+    zf = np.where(mask, zf, -np.inf)
+    mx = zf.max(-1, keepdims=True)
+    w = np.exp(zf - mx)
+    of = np.einsum("nhij,nhje->nhie", w / w.sum(-1, keepdims=True), v)
+    lse_fold = (mx[..., 0] + np.log(w.sum(-1)))
+    _close(o, of, 1e-12, "fold O")
+    _close(lse, lse_fold - gamma * np.sum(q * q, -1), 1e-11, "fold LSE")
+
+
+def pin_rbf_translation_invariance(lib):
+    gamma = 0.2
+    q, k, v = _qkv(310, 1, 2, 1, 5, 7, 8)
+    t = _rng(311).standard_normal(8)
+    o1, l1 = oracle.attn(q, k, v, mode="rbf", gamma=gamma, causal=True, lib=lib)
+    o2, l2 = oracle.attn(q + t, k + t, v, mode="rbf", gamma=gamma, causal=True, lib=lib)
+    _close(o1, o2, 1e-12, "rbf translation O")
+    _close(l1, l2, 1e-11, "rbf translation LSE")
+
+
+def pin_rbf_huge_keys_fall_to_registers(lib):
+    """All real keys very far away: the output is the mean of the register values."""
+    gamma = 0.125
+    N, H, L, S_real, E, n_reg = 1, 2, 4, 6, 8, 3
+    r = _rng(320)
+    q = r.standard_normal((N, H, L, E))
+    k = r.standard_normal((N, H, n_reg + S_real, E))
+    k[:, :, :n_reg] = 0.0
+    k[:, :, n_reg:] *= 1e3
+    v = r.standard_normal((N, H, n_reg + S_real, E))
+    o, _ = oracle.attn(q, k, v, mode="rbf", gamma=gamma, causal=True, n_reg=n_reg, lib=lib)
+    ref = np.broadcast_to(v[:, :, None, :n_reg].mean(axis=3), o.shape)
+    _close(o, ref, 1e-12, "registers absorb everything")
+
+
+# --------------------------------------------------------------------------- sink
+
+
+def pin_sink_minus_inf_is_no_sink(lib):
+    q, k, v = _qkv(400, 1, 4, 2, 6, 9, 8)
+    a = oracle.attn(q, k, v, causal=True, lib=lib)
+    b = oracle.attn(q, k, v, causal=True, sink=np.full(4, -np.inf), lib=lib)
+    _bitwise(a[0], b[0], "sink=-inf O")
+    _bitwise(a[1], b[1], "sink=-inf LSE")
+
+
+def pin_sink_closed_form(lib):
+    """O_sink = O * sigmoid(LSE - s), LSE_sink = logaddexp(LSE, s)."""
+    for mode, gamma in (("dot", 0.0), ("rbf", 0.2)):
+        q, k, v = _qkv(410, 2, 4, 2, 6, 8, 8)
+        s = _rng(411).standard_normal(4) * 2.0
+        o, l = oracle.attn(q, k, v, mode=mode, gamma=gamma, causal=True, window=4, lib=lib)
+        os_, ls = oracle.attn(q, k, v, mode=mode, gamma=gamma, causal=True, window=4, sink=s, lib=lib)
+        sh = s[None, :, None]
+        att = 1.0 / (1.0 + np.exp(sh - l))
+        _close(os_, o * att[..., None], 1e-12, f"{mode} sink attenuation O")
+        _close(ls, np.logaddexp(l, sh), 1e-12, f"{mode} sink LSE")
+
+
+def pin_zero_sink_is_zero_token(lib):
+    """Sink logit 0 in dot mode == one extra always-visible key with k = 0 and v = 0."""
+    N, Hq, Hkv, L, S, E = 1, 4, 2, 5, 7, 8
+    q, k, v = _qkv(420, N, Hq, Hkv, L, S, E)
+    k0 = np.concatenate([np.zeros((N, Hkv, 1, E)), k], axis=2)
+    v0 = np.concatenate([np.zeros((N, Hkv, 1, E)), v], axis=2)
+    for causal in (False, True):
+        a = oracle.attn(q, k, v, causal=causal, sink=np.zeros(Hq), lib=lib)
+        b = oracle.attn(q, k0, v0, causal=causal, n_reg=1, lib=lib)
+        _close(a[0], b[0], 1e-12, "zero sink O")
+        _close(a[1], b[1], 1e-12, "zero sink LSE")
+
+
+def pin_row_sums(lib):
+    q, k, v = _qkv(430, 1, 2, 2, 6, 8, 8)
+    s = np.array([0.5, -1.5])
+    _, l, p = oracle.attn(q, k, v, causal=True, want_p=True, lib=lib)
+    _close(p.sum(-1), np.ones_like(l), 1e-12, "row sums")
+    _, l, p = oracle.attn(q, k, v, causal=True, sink=s, want_p=True, lib=lib)
+    _close(p.sum(-1), 1.0 - np.exp(s[None, :, None] - l), 1e-12, "row sums with sink")
+
+
+# --------------------------------------------------------------------------- masking
+
+
+def _vis_matrix(L, S, causal, window, n_reg):
+    m = np.zeros((L, S), bool)
+    m[:, :n_reg] = True
+    if S > n_reg:
+        m[:, n_reg:] = _torch_mask(L, S - n_reg, causal, window).numpy()
+    return m
+
+
+def pin_masked_weights_exactly_zero(lib):
+    for (L, S, causal, window, n_reg) in [(6, 6, True, 0, 0), (4, 9, True, 3, 2), (5, 5, False, 0, 1)]:
+        q, k, v = _qkv(500, 1, 2, 2, L, S, 8)
+        _, _, p = oracle.attn(q, k, v, causal=causal, window=window, n_reg=n_reg, want_p=True, lib=lib)
+        vis = _vis_matrix(L, S, causal, window, n_reg)
+        assert np.all(p[..., ~vis] == 0.0), "masked weight not exactly zero"
+        assert np.all(p[..., vis] > 0.0), "visible weight not positive"
+
+
+def pin_invisible_values_do_not_matter(lib):
+    L = S = 7
+    q, k, v = _qkv(510, 1, 2, 2, L, S, 8)
+    v2 = v.copy()
+    v2[:, :, -1] += 1000.0  # last key: visible to the last query only
+    a, _ = oracle.attn(q, k, v, causal=True, lib=lib)
+    b, _ = oracle.attn(q, k, v2, causal=True, lib=lib)
+    _bitwise(a[:, :, :-1], b[:, :, :-1], "causal rows that cannot see the last key")
+    v3 = v.copy()
+    v3[:, :, 0] -= 1000.0  # first key: outside a width-3 window for queries 3..6
+    a, _ = oracle.attn(q, k, v, causal=True, window=3, lib=lib)
+    b, _ = oracle.attn(q, k, v3, causal=True, window=3, lib=lib)
+    _bitwise(a[:, :, 3:], b[:, :, 3:], "window rows that cannot see the first key")
+
+
+def pin_window_at_least_S_is_causal(lib):
+    q, k, v = _qkv(520, 1, 2, 1, 6, 10, 8)
+    a = oracle.attn(q, k, v, causal=True, lib=lib)
+    b = oracle.attn(q, k, v, causal=True, window=10, lib=lib)
+    _bitwise(a[0], b[0], "window>=S O")
+    _bitwise(a[1], b[1], "window>=S LSE")
+
+
+def pin_window_one_closed_form(lib):
+    """window=1: each query sees only its own aligned key, O_i = v_i', LSE_i = l_i,i'."""
+    L, S, E = 5, 8, 8
+    q, k, v = _qkv(530, 1, 2, 2, L, S, E)
+    scale = 0.3
+    o, lse = oracle.attn(q, k, v, scale=scale, causal=True, window=1, lib=lib)
+    off = S - L
+    for i in range(L):
+        _bitwise(o[:, :, i], v[:, :, i + off], f"window=1 O row {i}")
+        ref = scale * np.sum(q[:, :, i] * k[:, :, i + off], -1)
+        _close(lse[:, :, i], ref, 1e-13, f"window=1 LSE row {i}")
+
+
+def pin_decode_alignment_golden(lib):
+    with open(os.path.join(GOLDEN, "sdpa_causal_alignment_L1_S6.json")) as f:
+        g = json.load(f)
+    L, S = g["L"], g["S"]
+    br = [oracle.visible(L, S, True, 0, 0, 0, j, lib=lib) for j in range(S)]
+    assert all(br) == g["bottom_right_equals_unmasked_at_L1"], "L=1 bottom-right must see every key"
+    # top-left and bottom-right coincide when L == S: the first row of the S x S rule is the printed row
+    first = [oracle.visible(S, S, True, 0, 0, 0, j, lib=lib) for j in range(S)]
+    assert first == g["top_left_mask"][0], "L=S causal first row differs from the printed mask"
+    q, k, v = _qkv(540, 1, 2, 2, L, S, 8)
+    a = oracle.attn(q, k, v, causal=True, lib=lib)
+    b = oracle.attn(q, k, v, causal=False, lib=lib)
+    _bitwise(a[0], b[0], "L=1 causal vs unmasked")
+
+
+def pin_fully_masked_rows(lib):
+    """L > S with bottom-right causal: the first L-S rows see nothing -> O = 0, LSE = -inf (or s_h)."""
+    q, k, v = _qkv(550, 1, 2, 2, 4, 2, 8)
+    o, l = oracle.attn(q, k, v, causal=True, lib=lib)
+    assert np.all(o[:, :, :2] == 0.0) and np.all(np.isneginf(l[:, :, :2])), "empty rows"
+    assert np.all(np.isfinite(o[:, :, 2:])) and np.all(np.isfinite(l[:, :, 2:])), "non-empty rows"
+    s = np.array([0.3, -2.0])
+    o, l = oracle.attn(q, k, v, causal=True, sink=s, lib=lib)
+    assert np.all(o[:, :, :2] == 0.0), "empty rows with sink: O"
+    assert np.array_equal(l[0, :, 0], s) and np.array_equal(l[0, :, 1], s), "empty rows with sink: LSE = s_h"
+
+
+# --------------------------------------------------------------------------- uniform weights
+
+
+def pin_equal_logits_give_uniform_average(lib):
+    N, Hq, Hkv, L, S, E = 1, 4, 2, 6, 9, 8
+    _, k, v = _qkv(600, N, Hq, Hkv, L, S, E)
+    q = np.zeros((N, Hq, L, E))
+    o, lse = oracle.attn(q, k, v, causal=True, window=5, n_reg=1, lib=lib)
+    vis = _vis_matrix(L, S, True, 5, 1)
+    for h in range(Hq):
+        kh = h // (Hq // Hkv)
+        for i in range(L):
+            sel = v[0, kh, vis[i]]
+            _close(o[0, h, i], sel.mean(0), 1e-14, "uniform average")
+            _close(lse[0, h, i], math.log(sel.shape[0]), 1e-14, "LSE = ln n_visible")
+
+
+def pin_uniform_entropy_golden(lib):
+    with open(os.path.join(GOLDEN, "attention_uniform_entropy_n24.json")) as f:
+        g = json.load(f)
+    n = g["n"]
+    _, k, v = _qkv(610, 1, 1, 1, 3, n, 4)
+    q = np.zeros((1, 1, 3, 4))
+    _, _, p = oracle.attn(q, k, v, want_p=True, lib=lib)
+    ent = -np.sum(p * np.log(p), -1).mean()
+    assert round(float(ent), g["decimals"]) == g["mean_row_entropy"], f"entropy {ent}"
+
+
+# --------------------------------------------------------------------------- invariances
+
+
+def pin_shift_invariance(lib):
+    """Adding c_i to every logit of row i (via an extra coordinate) keeps O, shifts LSE by c_i."""
+    N, H, L, S, E = 1, 2, 5, 7, 8
+    q, k, v = _qkv(700, N, H, H, L, S, E)
+    scale = 0.4
+    c = _rng(701).standard_normal((N, H, L)) * 3.0
+    q2 = np.concatenate([q, (c / scale)[..., None]], -1)
+    k2 = np.concatenate([k, np.ones((N, H, S, 1))], -1)
+    o1, l1 = oracle.attn(q, k, v, scale=scale, causal=True, lib=lib)
+    v2 = v  # E_v stays 8: pad V to the new head size and drop the pad afterwards
+    v2p = np.concatenate([v2, np.zeros((N, H, S, 1))], -1)
+    o2, l2 = oracle.attn(q2, k2, v2p, scale=scale, causal=True, lib=lib)
+    _close(o2[..., :E], o1, 1e-12, "shifted O")
+    _close(l2, l1 + c, 1e-12, "shifted LSE")
+
+
+def pin_permutation_equivariance(lib):
+    N, H, L, S, E = 1, 2, 6, 8, 8
+    q, k, v = _qkv(710, N, H, H, L, S, E)
+    o, l = oracle.attn(q, k, v, lib=lib)
+    pq = _rng(711).permutation(L)
+    o2, l2 = oracle.attn(q[:, :, pq], k, v, lib=lib)
+    _bitwise(o2, o[:, :, pq], "query permutation O")
+    _bitwise(l2, l[:, :, pq], "query permutation LSE")
+    pk = _rng(712).permutation(S)
+    o3, l3 = oracle.attn(q, k[:, :, pk], v[:, :, pk], lib=lib)
+    _close(o3, o, 1e-12, "key permutation O")
+    _close(l3, l, 1e-12, "key permutation LSE")
+
+
+def pin_gqa_equals_repeat(lib):
+    N, Hq, Hkv, L, S, E = 2, 6, 2, 5, 8, 8
+    q, k, v = _qkv(720, N, Hq, Hkv, L, S, E)
+    G = Hq // Hkv
+    kr = np.repeat(k, G, axis=1)
+    vr = np.repeat(v, G, axis=1)
+    for mode in ("dot", "rbf"):
+        a = oracle.attn(q, k, v, mode=mode, gamma=0.2, causal=True, lib=lib)
+        b = oracle.attn(q, kr, vr, mode=mode, gamma=0.2, causal=True, lib=lib)
+        _bitwise(a[0], b[0], f"{mode} GQA O")
+        _bitwise(a[1], b[1], f"{mode} GQA LSE")
+
+
+def pin_convex_hull(lib):
+    q, k, v = _qkv(730, 1, 2, 2, 6, 6, 8)
+    o, _ = oracle.attn(q, k, v, causal=True, lib=lib)
+    for i in range(6):
+        lo = v[:, :, :i + 1].min(2)
+        hi = v[:, :, :i + 1].max(2)
+        assert np.all(o[:, :, i] >= lo - 1e-12) and np.all(o[:, :, i] <= hi + 1e-12), "outside hull"
+    o, _ = oracle.attn(q, k, v, causal=True, sink=np.array([1.0, 2.0]), lib=lib)
+    for i in range(6):
+        lo = np.minimum(v[:, :, :i + 1].min(2), 0.0)
+        hi = np.maximum(v[:, :, :i + 1].max(2), 0.0)
+        assert np.all(o[:, :, i] >= lo - 1e-12) and np.all(o[:, :, i] <= hi + 1e-12), "outside hull with 0"
+
+
+# --------------------------------------------------------------------------- input types, row sampling
+
+
+def pin_bf16_widening(lib):
+    r = _rng(800)
+    bits = [(r.standard_normal(s).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+            for s in ((1, 2, 5, 8), (1, 1, 7, 8), (1, 1, 7, 8))]
+    wide = [torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).double().numpy() for b in bits]
+    a = oracle.attn(*bits, causal=True, lib=lib)
+    b = oracle.attn(*wide, causal=True, lib=lib)
+    _bitwise(a[0], b[0], "bf16 O")
+    _bitwise(a[1], b[1], "bf16 LSE")
+
+
+def pin_f32_widening(lib):
+    q, k, v = _qkv(810, 1, 2, 1, 5, 7, 8, dtype=np.float32)
+    a = oracle.attn(q, k, v, mode="rbf", gamma=0.3, causal=True, lib=lib)
+    b = oracle.attn(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), mode="rbf",
+                    gamma=0.3, causal=True, lib=lib)
+    _bitwise(a[0], b[0], "f32 O")
+    _bitwise(a[1], b[1], "f32 LSE")
+
+
+def pin_row_sampling(lib):
+    q, k, v = _qkv(820, 2, 4, 2, 6, 9, 8)
+    s = np.array([0.1, -0.2, 0.3, 1.0])
+    full = oracle.attn(q, k, v, causal=True, window=4, sink=s, lib=lib)
+    rows = [0, 5, 13, 47, 22]
+    part = oracle.attn(q, k, v, causal=True, window=4, sink=s, rows=rows, lib=lib)
+    _bitwise(part[0], full[0].reshape(-1, 8)[rows], "sampled O")
+    _bitwise(part[1], full[1].reshape(-1)[rows], "sampled LSE")
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

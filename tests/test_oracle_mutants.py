@@ -1,0 +1,52 @@
+"""Planted mistakes in a copy of the oracle must each be caught by some pin.
+
+Each mutant is one plausible slip (a dropped term, a wrong sign or index, a
+transposed operand, an off-by-one in a mask).  The copy is compiled on the CPU
+into a temporary directory; the real oracle is untouched.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")
+
+MUTANTS = {
+    "gqa_index_modulo": ("const int kh = h / G;", "const int kh = h % Hkv;"),
+    "causal_top_left": ("((long long)S - n_reg - L);  /* bottom-right */", "0;"),
+    "window_off_by_one": ("if (window > 0 && ip - r >= window) return 0;",
+                          "if (window > 0 && ip - r > window) return 0;"),
+    "registers_masked": ("if (j < n_reg) return 1;                 /* register tokens: always visible */", ""),
+    "sink_dropped_from_denominator": ("if (sink) D += exp(sink[h] - M);", ""),
+    "sink_sign": ("if (sink) D += exp(sink[h] - M);", "if (sink) D += exp(-sink[h] - M);"),
+    "rbf_sign": ("return -gamma * acc;", "return gamma * acc;"),
+    "rbf_plus": ("double d = load_elem(dtype, q, qoff + e) - load_elem(dtype, k, koff + e);",
+                 "double d = load_elem(dtype, q, qoff + e) + load_elem(dtype, k, koff + e);"),
+    "scale_dropped": ("return scale * acc;", "return acc;"),
+    "key_row_reversed": ("z[j] = logit(dtype, q, qoff, k, (kvrow0 + j) * E, E, mode, scale, gamma);",
+                         "z[j] = logit(dtype, q, qoff, k, (kvrow0 + (S - 1 - j)) * E, E, mode, scale, gamma);"),
+    "head_dim_truncated": ("for (int e = 0; e < E; ++e) acc += load_elem", "for (int e = 0; e < E - 1; ++e) acc += load_elem"),
+    "lse_without_max": ("lse[r] = M + log(D);", "lse[r] = log(D);"),
+    "empty_row_nan": ("if (M == -INFINITY) {", "if (0) {"),
+    "bf16_shift": ("<< 16;", "<< 15;"),
+    "value_row_index": ("const size_t voff = (kvrow0 + j) * E;", "const size_t voff = (kvrow0 + (S - 1 - j)) * E;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    mpath = tmp_path / "attn_oracle_mutant.c"
+    mpath.write_text(src.replace(old, new))
+    lib = oracle.bind(oracle.build(force=True, src=str(mpath), out=str(tmp_path / "libmutant.so")))
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"

@@ -1,0 +1,100 @@
+"""The five synthetic attention workloads, as plain data.
+
+Each workload is one call of the attention forward (or decode) with the shapes,
+distributions and flags listed below.  Nothing here computes attention; this
+module only names sizes and flags so that the generator, the oracle, the tests
+and the benchmark agree on them.
+
+Sources (the pages): shapes Q (N,Hq,L,E) and K/V (N,H,S,E) follow the SDPA
+problem statement ("SDPA란 무엇인가?", section 1); the RBF logit and register
+tokens follow the RBF-attention digest ("Dot-Product Attention을 거리 기반
+RBF-Attention으로 교체한 실험기", section details paragraphs 2-4); the per-head
+sink logit follows "Attention Sink" section 4.2; the 100K+ token decode regime
+follows the SOCKET summary (results).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, replace
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str            # "bf16" or "f32": element type of Q, K, V and O
+    N: int                # batch
+    Hq: int               # query heads
+    Hkv: int              # key/value heads (Hq % Hkv == 0)
+    L: int                # query length
+    S_real: int           # real keys (registers not included)
+    E: int                # head dimension (E_v == E)
+    mode: str             # "dot" or "rbf"
+    scale: float          # dot mode logit scale (ignored in rbf mode)
+    gamma: float          # rbf mode gamma (ignored in dot mode)
+    causal: bool
+    window: int           # 0 = no window
+    n_reg: int            # register tokens prepended to K/V
+    sink: bool            # per-query-head sink logit present
+    decode: bool          # uses the split-K decode entry point (L == 1)
+    seed: int
+    k_dist: str = "normal"  # "normal" or "dir_lognormal"
+
+    @property
+    def S(self) -> int:
+        return self.S_real + self.n_reg
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+C1 = Workload("rbf_causal_f32_1x1x256x64", "f32", 1, 1, 1, 256, 256, 64,
+              "rbf", 1.0 / 8.0, 1.0 / 8.0, True, 0, 0, False, False, 1)
+C2 = Workload("dot_causal_bf16_4x16x2048x128", "bf16", 4, 16, 16, 2048, 2048, 128,
+              "dot", 1.0 / math.sqrt(128.0), 0.0, True, 0, 0, False, False, 2)
+C3 = Workload("rbf_causal_reg4_bf16_2x16x8192x64", "bf16", 2, 16, 16, 8192, 8192, 64,
+              "rbf", 1.0 / 8.0, 1.0 / 8.0, True, 0, 4, False, False, 3,
+              k_dist="dir_lognormal")
+C4 = Workload("sink_swa128_gqa64to8_bf16_1x8192x64", "bf16", 1, 64, 8, 8192, 8192, 64,
+              "dot", 1.0 / 8.0, 0.0, True, 128, 0, True, False, 4)
+C5 = Workload("decode_splitk_sink_bf16_8x32to8x131072x128", "bf16", 8, 32, 8, 1, 131072, 128,
+              "dot", 1.0 / math.sqrt(128.0), 0.0, True, 0, 0, True, True, 5)
+
+ALL = (C1, C2, C3, C4, C5)
+BY_NAME = {w.name: w for w in ALL}
+
+
+def visible_pairs_per_head(w: Workload) -> int:
+    """Count (query, key) pairs that the visibility rule lets through, per head.
+
+    Register keys are always visible; real key r is visible to query i (aligned
+    bottom-right, i' = i + S_real - L) iff (not causal or r <= i') and
+    (window <= 0 or i' - r < window).  Closed-form per query row.
+    """
+    total = 0
+    off = w.S_real - w.L
+    for i in range(w.L):
+        ip = i + off
+        hi = min(w.S_real - 1, ip) if w.causal else w.S_real - 1
+        lo = max(0, ip - w.window + 1) if w.window > 0 else 0
+        total += max(0, hi - lo + 1) + w.n_reg
+    return total
+
+
+def algorithmic_flops(w: Workload) -> float:
+    """4*E flops per visible pair (2E for q.k, 2E for p*v), times N*Hq heads."""
+    return 4.0 * w.E * visible_pairs_per_head(w) * w.N * w.Hq
+
+
+def algorithmic_bytes(w: Workload) -> float:
+    """Each tensor touched once: Q, K, V read, O written, LSE written, sink read."""
+    esz = 2 if w.dtype == "bf16" else 4
+    q = w.N * w.Hq * w.L * w.E * esz
+    kv = 2 * w.N * w.Hkv * w.S * w.E * esz
+    o = q
+    lse = w.N * w.Hq * w.L * 4
+    sink = w.Hq * 4 if w.sink else 0
+    return float(q + kv + o + lse + sink)
