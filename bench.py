@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--extras all|none]
+
+A step is one call of the library on one batch of synthetic inputs already
+resident in HBM.  The headline workload is the causal bf16 prefill
+N=4, H=16, L=S=2048, E=128 (dot_causal_bf16_4x16x2048x128); its value is
+TFLOP/s over the visible (query, key) pairs, 4*E flops each.  The other
+workloads are timed the same way and reported under "extras" (prefill in
+TFLOP/s, decode in HBM GB/s over the K/V bytes read once).
+
+The CPU baseline leg times the fp64 oracle on a bounded sample of rows of the
+headline workload, on this host's cores, and checks the GPU output on those
+rows against it.
+
+Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits with a
+message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from workloads import configs, gen  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "prefill TFLOP/s + decode HBM GB/s, as % of MI355X roofline, oracle-exact"
+
+KERNEL_FILES = {
+    "prefill_bf16": "softmax_attention_attn_amd/csrc/prefill_bf16.hip",
+    "prefill_f32": "softmax_attention_attn_amd/csrc/prefill_f32.hip",
+    "decode_bf16": "softmax_attention_attn_amd/csrc/decode_bf16.hip",
+}
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_of(w) -> str:
+    if w.decode:
+        return "decode_bf16"
+    return "prefill_bf16" if w.dtype == "bf16" else "prefill_f32"
+
+
+def source_sha(kernel: str) -> str:
+    with open(os.path.join(ROOT, KERNEL_FILES[kernel]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on this source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}__hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != source_sha(kernel):
+        return None
+    return float(m_b.group(1))
+
+
+def to_device(inp, torch, dev):
+    import numpy as np
+
+    def t(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+    sink = torch.from_numpy(inp.sink).to(dev) if inp.sink is not None else None
+    return t(inp.q), t(inp.k), t(inp.v), sink
+
+
+def time_workload(w, steps: int, warmup: int, rotate: int, torch, attn, keep_first_output=False):
+    """Average ms per call over `steps` back-to-back calls, inputs resident in HBM."""
+    dev = torch.device("cuda:0")
+    log(f"[bench] {w.name}: generating inputs")
+    t0 = time.time()
+    inp = gen.generate(w)
+    log(f"[bench] {w.name}: inputs ready in {time.time() - t0:.1f}s, copying to the GPU")
+    q, k, v, sink = to_device(inp, torch, dev)
+    sets = [(q, k, v)]
+    for _ in range(max(0, rotate - 1)):
+        sets.append((q.clone(), k.clone(), v.clone()))
+    outs = [(torch.empty_like(q), torch.empty((w.N, w.Hq, w.L), dtype=torch.float32, device=dev))
+            for _ in sets]
+    kw = dict(scale=w.scale, mode=w.mode, gamma=w.gamma, causal=w.causal, window=w.window, n_reg=w.n_reg,
+              sink=sink)
+    ws = None
+    if w.decode:
+        nbytes = attn.decode_workspace_bytes(w.N, w.Hq, w.Hkv, w.S, w.E, w.causal, w.window, w.n_reg)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+    def call(i):
+        qq, kk, vv = sets[i % len(sets)]
+        oo, ll = outs[i % len(outs)]
+        if w.decode:
+            attn.decode(qq, kk, vv, workspace=ws, out=oo, lse=ll, **kw)
+        else:
+            attn.fwd(qq, kk, vv, out=oo, lse=ll, **kw)
+
+    call(0)
+    torch.cuda.synchronize()
+    first = (outs[0][0].clone(), outs[0][1].clone()) if keep_first_output else None
+    for i in range(warmup):
+        call(i)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        call(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    return ms, inp, first
+
+
+def rate(w, ms: float):
+    if w.decode:
+        gbs = configs.algorithmic_bytes(w) / (ms * 1e-3) / 1e9
+        return {"value": gbs, "unit": "GB/s", "bound": "hbm", "peak": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS}
+    tf = configs.algorithmic_flops(w) / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    out = {"value": tf, "unit": "TFLOP/s", "bound": "mfma" if w.dtype == "bf16" else "alu", "peak": peak,
+           "frac": tf / peak}
+    gbs = configs.algorithmic_bytes(w) / (ms * 1e-3) / 1e9
+    out["hbm_GBps"] = gbs
+    out["hbm_frac"] = gbs / PEAK_HBM_GBS
+    return out
+
+
+def cpu_baseline(w, inp, o_gpu, lse_gpu, seconds: float):
+    """Time the fp64 oracle on a bounded row sample; compare the GPU rows with it."""
+    import numpy as np
+
+    import oracle
+    oracle.build(force=False)
+    threads = oracle.num_threads(0)
+    rng = np.random.default_rng(1234)
+    total = w.N * w.Hq * w.L
+    # probe the per-row cost, then size the sample to ~`seconds`
+    probe = np.sort(rng.choice(total, size=min(total, 4 * threads), replace=False))
+    t0 = time.perf_counter()
+    oracle.attn_workload(inp, rows=probe, threads=threads)
+    dt = max(time.perf_counter() - t0, 1e-6)
+    n = int(min(total, max(len(probe), len(probe) * seconds / dt)))
+    rows = np.sort(rng.choice(total, size=n, replace=False))
+    t0 = time.perf_counter()
+    o_ref, lse_ref = oracle.attn_workload(inp, rows=rows, threads=threads)
+    el = time.perf_counter() - t0
+    # algorithmic work of exactly these rows
+    off = w.S_real - w.L
+    i = rows % w.L
+    ip = i + off
+    hi = np.minimum(w.S_real - 1, ip) if w.causal else np.full_like(i, w.S_real - 1)
+    lo = np.maximum(0, ip - w.window + 1) if w.window > 0 else np.zeros_like(i)
+    pairs = float(np.maximum(0, hi - lo + 1).sum() + w.n_reg * len(rows))
+    flops = 4.0 * w.E * pairs
+    og = o_gpu.float().cpu().numpy().reshape(-1, w.E)[rows].astype(np.float64)
+    lg = lse_gpu.cpu().numpy().reshape(-1)[rows].astype(np.float64)
+    eo = float(np.abs(og - o_ref).max())
+    finite = np.isfinite(lse_ref)
+    el_lse = float(np.abs(lg[finite] - lse_ref[finite]).max()) if finite.any() else 0.0
+    tol = 2e-2 if w.dtype == "bf16" else 1e-4
+    base = {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {total} output rows of {w.name} (seeded uniform sample), "
+                      f"{pairs:.4g} visible pairs, {el:.1f}s wall, fp64, OpenMP over rows"}
+    parity = {"rows": len(rows), "max_abs_err_o": eo, "max_abs_err_lse": el_lse, "tol_o": tol,
+              "tol_lse": 1e-3, "pass": bool(eo <= tol and el_lse <= 1e-3)}
+    return base, parity
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=configs.C2.name, choices=sorted(configs.BY_NAME))
+    ap.add_argument("--extras", default="all", choices=["all", "none"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the attention kernels run on one GPU's share and nothing here spans GPUs.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import softmax_attention_attn_amd as attn
+    attn.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+
+    w = configs.BY_NAME[args.workload]
+    ms, inp, first = time_workload(w, args.steps, args.warmup, 1, torch, attn, keep_first_output=True)
+    r = rate(w, ms)
+    kern = kernel_of(w)
+    traffic = measured_traffic(kern, w.name)
+    result = {
+        "metric": METRIC,
+        "value": r["value"],
+        "unit": r["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded generator, workloads/gen.py)",
+        "config": {"workload": w.name, "N": w.N, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.L, "S": w.S, "E": w.E,
+                   "mode": w.mode, "causal": w.causal, "window": w.window, "n_reg": w.n_reg, "sink": w.sink,
+                   "decode": w.decode, "parallelism": "single GPU"},
+        "roofline": {"bound": r["bound"], "achieved": r["value"], "peak": r["peak"], "unit": r["unit"],
+                     "frac": r["frac"], "traffic": traffic, "kernel": kern,
+                     "algorithmic_per_launch": configs.algorithmic_bytes(w) if w.decode
+                     else configs.algorithmic_flops(w)},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline: timing the oracle on a row sample")
+        base, parity = cpu_baseline(w, inp, first[0], first[1], args.cpu_seconds)
+        result["cpu_baseline"] = base
+        result["parity"] = parity
+    del inp, first
+    if args.extras == "all":
+        extras = {}
+        for x in configs.ALL:
+            if x.name == w.name:
+                continue
+            rot = 3 if (not x.decode and configs.algorithmic_bytes(x) < 256e6 and x.name == configs.C4.name) else 1
+            xms, xinp, _ = time_workload(x, max(5, args.steps // 2), max(2, args.warmup // 2), rot, torch, attn)
+            del xinp
+            torch.cuda.empty_cache()
+            xr = rate(x, xms)
+            xr["ms"] = xms
+            xr["kernel"] = kernel_of(x)
+            xr["rotated_buffer_sets"] = rot
+            extras[x.name] = xr
+        result["extras"] = extras
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

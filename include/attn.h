@@ -1,0 +1,128 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) fused softmax-attention library.
+ *
+ * One operation, two entry points:
+ *
+ *   O = softmax(Z) V,  Z_ij = logit(q_i, k_j) + B_ij,  B_ij in {0, -inf}
+ *
+ * computed with a streaming (online) softmax so that the L x S matrix of
+ * logits never exists in memory.  The problem statement, argument names and
+ * tensor shapes follow "SDPA란 무엇인가?" (molayo1419.me) section 1: Q is
+ * (N, Hq, L, E), K and V are (N, H, S, E), B is an L x S matrix of 0 / -inf,
+ * and the scale is an explicit argument.  Variants:
+ *
+ *  - logits.  DOT: l_ij = scale * q_i . k_j ("어텐션 메커니즘", section 2).
+ *    RBF: l_ij = -gamma * |q_i - k_j|^2 (RBF-attention digest, section
+ *    details paragraph 2); the kernels evaluate it as gamma*(2 q.k - |k|^2),
+ *    dropping -gamma*|q_i|^2 by softmax shift invariance, with |k_j|^2 formed
+ *    on chip for each staged key tile (same digest, paragraph 3).  LSE is
+ *    still reported for the definition logits -gamma*|q-k|^2.
+ *  - visibility.  Keys j < n_reg are register tokens (RBF digest, paragraph
+ *    4): always visible.  Real key r = j - n_reg is visible to query i, with
+ *    i' = i + (S - n_reg - L) (bottom-right alignment, SDPA page section 4,
+ *    pitfall 3), iff (!causal || r <= i') and (window <= 0 || i' - r < window)
+ *    (sliding window, "어텐션 메커니즘" section 6 and "Attention Sink"
+ *    section 1).
+ *  - sink.  sink[h] (one logit per query head, "Attention Sink" section 4.2)
+ *    is added to the softmax denominator and contributes no value:
+ *    O_i = sum_j e^{Z_ij} v_j / (e^{s_h} + sum_j e^{Z_ij}); LSE includes it.
+ *  - GQA.  Query head h reads key/value head h / (Hq / Hkv) (SDPA page
+ *    section 5).
+ *  - empty rows.  A row with no visible key and no sink gives O = 0 and
+ *    LSE = -inf (SDPA page section 4: 0, never NaN).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or synchronises.  Work is enqueued on `stream`
+ *    (a hipStream_t; NULL = the default stream) and the call returns at once.
+ *  - Layouts are contiguous row-major with E innermost: q and o (N,Hq,L,E),
+ *    k and v (N,Hkv,S,E), lse (N,Hq,L) float32, sink (Hq) float32.
+ *  - q, k, v, o must be 16-byte aligned; lse and sink 4-byte aligned.
+ *  - Arguments are checked completely before any HIP call; on error nothing
+ *    is enqueued or written and a negative attn_status is returned.  The
+ *    library never substitutes a slower path for an unsupported case.
+ *  - attn_last_error() gives a message for the last failing call on the
+ *    calling thread.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = -2,       /* sizes inconsistent (Hq % Hkv, n_reg > S, decode with L != 1, ...) */
+  ATTN_ERR_DTYPE = -3,       /* unknown element type */
+  ATTN_ERR_UNSUPPORTED = -4, /* valid request outside what the kernels implement (E, window w/o causal, ...) */
+  ATTN_ERR_ALIGN = -5,       /* pointer misaligned */
+  ATTN_ERR_WORKSPACE = -6,   /* decode workspace NULL or too small */
+  ATTN_ERR_HIP = -7,         /* the HIP runtime reported an error at launch */
+  ATTN_ERR_ARG = -8          /* bad scalar argument (mode, non-finite scale/gamma, negative window, splits) */
+} attn_status;
+
+typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype;
+typedef enum { ATTN_MODE_DOT = 0, ATTN_MODE_RBF = 1 } attn_mode;
+
+/*
+ * attn_fwd -- prefill / general forward.
+ *   dt      element type of q, k, v, o (bf16: fp32 accumulation, P rounded to
+ *           bf16 for the PV product; f32: fp32 throughout)
+ *   N,Hq,Hkv,L,S,E  sizes; S counts the n_reg register rows; E in {64, 128}
+ *   scale   DOT logit scale (ignored for RBF); gamma  RBF width (ignored for DOT)
+ *   causal, window, n_reg  visibility as described above; window > 0 needs causal
+ *   sink    Hq logits (natural-log units, like the logits) or NULL
+ *   o, lse  outputs; o has element type dt, lse float32 (natural log)
+ * Sizes with N*Hq*L == 0 succeed without launching anything.
+ */
+int attn_fwd(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E,
+             const void* q, const void* k, const void* v,
+             attn_mode mode, float scale, float gamma,
+             int causal, int window, int n_reg, const float* sink,
+             void* o, float* lse, void* stream);
+
+/*
+ * attn_decode -- one query token per sequence (L must be 1) against a long
+ * key/value cache, split along the keys (flash-decode, named in the SOCKET
+ * summary, contributions 2): each split writes a partial (running max,
+ * running sum, unnormalised output) to `workspace`, and a second kernel merges
+ * the partials with log-sum-exp weights and the sink.  Same arguments and
+ * semantics as attn_fwd with L = 1 (so causal only matters for the window),
+ * plus:
+ *   num_splits       0 = choose from the sizes; otherwise the exact count
+ *                    (results are identical up to rounding for any count)
+ *   workspace, workspace_bytes  device scratch of at least
+ *                    attn_decode_workspace_bytes(...) bytes, 16-byte aligned,
+ *                    owned by the caller; its contents on entry do not matter.
+ * Only bf16 is implemented (dt = ATTN_F32 returns ATTN_ERR_UNSUPPORTED).
+ */
+int attn_decode(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E,
+                const void* q, const void* k, const void* v,
+                attn_mode mode, float scale, float gamma,
+                int causal, int window, int n_reg, const float* sink,
+                void* o, float* lse,
+                int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Split count attn_decode uses for these sizes when num_splits == 0
+ * (a pure function of its arguments); negative attn_status on bad sizes. */
+int attn_decode_num_splits(int N, int Hq, int Hkv, int S, int E, int causal, int window, int n_reg);
+
+/* Workspace bytes attn_decode needs for these sizes and num_splits
+ * (0 = the automatic count); 0 if the sizes are invalid. */
+size_t attn_decode_workspace_bytes(int N, int Hq, int Hkv, int S, int E, int causal, int window,
+                                   int n_reg, int num_splits);
+
+/* Static text for a status code. */
+const char* attn_status_string(int status);
+
+/* Message describing the last failing call on this thread ("" if none). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATTN_H */

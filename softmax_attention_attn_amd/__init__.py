@@ -1,0 +1,173 @@
+"""Python binding of libattn (fused softmax attention for MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of include/attn.h.  PyTorch supplies device memory
+and the current stream.  There is no fallback path: if libattn.so is missing
+or a call is rejected, an exception is raised.
+
+    o, lse = fwd(q, k, v, scale=..., mode="dot"|"rbf", gamma=..., causal=...,
+                 window=..., n_reg=..., sink=...)
+    o, lse = decode(q, k, v, ..., num_splits=0)
+
+q (N, Hq, L, E), k and v (N, Hkv, S, E), all bf16 (or all float32 for fwd),
+contiguous, on one GPU; sink (Hq,) float32.  Returns o like q and lse
+(N, Hq, L) float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+ATTN_OK = 0
+STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_DTYPE",
+          -4: "ATTN_ERR_UNSUPPORTED", -5: "ATTN_ERR_ALIGN", -6: "ATTN_ERR_WORKSPACE",
+          -7: "ATTN_ERR_HIP", -8: "ATTN_ERR_ARG"}
+BF16, F32 = 0, 1
+MODES = {"dot": 0, "rbf": 1}
+
+EXPORTS = ("attn_fwd", "attn_decode", "attn_decode_num_splits", "attn_decode_workspace_bytes",
+           "attn_status_string", "attn_last_error")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libattn.so (built in-tree by softmax_attention_attn_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run `python -m softmax_attention_attn_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        I, F, P, Z = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+        lib.attn_fwd.restype = I
+        lib.attn_fwd.argtypes = [I, I, I, I, I, I, I, P, P, P, I, F, F, I, I, I, P, P, P, P]
+        lib.attn_decode.restype = I
+        lib.attn_decode.argtypes = [I, I, I, I, I, I, I, P, P, P, I, F, F, I, I, I, P, P, P, I, P, Z, P]
+        lib.attn_decode_num_splits.restype = I
+        lib.attn_decode_num_splits.argtypes = [I] * 8
+        lib.attn_decode_workspace_bytes.restype = Z
+        lib.attn_decode_workspace_bytes.argtypes = [I] * 9
+        lib.attn_status_string.restype = ctypes.c_char_p
+        lib.attn_status_string.argtypes = [I]
+        lib.attn_last_error.restype = ctypes.c_char_p
+        lib.attn_last_error.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != ATTN_OK:
+        raise AttnError(rc, load().attn_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported element type {t.dtype} (bfloat16 or float32)")
+
+
+def _common(q, k, v, sink, scale, mode, gamma):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D, got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one element type")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on one device")
+    N, Hq, L, E = q.shape
+    if k.shape != v.shape:
+        raise ValueError(f"k {tuple(k.shape)} and v {tuple(v.shape)} must have the same shape")
+    if k.shape[0] != N or k.shape[3] != E:
+        raise ValueError(f"k {tuple(k.shape)} does not match q {tuple(q.shape)} in batch or head dimension")
+    if sink is not None:
+        if sink.dtype != torch.float32 or sink.device != q.device or not sink.is_contiguous() or sink.numel() != Hq:
+            raise ValueError("sink must be a contiguous float32 tensor of Hq values on q's device")
+    if mode not in MODES:
+        raise ValueError(f"mode must be 'dot' or 'rbf', got {mode!r}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(E)
+    if gamma is None:
+        gamma = 0.0
+    return N, Hq, k.shape[1], L, k.shape[2], E, float(scale), float(gamma)
+
+
+def _stream(dev: torch.device, stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    return s.cuda_stream
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
+        mode: str = "dot", gamma: Optional[float] = None, causal: bool = False, window: int = 0,
+        n_reg: int = 0, sink: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+        lse: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention forward through attn_fwd; returns (o, lse)."""
+    N, Hq, Hkv, L, S, E, scale, gamma = _common(q, k, v, sink, scale, mode, gamma)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((N, Hq, L), dtype=torch.float32, device=q.device)
+    lib = load()
+    rc = lib.attn_fwd(_dtype_code(q), N, Hq, Hkv, L, S, E, _ptr(q), _ptr(k), _ptr(v), MODES[mode],
+                      scale, gamma, int(bool(causal)), int(window), int(n_reg), _ptr(sink),
+                      _ptr(out), _ptr(lse), _stream(q.device, stream))
+    _check(rc)
+    return out, lse
+
+
+def decode_num_splits(N: int, Hq: int, Hkv: int, S: int, E: int, causal: bool = True, window: int = 0,
+                      n_reg: int = 0) -> int:
+    r = load().attn_decode_num_splits(N, Hq, Hkv, S, E, int(bool(causal)), window, n_reg)
+    _check(min(r, 0))
+    return r
+
+
+def decode_workspace_bytes(N: int, Hq: int, Hkv: int, S: int, E: int, causal: bool = True, window: int = 0,
+                           n_reg: int = 0, num_splits: int = 0) -> int:
+    return int(load().attn_decode_workspace_bytes(N, Hq, Hkv, S, E, int(bool(causal)), window, n_reg,
+                                                  num_splits))
+
+
+def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
+           mode: str = "dot", gamma: Optional[float] = None, causal: bool = True, window: int = 0,
+           n_reg: int = 0, sink: Optional[torch.Tensor] = None, num_splits: int = 0,
+           workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-K decode (q has L == 1) through attn_decode; returns (o, lse)."""
+    N, Hq, Hkv, L, S, E, scale, gamma = _common(q, k, v, sink, scale, mode, gamma)
+    need = decode_workspace_bytes(N, Hq, Hkv, S, E, causal, window, n_reg, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((N, Hq, L), dtype=torch.float32, device=q.device)
+    lib = load()
+    rc = lib.attn_decode(_dtype_code(q), N, Hq, Hkv, L, S, E, _ptr(q), _ptr(k), _ptr(v), MODES[mode],
+                         scale, gamma, int(bool(causal)), int(window), int(n_reg), _ptr(sink),
+                         _ptr(out), _ptr(lse), int(num_splits), _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _stream(q.device, stream))
+    _check(rc)
+    return out, lse

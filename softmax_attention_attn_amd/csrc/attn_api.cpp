@@ -1,0 +1,198 @@
+// attn_api.cpp -- the C ABI declared in include/attn.h.
+//
+// Every argument is checked before the first HIP call, so that misuse returns
+// a status (and a message) without touching the GPU; the error lessons follow
+// the SDPA page's table of errors (loud failure for head-count mismatches,
+// unsupported requests and bad arguments, never a silent fallback).
+#include "attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return ATTN_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr long long kMaxElems = 1LL << 40;  // per tensor; keeps every offset in int64 comfortably
+constexpr long long kMaxGrid = 0x7fffffffLL;
+
+// Checks shared by attn_fwd and attn_decode.  Returns ATTN_OK or an error.
+int check_args(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, const void* q, const void* k,
+               const void* v, attn_mode mode, float scale, float gamma, int causal, int window, int n_reg,
+               const float* sink, const void* o, const float* lse) {
+  (void)causal;
+  if (dt != ATTN_BF16 && dt != ATTN_F32) return fail(ATTN_ERR_DTYPE, "unknown dtype %d", (int)dt);
+  if (mode != ATTN_MODE_DOT && mode != ATTN_MODE_RBF) return fail(ATTN_ERR_ARG, "unknown mode %d", (int)mode);
+  if (N < 0 || L < 0 || S < 0) return fail(ATTN_ERR_SHAPE, "negative size (N=%d L=%d S=%d)", N, L, S);
+  if (Hq <= 0 || Hkv <= 0) return fail(ATTN_ERR_SHAPE, "head counts must be positive (Hq=%d Hkv=%d)", Hq, Hkv);
+  if (Hq % Hkv != 0)
+    return fail(ATTN_ERR_SHAPE, "query heads (%d) must be a multiple of key/value heads (%d)", Hq, Hkv);
+  if (n_reg < 0 || n_reg > S) return fail(ATTN_ERR_SHAPE, "n_reg=%d outside [0, S=%d]", n_reg, S);
+  if (window < 0) return fail(ATTN_ERR_ARG, "window=%d must be >= 0", window);
+  if (window > 0 && !causal) return fail(ATTN_ERR_UNSUPPORTED, "a sliding window needs causal=1");
+  if (E != 64 && E != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension E=%d (supported: 64, 128)", E);
+  if (mode == ATTN_MODE_DOT && !std::isfinite(scale)) return fail(ATTN_ERR_ARG, "scale must be finite");
+  if (mode == ATTN_MODE_RBF && !(std::isfinite(gamma) && gamma >= 0.f))
+    return fail(ATTN_ERR_ARG, "gamma must be finite and >= 0");
+  if ((long long)N * Hq * L * E > kMaxElems || (long long)N * Hkv * S * E > kMaxElems)
+    return fail(ATTN_ERR_SHAPE, "tensor too large");
+  if ((long long)N * Hq * L == 0) return ATTN_OK;  // nothing to compute; pointers unused
+  if (!q || !o || !lse) return fail(ATTN_ERR_NULL, "q, o and lse must not be NULL");
+  if (S > 0 && (!k || !v)) return fail(ATTN_ERR_NULL, "k and v must not be NULL when S > 0");
+  if (!aligned(q, 16) || !aligned(o, 16) || (S > 0 && (!aligned(k, 16) || !aligned(v, 16))))
+    return fail(ATTN_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+  if (!aligned(lse, 4) || (sink && !aligned(sink, 4))) return fail(ATTN_ERR_ALIGN, "lse and sink must be 4-byte aligned");
+  return ATTN_OK;
+}
+
+attn_impl::FwdArgs make_args(int N, int Hq, int Hkv, int L, int S, int E, const void* q, const void* k,
+                             const void* v, attn_mode mode, float scale, float gamma, int causal, int window,
+                             int n_reg, const float* sink, void* o, float* lse) {
+  attn_impl::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.sink = sink;
+  a.N = N;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.L = L;
+  a.S = S;
+  a.E = E;
+  a.n_reg = n_reg;
+  a.causal = causal ? 1 : 0;
+  a.window = window;
+  a.rbf = (mode == ATTN_MODE_RBF) ? 1 : 0;
+  a.scale = scale;
+  a.gamma = gamma;
+  return a;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Split count for decode (pure function of the sizes): enough workgroups to
+// cover the chip several times over, but at least 256 keys per split.
+int resolve_splits(int N, int Hq, int Hkv, int S, int causal, int window, int n_reg, int num_splits) {
+  if (num_splits > 0) return num_splits;
+  const attn_impl::DecodeKeys dk = attn_impl::decode_keys(S, n_reg, causal ? 1 : 0, window);
+  const long long units = (long long)N * Hkv * ((Hq / Hkv + 15) / 16);
+  const long long want = units > 0 ? (2048 + units - 1) / units : 1;
+  const long long cap = dk.count > 256 ? (dk.count + 255) / 256 : 1;
+  long long s = want < cap ? want : cap;
+  if (s < 1) s = 1;
+  if (s > 65535) s = 65535;
+  return (int)s;
+}
+
+size_t workspace_for(int N, int Hq, int E, int splits) {
+  const size_t parts = (size_t)N * Hq * splits;
+  return parts * E * sizeof(float) + parts * 2 * sizeof(float);
+}
+
+}  // namespace
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+int attn_fwd(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, const void* q, const void* k,
+             const void* v, attn_mode mode, float scale, float gamma, int causal, int window, int n_reg,
+             const float* sink, void* o, float* lse, void* stream) {
+  int rc = check_args(dt, N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o, lse);
+  if (rc != ATTN_OK) return rc;
+  if ((long long)N * Hq * L == 0) return ok();
+  const int tile = dt == ATTN_BF16 ? 128 : 64;
+  if ((long long)((L + tile - 1) / tile) * N * Hq > kMaxGrid) return fail(ATTN_ERR_SHAPE, "grid too large");
+  const attn_impl::FwdArgs a =
+      make_args(N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o, lse);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = dt == ATTN_BF16 ? attn_impl::launch_prefill_bf16(a, st) : attn_impl::launch_prefill_f32(a, st);
+  return hip_status(e, "attn_fwd launch");
+}
+
+int attn_decode_num_splits(int N, int Hq, int Hkv, int S, int E, int causal, int window, int n_reg) {
+  if (N < 0 || Hq <= 0 || Hkv <= 0 || S < 0 || Hq % Hkv != 0 || n_reg < 0 || n_reg > S || window < 0)
+    return fail(ATTN_ERR_SHAPE, "invalid decode sizes");
+  if (E != 64 && E != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension E=%d (supported: 64, 128)", E);
+  return resolve_splits(N, Hq, Hkv, S, causal, window, n_reg, 0);
+}
+
+size_t attn_decode_workspace_bytes(int N, int Hq, int Hkv, int S, int E, int causal, int window, int n_reg,
+                                   int num_splits) {
+  if (N < 0 || Hq <= 0 || Hkv <= 0 || S < 0 || Hq % Hkv != 0 || n_reg < 0 || n_reg > S || window < 0 ||
+      num_splits < 0 || (E != 64 && E != 128))
+    return 0;
+  const int splits = resolve_splits(N, Hq, Hkv, S, causal, window, n_reg, num_splits);
+  return workspace_for(N, Hq, E, splits);
+}
+
+int attn_decode(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, const void* q, const void* k,
+                const void* v, attn_mode mode, float scale, float gamma, int causal, int window, int n_reg,
+                const float* sink, void* o, float* lse, int num_splits, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  if (L != 1) return fail(ATTN_ERR_SHAPE, "decode takes exactly one query per sequence (L=%d)", L);
+  int rc = check_args(dt, N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o, lse);
+  if (rc != ATTN_OK) return rc;
+  if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode is implemented for bf16 only");
+  if (num_splits < 0) return fail(ATTN_ERR_ARG, "num_splits=%d must be >= 0", num_splits);
+  if (N == 0) return ok();
+  const int splits = resolve_splits(N, Hq, Hkv, S, causal, window, n_reg, num_splits);
+  const size_t need = workspace_for(N, Hq, E, splits);
+  if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, need);
+  if (!aligned(workspace, 16)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if ((long long)N * Hkv * ((Hq / Hkv + 15) / 16) > 65535LL || (long long)N * Hq > kMaxGrid)
+    return fail(ATTN_ERR_SHAPE, "grid too large");
+  attn_impl::DecodeArgs d;
+  d.f = make_args(N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o, lse);
+  d.num_splits = splits;
+  d.part_o = static_cast<float*>(workspace);
+  d.part_ml = d.part_o + (size_t)N * Hq * splits * E;
+  return hip_status(attn_impl::launch_decode_bf16(d, static_cast<hipStream_t>(stream)), "attn_decode launch");
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "null pointer";
+    case ATTN_ERR_SHAPE: return "inconsistent sizes";
+    case ATTN_ERR_DTYPE: return "unknown element type";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_ALIGN: return "misaligned pointer";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+    case ATTN_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+}  // extern "C"
+#pragma GCC visibility pop

@@ -1,0 +1,63 @@
+// device_common.h -- small device-side helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn_dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Exact widening of the low / high bf16 halves of a packed dword.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Sum of squares of the 8 bf16 values in a 16-byte chunk, in fp32 (products are exact).
+__device__ __forceinline__ float sumsq8(u32x4 c) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = bf16_lo(c[i]), b = bf16_hi(c[i]);
+    s = __builtin_fmaf(a, a, s);
+    s = __builtin_fmaf(b, b, s);
+  }
+  return s;
+}
+
+// Round 8 floats to bf16 (nearest-even, v_cvt_pk_bf16_f32) as an MFMA operand.
+__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3,
+                                              float a4, float a5, float a6, float a7) {
+  f32x8 f = {a0, a1, a2, a3, a4, a5, a6, a7};
+  return __builtin_convertvector(f, bf16x8);
+}
+
+__device__ __forceinline__ bf16x4 pack_bf16x4(float a0, float a1, float a2, float a3) {
+  f32x4 f = {a0, a1, a2, a3};
+  return __builtin_convertvector(f, bf16x4);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 2^x on the hardware transcendental unit (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value held by lane (lane ^ mask) of the wave.
+__device__ __forceinline__ float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// 16-byte global load that returns zeros when `ok` is false (no access is made then).
+__device__ __forceinline__ u32x4 load16_or_zero(const uint16_t* p, bool ok) {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return ok ? *reinterpret_cast<const u32x4*>(p) : z;
+}
+
+}  // namespace attn_dev

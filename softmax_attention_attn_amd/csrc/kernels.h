@@ -1,0 +1,52 @@
+// kernels.h -- launch-side description of the gfx950 kernels (internal to libattn).
+//
+// The host API (attn_api.cpp) validates arguments, fills these parameter blocks
+// and calls the launchers; each launcher enqueues its kernel(s) on the given
+// stream and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn_impl {
+
+// Everything a forward kernel needs; element pointers are raw bit storage
+// (uint16_t for bf16, float for f32).  Layouts: q,o (N,Hq,L,E); k,v (N,Hkv,S,E).
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const float* sink;  // Hq logits or nullptr
+  int N, Hq, Hkv, L, S, E;
+  int n_reg;          // register rows at the start of K/V
+  int causal;
+  int window;         // 0 = none
+  int rbf;            // 0 = dot, 1 = rbf
+  float scale;        // dot logit scale
+  float gamma;        // rbf width
+};
+
+// Split-K decode: workspace holds the per-split partial results.
+struct DecodeArgs {
+  FwdArgs f;          // f.L == 1
+  int num_splits;
+  float* part_o;      // [N][Hq][num_splits][E]   unnormalised outputs
+  float* part_ml;     // [N][Hq][num_splits][2]   running max (log2 units), running sum
+};
+
+hipError_t launch_prefill_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_prefill_f32(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+
+// Key range attn_decode streams: registers [0, n_reg) followed by the visible
+// real keys [n_reg + first_real, S); `count` = number of keys in that list.
+struct DecodeKeys {
+  int first_real;
+  int count;
+};
+DecodeKeys decode_keys(int S, int n_reg, int causal, int window);
+
+}  // namespace attn_impl

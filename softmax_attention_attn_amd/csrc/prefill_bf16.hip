@@ -1,0 +1,388 @@
+// prefill_bf16.hip -- fused tiled attention forward for bf16 inputs on gfx950.
+//
+// One workgroup = 4 waves = 128 query rows of one (batch, query head); each
+// wave owns 32 rows.  Keys are streamed in tiles of 64 through LDS; the score
+// tile is never written to memory (the tiling + online softmax of the
+// FlashAttention row in "어텐션 메커니즘" section 6, and the running max /
+// running sum described in "SDPA란 무엇인가?" section 2).
+//
+// Orientation.  Each wave computes S^T = K * Q^T with v_mfma_f32_32x32x16_bf16
+// (A = 32 keys x 16 head-dims from LDS, B = the wave's Q^T held in VGPRs), so in
+// the accumulator layout every lane holds ONE query (column) and 16 keys.  The
+// row max and the rescale factor are then per-lane scalars; only one exchange
+// with lane^32 (the other half of the same query's keys) is needed per tile.
+// The output is accumulated the same way, O^T = V^T * P^T: P^T comes straight
+// from the S^T registers (rounded to bf16), V^T is read from an LDS copy of the
+// V tile that was transposed while staging, with its keys permuted into the
+// order in which the S^T accumulator hands them to each lane.
+//
+// Logits are kept in log2 units: x = c_logit * (q.k) + c_bias * |k|^2 with
+//   dot: c_logit = scale*log2(e),     c_bias = 0
+//   rbf: c_logit = 2*gamma*log2(e),   c_bias = -gamma*log2(e)
+// i.e. the RBF logit -gamma|q-k|^2 with -gamma|q|^2 dropped by shift invariance
+// (RBF-attention digest, section details paragraph 2); |k|^2 is formed from the
+// staged key tile on chip (same digest, paragraph 3).  The sink logit seeds the
+// running state (m = s_h, l = 1: "Attention Sink" section 4.2 -- in the
+// denominator, no value), shifted by gamma|q|^2 in RBF mode so that it competes
+// in the same frame; the LSE is reported for the unfolded logits.
+#include "device_common.h"
+#include "kernels.h"
+
+using namespace attn_dev;
+
+namespace {
+
+constexpr int BM = 128;  // query rows per workgroup
+constexpr int BN = 64;   // keys per staged tile
+constexpr int NT = 256;  // threads per workgroup
+
+struct PrefillParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  const float* sink;
+  int N, Hq, Hkv, L, S, n_reg, S_real, off, causal, window;
+  float c_logit, c_bias, gamma;
+  int num_q_tiles;
+  int xcd_groups;   // 1: the 8 XCDs each take whole K/V heads (needs N*Hkv % 8 == 0)
+  int heavy_first;  // 1: causal, dispatch the query tiles with the most keys first
+};
+
+// Workgroup id -> (query tile, batch, head).  Workgroups are handed to the 8
+// XCDs round-robin (id % 8), and each XCD has its own L2: with xcd_groups all
+// query heads that read one K/V head land on the same XCD.
+__device__ __forceinline__ void map_block(int bid, const PrefillParams& p, int& qt, int& n, int& h) {
+  const int G = p.Hq / p.Hkv;
+  int qt_rev;
+  if (p.xcd_groups) {
+    const int U = p.N * p.Hkv;
+    const int x = bid & 7, y = bid >> 3;
+    const int per = (U >> 3) * G;
+    qt_rev = y / per;
+    const int rest = y - qt_rev * per;
+    const int ul = rest / G;
+    const int u = ul * 8 + x;
+    n = u / p.Hkv;
+    h = (u - n * p.Hkv) * G + (rest - ul * G);
+  } else {
+    const int per = p.N * p.Hq;
+    qt_rev = bid / per;
+    const int nh = bid - qt_rev * per;
+    n = nh / p.Hq;
+    h = nh - n * p.Hq;
+  }
+  qt = p.heavy_first ? (p.num_q_tiles - 1 - qt_rev) : qt_rev;
+}
+
+template <int E, bool RBF>
+__global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(PrefillParams p) {
+  constexpr int KSTR = E + 8;   // K tile row stride (elements): +16 B against bank conflicts
+  constexpr int VSTR = BN + 8;  // V^T tile row stride (elements)
+  constexpr int QS = E / 16;    // MFMA steps over the head dimension
+  constexpr int EB = E / 32;    // 32-row blocks of O^T
+  constexpr int NB = BN / 32;   // 32-key blocks of S^T per tile
+  constexpr int ECH = E / 8;    // 16-byte chunks per row
+  constexpr int KCH = BN * ECH / NT;          // K chunks staged per thread
+  constexpr int VTHREADS = (BN / 4) * ECH;    // threads staging a 4-key x 8-dim block of V
+  static_assert(KCH * NT == BN * ECH, "K staging must tile evenly");
+  static_assert(VTHREADS <= NT, "V staging needs at most one block per thread");
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t sVT[E * VSTR];
+  __shared__ __attribute__((aligned(16))) float sBias[BN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  int qt, n, h;
+  map_block(blockIdx.x, p, qt, n, h);
+  const int G = p.Hq / p.Hkv;
+  const int kh = h / G;
+  const int i0 = qt * BM;
+  const int qa = i0 + wave * 32;          // first query row of this wave
+  const int qi = qa + l32;                // this lane's query row
+  const bool qvalid = qi < p.L;
+  const int qb = min(qa + 31, p.L - 1);   // last valid row of this wave (qb < qa: none)
+
+  // Q^T fragments: lane holds Q[qi][16s + 8g .. +8] for every step s.
+  const uint16_t* qrow = p.q + (((size_t)n * p.Hq + h) * p.L + (qvalid ? qi : 0)) * E;
+  bf16x8 qf[QS];
+  float qn2 = 0.f;
+#pragma unroll
+  for (int s = 0; s < QS; ++s) {
+    const u32x4 c = load16_or_zero(qrow + 16 * s + 8 * g, qvalid);
+    qf[s] = as_bf16x8(c);
+    if (RBF) qn2 += sumsq8(c);
+  }
+  if (RBF) qn2 += xor_lane(qn2, 32);
+
+  // Running state in log2 units.  lsum is this lane's share of the row sum
+  // (its 16 keys per block); the two halves are added in the epilogue.
+  float m = kNegInf, lsum = 0.f;
+  if (p.sink) {
+    float s0 = p.sink[h];
+    if (RBF) s0 += p.gamma * qn2;
+    m = s0 * kLog2e;
+    lsum = (g == 0) ? 1.f : 0.f;
+  }
+  f32x16 acc[EB];
+#pragma unroll
+  for (int c = 0; c < EB; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+
+  // Tiles: register rows first, then the real keys some row of this workgroup sees.
+  const int i_last = min(i0 + BM, p.L) - 1;
+  const int r_hi = p.causal ? min(p.S_real - 1, i_last + p.off) : p.S_real - 1;
+  const int r_lo = p.window > 0 ? max(0, i0 + p.off - p.window + 1) : 0;
+  const int n_real_tiles = r_hi >= r_lo ? (r_hi - r_lo + BN) / BN : 0;
+  const int n_reg_tiles = (p.n_reg + BN - 1) / BN;
+  const int T = n_reg_tiles + n_real_tiles;
+
+  const size_t kvoff = ((size_t)n * p.Hkv + kh) * (size_t)p.S * E;
+  const uint16_t* kbase = p.k + kvoff;
+  const uint16_t* vbase = p.v + kvoff;
+
+  // Staging roles.  K: chunk id = tid + NT*i is row id/ECH, dims 8*(id%ECH)..+8.
+  // V: thread (va, vc) stages rows 4va..4va+3, dims 8vc..8vc+7, transposed.
+  const int va = tid % (BN / 4), vc = tid / (BN / 4);
+  const bool vrole = tid < VTHREADS;
+  // Position of key quad va in the permuted V^T row: within each 16-key group the
+  // order is keys {0-3, 8-11, 4-7, 12-15}, i.e. lane half g of the PV operand
+  // reads keys {4g..4g+3, 8+4g..8+4g+3} as 8 consecutive elements.
+  const int vpos = 16 * (va >> 2) + ((va & 1) ? 8 : 0) + ((va & 2) ? 4 : 0);
+
+  u32x4 kreg[KCH], vreg[4];
+
+  auto tile_keys = [&](int t, int& j0, int& kc) {
+    if (t < n_reg_tiles) {
+      j0 = t * BN;
+      kc = min(BN, p.n_reg - j0);
+    } else {
+      j0 = p.n_reg + r_lo + (t - n_reg_tiles) * BN;
+      kc = min(BN, p.S - j0);
+    }
+  };
+
+  auto load_tile = [&](int t) {
+    int j0, kc;
+    tile_keys(t, j0, kc);
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int id = tid + NT * i;
+      const int row = id / ECH, c = id % ECH;
+      kreg[i] = load16_or_zero(kbase + (size_t)(j0 + row) * E + 8 * c, row < kc);
+    }
+    if (vrole) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int row = 4 * va + ii;
+        vreg[ii] = load16_or_zero(vbase + (size_t)(j0 + row) * E + 8 * vc, row < kc);
+      }
+    }
+  };
+
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int id = tid + NT * i;
+      const int row = id / ECH, c = id % ECH;
+      *reinterpret_cast<u32x4*>(&sK[row * KSTR + 8 * c]) = kreg[i];
+      if (RBF) {
+        float ss = sumsq8(kreg[i]);
+#pragma unroll
+        for (int o = 1; o < ECH; o <<= 1) ss += xor_lane(ss, o);
+        if (c == 0) sBias[row] = p.c_bias * ss;
+      }
+    }
+    if (vrole) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int w = j >> 1, sh = (j & 1) * 16;
+        const uint32_t e0 = (vreg[0][w] >> sh) & 0xffffu, e1 = (vreg[1][w] >> sh) & 0xffffu;
+        const uint32_t e2 = (vreg[2][w] >> sh) & 0xffffu, e3 = (vreg[3][w] >> sh) & 0xffffu;
+        u32x2 d = {e0 | (e1 << 16), e2 | (e3 << 16)};
+        *reinterpret_cast<u32x2*>(&sVT[(8 * vc + j) * VSTR + vpos]) = d;
+      }
+    }
+  };
+
+  auto compute_tile = [&](int t) {
+    int j0, kc;
+    tile_keys(t, j0, kc);
+    const bool is_reg = t < n_reg_tiles;
+    bool any, full;
+    if (qb < qa) {
+      any = false;
+      full = false;
+    } else if (is_reg) {
+      any = true;
+      full = (kc == BN);
+    } else {
+      const int ra = j0 - p.n_reg, rb = ra + BN - 1;
+      any = !((ra >= p.S_real) || (p.causal && ra > qb + p.off) ||
+              (p.window > 0 && qa + p.off - rb >= p.window));
+      full = rb < p.S_real && (!p.causal || rb <= qa + p.off) &&
+             (p.window <= 0 || qb + p.off - ra < p.window);
+    }
+    if (!any) return;
+
+    // S^T = K * Q^T for NB blocks of 32 keys.
+    f32x16 st[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[b][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < QS; ++s) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sK[(32 * b + l32) * KSTR + 16 * s + 8 * g]);
+        st[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st[b], 0, 0, 0);
+      }
+    }
+
+    // Logits (log2 units), penalty, visibility; the accumulator row of register
+    // r in block b is key 32b + 8(r/4) + 4g + r%4 of the tile.
+    float mx = kNegInf;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kt = 32 * b + 8 * (r >> 2) + 4 * g + (r & 3);
+        float x = st[b][r] * p.c_logit;
+        if (RBF) x += sBias[kt];
+        if (!full) {
+          bool vis;
+          if (is_reg) {
+            vis = kt < kc;
+          } else {
+            const int rr = j0 - p.n_reg + kt;
+            vis = rr < p.S_real && (!p.causal || rr <= qi + p.off) &&
+                  (p.window <= 0 || qi + p.off - rr < p.window);
+          }
+          if (!vis) x = kNegInf;
+        }
+        st[b][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, xor_lane(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    m = m_new;
+    lsum *= alpha;
+#pragma unroll
+    for (int c = 0; c < EB; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[c][r] *= alpha;
+
+    float ps = 0.f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = fast_exp2(st[b][r] - m_use);
+        st[b][r] = pv;
+        ps += pv;
+      }
+    lsum += ps;
+
+    // O^T += V^T * P^T, 16 keys per MFMA step.
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int r0 = 8 * s2;
+        const bf16x8 pf = pack_bf16x8(st[b][r0 + 0], st[b][r0 + 1], st[b][r0 + 2], st[b][r0 + 3],
+                                      st[b][r0 + 4], st[b][r0 + 5], st[b][r0 + 6], st[b][r0 + 7]);
+        const int u = 2 * b + s2;
+#pragma unroll
+        for (int c = 0; c < EB; ++c) {
+          const bf16x8 vt = *reinterpret_cast<const bf16x8*>(&sVT[(32 * c + l32) * VSTR + 16 * u + 8 * g]);
+          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pf, acc[c], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  if (T > 0) load_tile(0);
+  for (int t = 0; t < T; ++t) {
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (t + 1 < T) load_tile(t + 1);
+    compute_tile(t);
+  }
+
+  // Epilogue: O = acc / l (0 for an empty row), LSE in natural-log units.
+  const float ltot = lsum + xor_lane(lsum, 32);
+  if (qvalid) {
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    uint16_t* orow = p.o + (((size_t)n * p.Hq + h) * p.L + qi) * E;
+#pragma unroll
+    for (int c = 0; c < EB; ++c)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const bf16x4 pk = pack_bf16x4(acc[c][4 * rq + 0] * inv, acc[c][4 * rq + 1] * inv,
+                                      acc[c][4 * rq + 2] * inv, acc[c][4 * rq + 3] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * c + 8 * rq + 4 * g) = pk;
+      }
+    if (g == 0) {
+      float l = kNegInf;
+      if (ltot > 0.f) {
+        l = (m + log2f(ltot)) * kLn2;
+        if (RBF) l -= p.gamma * qn2;
+      }
+      p.lse[((size_t)n * p.Hq + h) * p.L + qi] = l;
+    }
+  }
+}
+
+template <int E, bool RBF>
+hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
+  const long long blocks = (long long)p.num_q_tiles * p.N * p.Hq;
+  hipLaunchKernelGGL((prefill_bf16_kernel<E, RBF>), dim3((unsigned)blocks), dim3(NT), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+namespace attn_impl {
+
+hipError_t launch_prefill_bf16(const FwdArgs& a, hipStream_t stream) {
+  PrefillParams p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.o = static_cast<uint16_t*>(a.o);
+  p.lse = a.lse;
+  p.sink = a.sink;
+  p.N = a.N;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.L = a.L;
+  p.S = a.S;
+  p.n_reg = a.n_reg;
+  p.S_real = a.S - a.n_reg;
+  p.off = a.S - a.n_reg - a.L;
+  p.causal = a.causal ? 1 : 0;
+  p.window = a.window;
+  p.gamma = a.gamma;
+  if (a.rbf) {
+    p.c_logit = 2.f * a.gamma * 1.4426950408889634f;
+    p.c_bias = -a.gamma * 1.4426950408889634f;
+  } else {
+    p.c_logit = a.scale * 1.4426950408889634f;
+    p.c_bias = 0.f;
+  }
+  p.num_q_tiles = (a.L + BM - 1) / BM;
+  p.xcd_groups = ((a.N * a.Hkv) % 8 == 0) ? 1 : 0;
+  p.heavy_first = p.causal;
+  if (a.E == 128) return a.rbf ? launch_t<128, true>(p, stream) : launch_t<128, false>(p, stream);
+  return a.rbf ? launch_t<64, true>(p, stream) : launch_t<64, false>(p, stream);
+}
+
+}  // namespace attn_impl

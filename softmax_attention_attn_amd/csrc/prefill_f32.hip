@@ -1,0 +1,190 @@
+// prefill_f32.hip -- fused tiled attention forward for float32 inputs on gfx950.
+//
+// Full fp32 arithmetic (no bf16 rounding of P).  One wave = 64 query rows, one
+// row per lane; keys stream through LDS in tiles of 32 with the online softmax
+// (running max and running sum, "SDPA란 무엇인가?" section 2).  Same logit frame, visibility rule, sink and
+// LSE conventions as the bf16 kernel: x = c_logit*(q.k) + c_bias*|k|^2 in log2
+// units, with |k|^2 computed once per staged tile from LDS.  Keys are taken
+// one at a time: the running max only moves (and the accumulator is only
+// rescaled) when a larger logit arrives.
+#include "device_common.h"
+#include "kernels.h"
+
+using namespace attn_dev;
+
+namespace {
+
+constexpr int BQ = 64;  // query rows per workgroup (one wave)
+constexpr int BK = 32;  // keys per staged tile
+
+struct PrefillF32Params {
+  const float* q;
+  const float* k;
+  const float* v;
+  float* o;
+  float* lse;
+  const float* sink;
+  int N, Hq, Hkv, L, S, n_reg, S_real, off, causal, window;
+  float c_logit, c_bias, gamma;
+  int num_q_tiles;
+};
+
+template <int E, bool RBF>
+__global__ __launch_bounds__(BQ) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_f32_kernel(PrefillF32Params p) {
+  __shared__ __attribute__((aligned(16))) float sK[BK * E];
+  __shared__ __attribute__((aligned(16))) float sV[BK * E];
+  __shared__ float sBias[BK];
+
+  const int tid = threadIdx.x;
+  const int qt = blockIdx.x % p.num_q_tiles;
+  const int nh = blockIdx.x / p.num_q_tiles;
+  const int h = nh % p.Hq, n = nh / p.Hq;
+  const int kh = h / (p.Hq / p.Hkv);
+  const int i0 = qt * BQ;
+  const int qi = i0 + tid;
+  const bool qvalid = qi < p.L;
+
+  float q[E], acc[E];
+  const float* qrow = p.q + (((size_t)n * p.Hq + h) * p.L + (qvalid ? qi : 0)) * E;
+  float qn2 = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    q[e] = qvalid ? qrow[e] : 0.f;
+    qn2 = __builtin_fmaf(q[e], q[e], qn2);
+    acc[e] = 0.f;
+  }
+  float m = kNegInf, lsum = 0.f;
+  if (p.sink) {
+    float s0 = p.sink[h];
+    if (RBF) s0 += p.gamma * qn2;
+    m = s0 * kLog2e;
+    lsum = 1.f;
+  }
+
+  const int i_last = min(i0 + BQ, p.L) - 1;
+  const int r_hi = p.causal ? min(p.S_real - 1, i_last + p.off) : p.S_real - 1;
+  const int r_lo = p.window > 0 ? max(0, i0 + p.off - p.window + 1) : 0;
+  const int n_real_tiles = r_hi >= r_lo ? (r_hi - r_lo + BK) / BK : 0;
+  const int n_reg_tiles = (p.n_reg + BK - 1) / BK;
+  const int T = n_reg_tiles + n_real_tiles;
+  const size_t kvoff = ((size_t)n * p.Hkv + kh) * (size_t)p.S * E;
+
+  for (int t = 0; t < T; ++t) {
+    int j0, kc;
+    const bool is_reg = t < n_reg_tiles;
+    if (is_reg) {
+      j0 = t * BK;
+      kc = min(BK, p.n_reg - j0);
+    } else {
+      j0 = p.n_reg + r_lo + (t - n_reg_tiles) * BK;
+      kc = min(BK, p.S - j0);
+    }
+    __syncthreads();
+    for (int idx = tid; idx < BK * E / 4; idx += BQ) {
+      const int row = (idx * 4) / E, col = (idx * 4) % E;
+      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+      if (row < kc) {
+        kv = *reinterpret_cast<const f32x4*>(p.k + kvoff + (size_t)(j0 + row) * E + col);
+        vv = *reinterpret_cast<const f32x4*>(p.v + kvoff + (size_t)(j0 + row) * E + col);
+      }
+      *reinterpret_cast<f32x4*>(&sK[row * E + col]) = kv;
+      *reinterpret_cast<f32x4*>(&sV[row * E + col]) = vv;
+    }
+    __syncthreads();
+    if (RBF && tid < BK) {
+      float ss = 0.f;
+      for (int e = 0; e < E; ++e) ss = __builtin_fmaf(sK[tid * E + e], sK[tid * E + e], ss);
+      sBias[tid] = p.c_bias * ss;
+    }
+    __syncthreads();
+
+#pragma unroll 1
+    for (int kt = 0; kt < BK; ++kt) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) d = __builtin_fmaf(q[e], sK[kt * E + e], d);
+      float x = d * p.c_logit;
+      if (RBF) x += sBias[kt];
+      bool vis;
+      if (is_reg) {
+        vis = kt < kc;
+      } else {
+        const int rr = j0 - p.n_reg + kt;
+        vis = rr < p.S_real && (!p.causal || rr <= qi + p.off) &&
+              (p.window <= 0 || qi + p.off - rr < p.window);
+      }
+      if (!vis) continue;  // weight exactly zero
+      if (x > m) {         // new running max: rescale what was accumulated
+        const float alpha = exp2f(m - x);
+        lsum *= alpha;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] *= alpha;
+        m = x;
+      }
+      const float pv = exp2f(x - m);
+      lsum += pv;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(pv, sV[kt * E + e], acc[e]);
+    }
+  }
+
+  if (qvalid) {
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    float* orow = p.o + (((size_t)n * p.Hq + h) * p.L + qi) * E;
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      f32x4 ov = {acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
+      *reinterpret_cast<f32x4*>(orow + e) = ov;
+    }
+    float l = kNegInf;
+    if (lsum > 0.f) {
+      l = (m + log2f(lsum)) * kLn2;
+      if (RBF) l -= p.gamma * qn2;
+    }
+    p.lse[((size_t)n * p.Hq + h) * p.L + qi] = l;
+  }
+}
+
+template <int E, bool RBF>
+hipError_t launch_t(const PrefillF32Params& p, hipStream_t stream) {
+  const long long blocks = (long long)p.num_q_tiles * p.N * p.Hq;
+  hipLaunchKernelGGL((prefill_f32_kernel<E, RBF>), dim3((unsigned)blocks), dim3(BQ), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+namespace attn_impl {
+
+hipError_t launch_prefill_f32(const FwdArgs& a, hipStream_t stream) {
+  PrefillF32Params p;
+  p.q = static_cast<const float*>(a.q);
+  p.k = static_cast<const float*>(a.k);
+  p.v = static_cast<const float*>(a.v);
+  p.o = static_cast<float*>(a.o);
+  p.lse = a.lse;
+  p.sink = a.sink;
+  p.N = a.N;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.L = a.L;
+  p.S = a.S;
+  p.n_reg = a.n_reg;
+  p.S_real = a.S - a.n_reg;
+  p.off = a.S - a.n_reg - a.L;
+  p.causal = a.causal ? 1 : 0;
+  p.window = a.window;
+  p.gamma = a.gamma;
+  if (a.rbf) {
+    p.c_logit = 2.f * a.gamma * 1.4426950408889634f;
+    p.c_bias = -a.gamma * 1.4426950408889634f;
+  } else {
+    p.c_logit = a.scale * 1.4426950408889634f;
+    p.c_bias = 0.f;
+  }
+  p.num_q_tiles = (a.L + BQ - 1) / BQ;
+  if (a.E == 128) return a.rbf ? launch_t<128, true>(p, stream) : launch_t<128, false>(p, stream);
+  return a.rbf ? launch_t<64, true>(p, stream) : launch_t<64, false>(p, stream);
+}
+
+}  // namespace attn_impl

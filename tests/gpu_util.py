@@ -1,0 +1,83 @@
+"""Helpers for the GPU parity tests: move generated inputs to the GPU, run the
+library, run the oracle on the same bits, and compare."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import softmax_attention_attn_amd as attn
+from workloads import gen
+from workloads.configs import Workload
+
+TOL_O = {"bf16": 2e-2, "f32": 1e-4}
+TOL_LSE = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(inp: gen.Inputs, dev="cuda:0"):
+    def t(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+    sink = torch.from_numpy(inp.sink).to(dev) if inp.sink is not None else None
+    return t(inp.q), t(inp.k), t(inp.v), sink
+
+
+def run_gpu(w: Workload, q, k, v, sink, num_splits=0):
+    if w.decode:
+        return attn.decode(q, k, v, scale=w.scale, mode=w.mode, gamma=w.gamma, causal=w.causal,
+                           window=w.window, n_reg=w.n_reg, sink=sink, num_splits=num_splits)
+    return attn.fwd(q, k, v, scale=w.scale, mode=w.mode, gamma=w.gamma, causal=w.causal,
+                    window=w.window, n_reg=w.n_reg, sink=sink)
+
+
+def sample_rows(w: Workload, per_head: int = 4, extra: int = 256, seed: int = 0):
+    """Flat row indices (n*Hq+h)*L+i: every head's first/last rows plus random rows."""
+    r = np.random.default_rng(seed)
+    rows = set()
+    for n in range(w.N):
+        for h in range(w.Hq):
+            base = (n * w.Hq + h) * w.L
+            for i in {0, w.L - 1, min(w.L - 1, 127), min(w.L - 1, 128)}:
+                rows.add(base + i)
+            for i in r.integers(0, w.L, per_head):
+                rows.add(base + int(i))
+    total = w.N * w.Hq * w.L
+    for x in r.integers(0, total, extra):
+        rows.add(int(x))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def compare(w: Workload, inp: gen.Inputs, o_gpu: torch.Tensor, lse_gpu: torch.Tensor, rows=None, threads=0):
+    """Max-abs errors of O and LSE against the oracle (all rows or the given flat rows)."""
+    o_ref, lse_ref = oracle.attn_workload(inp, rows=rows, threads=threads)
+    og = o_gpu.float().cpu().numpy().astype(np.float64).reshape(-1, w.E)
+    lg = lse_gpu.cpu().numpy().astype(np.float64).reshape(-1)
+    o_ref = o_ref.reshape(-1, w.E)
+    lse_ref = lse_ref.reshape(-1)
+    if rows is not None:
+        og = og[rows]
+        lg = lg[rows]
+    assert np.all(np.isfinite(og)), "non-finite output"
+    both_ninf = np.isneginf(lg) & np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lg), np.isneginf(lse_ref)), "LSE -inf pattern differs"
+    assert not np.any(np.isnan(lg)), "NaN LSE"
+    eo = np.abs(og - o_ref)
+    el = np.where(both_ninf, 0.0, np.abs(lg - lse_ref))
+    worst = np.unravel_index(int(np.argmax(eo)), eo.shape) if eo.size else None
+    return float(eo.max()) if eo.size else 0.0, float(el.max()) if el.size else 0.0, worst
+
+
+def check(w: Workload, inp: gen.Inputs, o_gpu, lse_gpu, rows=None, threads=0):
+    eo, el, worst = compare(w, inp, o_gpu, lse_gpu, rows=rows, threads=threads)
+    say(f"  {w.name}: max|dO|={eo:.3e} (worst row/col {worst}) max|dLSE|={el:.3e}")
+    assert eo <= TOL_O[w.dtype], f"{w.name}: O error {eo:.3e} > {TOL_O[w.dtype]}"
+    assert el <= TOL_LSE, f"{w.name}: LSE error {el:.3e} > {TOL_LSE}"
+    return eo, el

@@ -1,0 +1,122 @@
+"""The C ABI: library loads, exports what include/attn.h declares, and rejects
+misuse before any HIP call (CPU only: every call here fails validation or has
+nothing to compute, so no GPU is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import softmax_attention_attn_amd as attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+A = 0x100000  # a 16-byte aligned fake device address; validation never dereferences it
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+[\s\*]+(attn_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(attn.LIB_PATH):
+        from softmax_attention_attn_amd import build
+        build.build()
+    return attn.load()
+
+
+def test_header_declares_the_bound_functions():
+    assert declared_functions() == sorted(attn.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in attn.STATUS:
+        assert lib.attn_status_string(code).decode() not in ("", "unknown status")
+    assert lib.attn_status_string(12345).decode() == "unknown status"
+
+
+def fwd(lib, dt=0, N=1, Hq=4, Hkv=2, L=8, S=8, E=64, q=A, k=A, v=A, mode=0, scale=0.125, gamma=0.0,
+        causal=1, window=0, n_reg=0, sink=None, o=A, lse=A):
+    return lib.attn_fwd(dt, N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o,
+                        lse, None)
+
+
+def dec(lib, dt=0, N=1, Hq=4, Hkv=2, L=1, S=64, E=64, q=A, k=A, v=A, mode=0, scale=0.125, gamma=0.0,
+        causal=1, window=0, n_reg=0, sink=None, o=A, lse=A, splits=0, ws=A, wsb=1 << 30):
+    return lib.attn_decode(dt, N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o,
+                           lse, splits, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), -3),
+    (dict(mode=5), -8),
+    (dict(Hq=6, Hkv=4), -2),
+    (dict(Hq=0), -2),
+    (dict(L=-1), -2),
+    (dict(n_reg=9), -2),
+    (dict(n_reg=-1), -2),
+    (dict(window=-3), -8),
+    (dict(window=4, causal=0), -4),
+    (dict(E=96), -4),
+    (dict(E=256), -4),
+    (dict(scale=float("inf")), -8),
+    (dict(mode=1, gamma=-1.0), -8),
+    (dict(mode=1, gamma=float("nan")), -8),
+    (dict(q=None), -1),
+    (dict(o=None), -1),
+    (dict(lse=None), -1),
+    (dict(k=None), -1),
+    (dict(q=A + 8), -5),
+    (dict(v=A + 2), -5),
+    (dict(lse=A + 2), -5),
+    (dict(sink=A + 1), -5),
+])
+def test_fwd_rejects(lib, kw, code):
+    assert fwd(lib, **kw) == code
+    assert lib.attn_last_error().decode() != ""
+
+
+def test_fwd_empty_is_a_no_op(lib):
+    assert fwd(lib, N=0, q=None, k=None, v=None, o=None, lse=None) == 0
+    assert fwd(lib, L=0, q=None, k=None, v=None, o=None, lse=None) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(L=2), -2),
+    (dict(L=0), -2),
+    (dict(dt=1), -4),
+    (dict(splits=-1), -8),
+    (dict(ws=None), -6),
+    (dict(wsb=16), -6),
+    (dict(ws=A + 4), -5),
+    (dict(Hq=5, Hkv=2), -2),
+    (dict(window=8, causal=0), -4),
+])
+def test_decode_rejects(lib, kw, code):
+    assert dec(lib, **kw) == code
+
+
+def test_decode_split_and_workspace_sizes(lib):
+    # long-context decode shape: 8 sequences, 32 query heads over 8 kv heads, 131072 keys, E=128
+    s = lib.attn_decode_num_splits(8, 32, 8, 131072, 128, 1, 0, 0)
+    assert s == 32
+    assert lib.attn_decode_workspace_bytes(8, 32, 8, 131072, 128, 1, 0, 0, 0) == 8 * 32 * s * (128 + 2) * 4
+    assert lib.attn_decode_workspace_bytes(8, 32, 8, 131072, 128, 1, 0, 0, 5) == 8 * 32 * 5 * 130 * 4
+    assert lib.attn_decode_num_splits(1, 4, 4, 100, 64, 1, 0, 0) == 1  # short cache: one split
+    assert lib.attn_decode_num_splits(1, 4, 3, 100, 64, 1, 0, 0) < 0
+    assert lib.attn_decode_workspace_bytes(1, 4, 3, 100, 64, 1, 0, 0, 0) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(attn, "LIB_PATH", "/nonexistent/libattn.so")
+    monkeypatch.setattr(attn, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        attn.load()

@@ -1,0 +1,175 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle.
+
+Small shapes cover every flag combination with ragged tails (L and S not
+multiples of the tiles), L < S, L > S (rows with nothing visible), GQA, more
+register rows than one key tile, and forced split counts for decode.  The five
+workload configurations run at full size; where the oracle would need minutes,
+it is evaluated on sampled rows (every head's first and last rows plus random
+ones).  Bar: max-abs error 2e-2 on bf16 outputs, 1e-4 on fp32 outputs, 1e-3 on
+the row LSE.
+"""
+import numpy as np
+import pytest
+import torch
+
+import softmax_attention_attn_amd as attn
+from gpu_util import check, run_gpu, sample_rows, say, to_device
+from workloads import configs, gen
+from workloads.configs import Workload
+
+pytestmark = pytest.mark.gpu
+
+
+def W(name, dtype="bf16", N=1, Hq=2, Hkv=2, L=64, S_real=64, E=64, mode="dot", scale=None, gamma=0.125,
+      causal=True, window=0, n_reg=0, sink=False, decode=False, seed=11, k_dist="normal"):
+    if scale is None:
+        scale = 1.0 / np.sqrt(E)
+    return Workload(name, dtype, N, Hq, Hkv, L, S_real, E, mode, float(scale), float(gamma), causal, window,
+                    n_reg, sink, decode, seed, k_dist)
+
+
+PREFILL_CASES = [
+    W("dot_noncausal_mha", N=2, L=150, S_real=150, causal=False),
+    W("dot_causal_e128_ragged", Hq=3, Hkv=3, L=300, S_real=300, E=128),
+    W("dot_causal_L_lt_S", L=100, S_real=333, E=128),
+    W("dot_causal_L_gt_S_empty_rows", L=200, S_real=70),
+    W("dot_gqa_causal", Hq=8, Hkv=2, L=257, S_real=257),
+    W("dot_window_sink", L=400, S_real=400, window=37, sink=True),
+    W("dot_window_gqa_sink_e128", Hq=6, Hkv=3, L=520, S_real=520, E=128, window=128, sink=True),
+    W("dot_sink_noncausal_e128", N=2, L=130, S_real=190, E=128, causal=False, sink=True),
+    W("dot_registers_window", L=300, S_real=300, n_reg=5, window=50),
+    W("dot_single_query", N=3, Hq=4, Hkv=1, L=1, S_real=999, E=128),
+    W("rbf_causal_registers", L=300, S_real=300, mode="rbf", n_reg=4, k_dist="dir_lognormal"),
+    W("rbf_noncausal_many_registers_e128", L=130, S_real=90, E=128, mode="rbf", n_reg=70, causal=False),
+    W("rbf_window_gqa_sink", Hq=4, Hkv=2, L=333, S_real=333, mode="rbf", window=100, sink=True, gamma=0.05),
+    W("rbf_L_lt_S_e128", L=77, S_real=400, E=128, mode="rbf", gamma=0.02),
+    W("f32_rbf_causal", dtype="f32", Hq=1, Hkv=1, L=256, S_real=256, mode="rbf"),
+    W("f32_dot_window_gqa_sink_e128", dtype="f32", Hq=4, Hkv=2, L=100, S_real=100, E=128, window=30, sink=True),
+    W("f32_rbf_registers_L_lt_S", dtype="f32", L=70, S_real=150, mode="rbf", n_reg=3, gamma=0.05),
+    W("f32_dot_L_gt_S", dtype="f32", L=90, S_real=40, E=64),
+]
+
+DECODE_CASES = [
+    (W("dec_dot_sink_gqa4_e128", N=2, Hq=8, Hkv=2, L=1, S_real=5000, E=128, sink=True, decode=True), [0, 1, 3, 64]),
+    (W("dec_rbf_registers", N=2, Hq=4, Hkv=2, L=1, S_real=3000, mode="rbf", n_reg=4, decode=True,
+       k_dist="dir_lognormal"), [0, 7]),
+    (W("dec_window_registers_sink", Hq=4, Hkv=1, L=1, S_real=4000, E=128, window=700, n_reg=4, sink=True,
+       decode=True), [0, 2]),
+    (W("dec_gqa20_two_query_groups", Hq=40, Hkv=2, L=1, S_real=1500, decode=True), [0]),
+    (W("dec_mha_ragged", N=3, Hq=3, Hkv=3, L=1, S_real=777, decode=True, sink=True), [0, 5]),
+    (W("dec_tiny_cache", Hq=4, Hkv=2, L=1, S_real=5, E=128, decode=True), [0, 3]),
+]
+
+
+@pytest.mark.parametrize("w", PREFILL_CASES, ids=[w.name for w in PREFILL_CASES])
+def test_prefill_small(w):
+    say(f"[prefill] {w}")
+    inp = gen.generate(w)
+    q, k, v, sink = to_device(inp)
+    o, lse = run_gpu(w, q, k, v, sink)
+    torch.cuda.synchronize()
+    check(w, inp, o, lse)
+
+
+@pytest.mark.parametrize("w,splits", DECODE_CASES, ids=[c[0].name for c in DECODE_CASES])
+def test_decode_small(w, splits):
+    say(f"[decode] {w} splits={splits}")
+    inp = gen.generate(w)
+    q, k, v, sink = to_device(inp)
+    for s in splits:
+        o, lse = run_gpu(w, q, k, v, sink, num_splits=s)
+        torch.cuda.synchronize()
+        say(f"  num_splits={s}")
+        check(w, inp, o, lse)
+
+
+def test_decode_matches_prefill_single_query():
+    w = W("dec_vs_prefill", N=2, Hq=8, Hkv=2, L=1, S_real=2000, E=128, sink=True, decode=True)
+    inp = gen.generate(w)
+    q, k, v, sink = to_device(inp)
+    od, ld = run_gpu(w, q, k, v, sink, num_splits=9)
+    of, lf = run_gpu(w.with_(decode=False), q, k, v, sink)
+    torch.cuda.synchronize()
+    assert (od.float() - of.float()).abs().max().item() <= 2e-2
+    assert (ld - lf).abs().max().item() <= 1e-3
+
+
+def test_empty_and_keyless_inputs():
+    dev = "cuda:0"
+    q = torch.zeros((0, 2, 5, 64), dtype=torch.bfloat16, device=dev)
+    k = torch.zeros((0, 2, 7, 64), dtype=torch.bfloat16, device=dev)
+    o, lse = attn.fwd(q, k, k)
+    assert o.shape == q.shape and lse.shape == (0, 2, 5)
+    # no keys at all: O = 0, LSE = -inf; with a sink, LSE = s_h
+    q = torch.randn((1, 2, 5, 64), device=dev).to(torch.bfloat16)
+    k = torch.zeros((1, 2, 0, 64), dtype=torch.bfloat16, device=dev)
+    o, lse = attn.fwd(q, k, k, causal=False)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    s = torch.tensor([0.25, -1.5], device=dev)
+    o, lse = attn.fwd(q, k, k, causal=False, sink=s)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.allclose(lse, s[None, :, None].expand(1, 2, 5), atol=1e-6)
+
+
+def test_outputs_stay_in_bounds_and_runs_are_deterministic():
+    w = W("guard", Hq=4, Hkv=2, L=333, S_real=333, E=128, sink=True, window=100)
+    inp = gen.generate(w)
+    q, k, v, sink = to_device(inp)
+    n_o, n_l = q.numel(), w.N * w.Hq * w.L
+    obuf = torch.full((n_o + 4096,), 7.0, dtype=torch.bfloat16, device="cuda:0")
+    lbuf = torch.full((n_l + 1024,), 7.0, dtype=torch.float32, device="cuda:0")
+    o1, l1 = attn.fwd(q, k, v, scale=w.scale, causal=True, window=w.window, sink=sink,
+                      out=obuf[:n_o].view(q.shape), lse=lbuf[:n_l].view(w.N, w.Hq, w.L))
+    o1, l1 = o1.clone(), l1.clone()
+    o2, l2 = attn.fwd(q, k, v, scale=w.scale, causal=True, window=w.window, sink=sink)
+    torch.cuda.synchronize()
+    assert torch.all(obuf[n_o:] == 7.0) and torch.all(lbuf[n_l:] == 7.0)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+    check(w, inp, o1, l1)
+
+
+def test_binding_raises_on_misuse():
+    q = torch.zeros((1, 6, 8, 64), dtype=torch.bfloat16, device="cuda:0")
+    k = torch.zeros((1, 4, 8, 64), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(attn.AttnError) as ei:
+        attn.fwd(q, k, k)
+    assert ei.value.status == -2
+    with pytest.raises(attn.AttnError) as ei:
+        attn.fwd(q[:, :4], k, k, window=3, causal=False)
+    assert ei.value.status == -4
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+
+
+def _full(w, rows, splits=0):
+    say(f"[full] {w.name}: generating inputs")
+    inp = gen.generate(w)
+    say(f"[full] {w.name}: running on the GPU")
+    q, k, v, sink = to_device(inp)
+    o, lse = run_gpu(w, q, k, v, sink, num_splits=splits)
+    torch.cuda.synchronize()
+    say(f"[full] {w.name}: oracle on {('all' if rows is None else len(rows))} rows")
+    check(w, inp, o, lse, rows=rows)
+
+
+def test_full_c1_rbf_causal_f32():
+    _full(configs.C1, None)
+
+
+def test_full_c2_dot_causal_bf16():
+    _full(configs.C2, sample_rows(configs.C2))
+
+
+def test_full_c3_rbf_causal_registers_bf16():
+    _full(configs.C3, sample_rows(configs.C3, per_head=6))
+
+
+def test_full_c4_sink_window_gqa_bf16():
+    _full(configs.C4, sample_rows(configs.C4))
+
+
+def test_full_c5_decode_splitk_bf16():
+    _full(configs.C5, None)
