@@ -194,6 +194,9 @@ def main() -> int:
     ap.add_argument("--extras", default="all", choices=["all", "none"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of attention, time a plain device-to-device copy of this many bytes "
+                         "(the reference kernel for calibrating HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -209,6 +212,24 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / args.steps
+        print(json.dumps({"copy_bytes": args.copy_bytes, "ms": ms,
+                          "GBps_read_plus_write": 2 * args.copy_bytes / (ms * 1e-3) / 1e9}), flush=True)
+        return 0
 
     w = configs.BY_NAME[args.workload]
     ms, inp, first = time_workload(w, args.steps, args.warmup, 1, torch, attn, keep_first_output=True)
