@@ -35,29 +35,37 @@ def common_flags() -> list:
             "-I", INCLUDE, "-I", CSRC]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + common_flags() + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str, defines: tuple) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    # Kernel sources never produce or test for NaN (masked logits are -inf and every
+    # -inf - -inf case is guarded), so max/min need no NaN canonicalisation there.
+    # The host API keeps IEEE semantics: it checks scale/gamma with isfinite().
+    extra = ["-fno-honor-nans"] if src.endswith(".hip") else []
+    cmd = [hipcc()] + common_flags() + extra + [f"-D{d}" for d in defines] + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libattn.so; returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, defines: tuple = ()) -> str:
+    """Compile every source and link the library (default: libattn.so here); returns its path.
+
+    `defines` are extra preprocessor definitions (NAME or NAME=VALUE), e.g. to pin a kernel
+    variant in an A/B build written to another path."""
+    build_dir = BUILD_DIR if not defines else BUILD_DIR + "_" + "_".join(d.replace("=", "") for d in defines)
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, build_dir, tuple(defines)), SOURCES))
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -126,7 +126,7 @@ int attn_fwd(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, const v
   int rc = check_args(dt, N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o, lse);
   if (rc != ATTN_OK) return rc;
   if ((long long)N * Hq * L == 0) return ok();
-  const int tile = dt == ATTN_BF16 ? 128 : 64;
+  const int tile = 64;  // smallest query tile of any kernel
   if ((long long)((L + tile - 1) / tile) * N * Hq > kMaxGrid) return fail(ATTN_ERR_SHAPE, "grid too large");
   const attn_impl::FwdArgs a =
       make_args(N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o, lse);

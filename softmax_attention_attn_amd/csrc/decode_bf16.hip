@@ -60,7 +60,8 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) float sO[NWAVE][16][OSTR];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int l16 = lane & 15, g = lane >> 4;
   const int split = blockIdx.x;
   const int kvh = blockIdx.y / p.qgroups, qg = blockIdx.y % p.qgroups;

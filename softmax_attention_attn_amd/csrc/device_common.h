@@ -51,8 +51,20 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 // 2^x on the hardware transcendental unit (v_exp_f32); 2^-inf = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Value held by lane (lane ^ mask) of the wave.
+// Value held by lane (lane ^ mask) of the wave (LDS crossbar; any mask).
 __device__ __forceinline__ float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// max / sum of v over the lane pair {l, l ^ 32} (v_permlane32_swap, no LDS).
+// The swap hands each lane the values of both halves, in some order, which is
+// all a symmetric combine needs.
+__device__ __forceinline__ float pair32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // 16-byte global load that returns zeros when `ok` is false (no access is made then).
 __device__ __forceinline__ u32x4 load16_or_zero(const uint16_t* p, bool ok) {

@@ -25,6 +25,18 @@
 // running state (m = s_h, l = 1: "Attention Sink" section 4.2 -- in the
 // denominator, no value), shifted by gamma|q|^2 in RBF mode so that it competes
 // in the same frame; the LSE is reported for the unfolded logits.
+//
+// Pipeline.  K and V^T tiles are double-buffered in LDS: while tile t is
+// consumed from one buffer, tile t+1 (loaded into registers one tile earlier)
+// is written to the other, so one barrier per tile suffices.  Two workgroups
+// share a CU (2 waves per SIMD), so one wave's softmax overlaps the other's
+// MFMAs.  The running max moves lazily: the accumulator is rescaled only when
+// a row max grows by more than 2^8 over the reference (O = acc / l does not
+// depend on the reference; it only bounds p by 256).  With a positive scale the
+// dot-mode max is taken on the raw scores and each weight costs one fma + exp2.
+// The epilogue transposes O through LDS so that stores are whole rows.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -35,6 +47,7 @@ namespace {
 constexpr int BM = 128;  // query rows per workgroup
 constexpr int BN = 64;   // keys per staged tile
 constexpr int NT = 256;  // threads per workgroup
+constexpr float kLazy = 8.f;  // rescale when a row max grows by more than this (log2 units)
 
 struct PrefillParams {
   const uint16_t* q;
@@ -76,25 +89,39 @@ __device__ __forceinline__ void map_block(int bid, const PrefillParams& p, int& 
   qt = p.heavy_first ? (p.num_q_tiles - 1 - qt_rev) : qt_rev;
 }
 
-template <int E, bool RBF>
+// Softmax front end, fixed per launch:
+//   kDotPos: dot mode, scale > 0 -- max over raw scores, weight = exp2(fma(s, c, -m));
+//   kDotAny: dot mode, any finite scale -- x = c*s first;
+//   kRbf:    x = c*s + bias_k with bias_k = -gamma*log2(e)*|k|^2 from the staged tile.
+enum { kDotPos = 0, kDotAny = 1, kRbf = 2 };
+
+template <int E, int MODE>
 __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(PrefillParams p) {
+  constexpr bool RBF = MODE == kRbf;
+  constexpr bool FAST = MODE == kDotPos;
   constexpr int KSTR = E + 8;   // K tile row stride (elements): +16 B against bank conflicts
   constexpr int VSTR = BN + 8;  // V^T tile row stride (elements)
+  constexpr int OSTR = E + 8;   // epilogue O row stride (elements)
   constexpr int QS = E / 16;    // MFMA steps over the head dimension
   constexpr int EB = E / 32;    // 32-row blocks of O^T
   constexpr int NB = BN / 32;   // 32-key blocks of S^T per tile
   constexpr int ECH = E / 8;    // 16-byte chunks per row
   constexpr int KCH = BN * ECH / NT;          // K chunks staged per thread
   constexpr int VTHREADS = (BN / 4) * ECH;    // threads staging a 4-key x 8-dim block of V
+  constexpr int KTILE = BN * KSTR;
+  constexpr int VTILE = E * VSTR;
   static_assert(KCH * NT == BN * ECH, "K staging must tile evenly");
   static_assert(VTHREADS <= NT, "V staging needs at most one block per thread");
+  static_assert(BM * OSTR <= 2 * (KTILE + VTILE), "epilogue staging must fit the tile buffers");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sVT[E * VSTR];
-  __shared__ __attribute__((aligned(16))) float sBias[BN];
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * (KTILE + VTILE)];
+  __shared__ __attribute__((aligned(16))) float sBias[2][BN];
+  uint16_t* const sK = sKV;                // [2][KTILE]
+  uint16_t* const sVT = sKV + 2 * KTILE;   // [2][VTILE]
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int l32 = lane & 31, g = lane >> 5;
 
   int qt, n, h;
@@ -107,20 +134,21 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(PrefillParams p) {
   const bool qvalid = qi < p.L;
   const int qb = min(qa + 31, p.L - 1);   // last valid row of this wave (qb < qa: none)
 
-  // Q^T fragments: lane holds Q[qi][16s + 8g .. +8] for every step s.
-  const uint16_t* qrow = p.q + (((size_t)n * p.Hq + h) * p.L + (qvalid ? qi : 0)) * E;
+  // Q^T fragments: lane holds Q[qi][16s + 8g .. +8] for every step s.  Rows past
+  // the end read the last row instead (their results are never stored).
+  const uint16_t* qrow = p.q + (((size_t)n * p.Hq + h) * p.L + min(qi, p.L - 1)) * E;
   bf16x8 qf[QS];
   float qn2 = 0.f;
 #pragma unroll
   for (int s = 0; s < QS; ++s) {
-    const u32x4 c = load16_or_zero(qrow + 16 * s + 8 * g, qvalid);
+    const u32x4 c = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * g);
     qf[s] = as_bf16x8(c);
     if (RBF) qn2 += sumsq8(c);
   }
-  if (RBF) qn2 += xor_lane(qn2, 32);
+  if (RBF) qn2 = pair32_sum(qn2);
 
-  // Running state in log2 units.  lsum is this lane's share of the row sum
-  // (its 16 keys per block); the two halves are added in the epilogue.
+  // Running state in log2 units: m is the reference max, lsum this lane's share
+  // of the row sum (its 16 keys per block); the halves are added at the end.
   float m = kNegInf, lsum = 0.f;
   if (p.sink) {
     float s0 = p.sink[h];
@@ -167,35 +195,39 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(PrefillParams p) {
     }
   };
 
+  // Rows past the tile's last key re-read that key (always masked later), so
+  // every load is unconditional and in bounds.
   auto load_tile = [&](int t) {
     int j0, kc;
     tile_keys(t, j0, kc);
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int id = tid + NT * i;
-      const int row = id / ECH, c = id % ECH;
-      kreg[i] = load16_or_zero(kbase + (size_t)(j0 + row) * E + 8 * c, row < kc);
+      const int row = min(id / ECH, kc - 1), c = id % ECH;
+      kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)(j0 + row) * E + 8 * c);
     }
     if (vrole) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const int row = 4 * va + ii;
-        vreg[ii] = load16_or_zero(vbase + (size_t)(j0 + row) * E + 8 * vc, row < kc);
+        const int row = min(4 * va + ii, kc - 1);
+        vreg[ii] = *reinterpret_cast<const u32x4*>(vbase + (size_t)(j0 + row) * E + 8 * vc);
       }
     }
   };
 
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
+    uint16_t* k_s = sK + buf * KTILE;
+    uint16_t* v_s = sVT + buf * VTILE;
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int id = tid + NT * i;
       const int row = id / ECH, c = id % ECH;
-      *reinterpret_cast<u32x4*>(&sK[row * KSTR + 8 * c]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&k_s[row * KSTR + 8 * c]) = kreg[i];
       if (RBF) {
         float ss = sumsq8(kreg[i]);
 #pragma unroll
         for (int o = 1; o < ECH; o <<= 1) ss += xor_lane(ss, o);
-        if (c == 0) sBias[row] = p.c_bias * ss;
+        if (c == 0) sBias[buf][row] = p.c_bias * ss;
       }
     }
     if (vrole) {
@@ -205,17 +237,23 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(PrefillParams p) {
         const uint32_t e0 = (vreg[0][w] >> sh) & 0xffffu, e1 = (vreg[1][w] >> sh) & 0xffffu;
         const uint32_t e2 = (vreg[2][w] >> sh) & 0xffffu, e3 = (vreg[3][w] >> sh) & 0xffffu;
         u32x2 d = {e0 | (e1 << 16), e2 | (e3 << 16)};
-        *reinterpret_cast<u32x2*>(&sVT[(8 * vc + j) * VSTR + vpos]) = d;
+        *reinterpret_cast<u32x2*>(&v_s[(8 * vc + j) * VSTR + vpos]) = d;
       }
     }
   };
 
-  auto compute_tile = [&](int t) {
+  // MASKED is a compile-time flag: false only for tiles every row of the
+  // workgroup sees completely, whose code then carries no visibility test.
+  auto compute_tile = [&](int t, int buf, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     int j0, kc;
     tile_keys(t, j0, kc);
     const bool is_reg = t < n_reg_tiles;
     bool any, full;
-    if (qb < qa) {
+    if (!MASKED) {
+      any = qb >= qa;
+      full = true;
+    } else if (qb < qa) {
       any = false;
       full = false;
     } else if (is_reg) {
@@ -229,62 +267,92 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(PrefillParams p) {
              (p.window <= 0 || qb + p.off - ra < p.window);
     }
     if (!any) return;
+    const uint16_t* k_s = sK + buf * KTILE;
+    const uint16_t* v_s = sVT + buf * VTILE;
 
-    // S^T = K * Q^T for NB blocks of 32 keys.
+    // S^T = K * Q^T for NB blocks of 32 keys; the NB accumulation chains are
+    // interleaved so that consecutive MFMAs never depend on each other.
     f32x16 st[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[b][r] = 0.f;
 #pragma unroll
-      for (int s = 0; s < QS; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sK[(32 * b + l32) * KSTR + 16 * s + 8 * g]);
-        st[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st[b], 0, 0, 0);
-      }
+    for (int s = 0; s < QS; ++s) {
+      bf16x8 a[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        a[b] = *reinterpret_cast<const bf16x8*>(&k_s[(32 * b + l32) * KSTR + 16 * s + 8 * g]);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) st[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[b], qf[s], st[b], 0, 0, 0);
     }
 
-    // Logits (log2 units), penalty, visibility; the accumulator row of register
-    // r in block b is key 32b + 8(r/4) + 4g + r%4 of the tile.
+    // Accumulator row of register r in block b = key 32b + 8(r/4) + 4g + r%4 of
+    // the tile.  FAST keeps raw scores (the scale goes into the exponent);
+    // otherwise the scores become log2-unit logits here.
+    if (!FAST) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = st[b][r] * p.c_logit;
+          if (RBF) x += sBias[buf][32 * b + 8 * (r >> 2) + 4 * g + (r & 3)];
+          st[b][r] = x;
+        }
+    }
+    if (MASKED && !full) {
+      // Visible keys of this lane's row form one interval [lo, hi] of tile
+      // offsets; the offset of register r is its compile-time key minus 4g.
+      int lo, hi;
+      if (is_reg) {
+        lo = 0;
+        hi = kc - 1;
+      } else {
+        const int base = j0 - p.n_reg;  // real position of tile key 0
+        const int ip = qi + p.off;      // this row's aligned position
+        hi = min(p.S_real - 1, p.causal ? ip : p.S_real - 1) - base;
+        lo = (p.window > 0 ? ip - p.window + 1 : 0) - base;
+      }
+      lo -= 4 * g;
+      hi -= 4 * g;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ko = 32 * b + 8 * (r >> 2) + (r & 3);
+          const bool vis = (ko >= lo) & (ko <= hi);
+          st[b][r] = vis ? st[b][r] : kNegInf;
+        }
+    }
     float mx = kNegInf;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kt = 32 * b + 8 * (r >> 2) + 4 * g + (r & 3);
-        float x = st[b][r] * p.c_logit;
-        if (RBF) x += sBias[kt];
-        if (!full) {
-          bool vis;
-          if (is_reg) {
-            vis = kt < kc;
-          } else {
-            const int rr = j0 - p.n_reg + kt;
-            vis = rr < p.S_real && (!p.causal || rr <= qi + p.off) &&
-                  (p.window <= 0 || qi + p.off - rr < p.window);
-          }
-          if (!vis) x = kNegInf;
-        }
-        st[b][r] = x;
-        mx = fmaxf(mx, x);
-      }
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(st[b][r], st[b][r + 1]));
+    mx = pair32_max(mx);
+    if (FAST) mx = (mx == kNegInf) ? kNegInf : mx * p.c_logit;
+
+    // Lazy reference max: move it (and rescale) only when a row max would grow
+    // by more than kLazy; otherwise weights stay below 2^kLazy.
+    if (__any(mx > m + kLazy)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m - m_new);
+      m = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int c = 0; c < EB; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[c][r] *= alpha;
     }
-    mx = fmaxf(mx, xor_lane(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    m = m_new;
-    lsum *= alpha;
-#pragma unroll
-    for (int c = 0; c < EB; ++c)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[c][r] *= alpha;
+    const float m_use = (m == kNegInf) ? 0.f : m;
 
     float ps = 0.f;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pv = fast_exp2(st[b][r] - m_use);
+        const float pv = FAST ? fast_exp2(__builtin_fmaf(st[b][r], p.c_logit, -m_use))
+                              : fast_exp2(st[b][r] - m_use);
         st[b][r] = pv;
         ps += pv;
       }
@@ -301,51 +369,105 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(PrefillParams p) {
         const int u = 2 * b + s2;
 #pragma unroll
         for (int c = 0; c < EB; ++c) {
-          const bf16x8 vt = *reinterpret_cast<const bf16x8*>(&sVT[(32 * c + l32) * VSTR + 16 * u + 8 * g]);
+          const bf16x8 vt = *reinterpret_cast<const bf16x8*>(&v_s[(32 * c + l32) * VSTR + 16 * u + 8 * g]);
           acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pf, acc[c], 0, 0, 0);
         }
       }
     }
   };
 
-  if (T > 0) load_tile(0);
-  for (int t = 0; t < T; ++t) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < T) load_tile(t + 1);
-    compute_tile(t);
+  // Tile t lives in buffer t % 2.  Iteration t computes it while tile t+1
+  // (already in registers) goes to the other buffer and tile t+2 is loaded.
+  // Real tiles k in [k_full0, k_full1] are seen completely by every row of the
+  // workgroup and run without visibility code; the tiles before and after them
+  // (and the register tiles) run with it.
+  int k_full0 = 0, k_full1 = -1;
+  {
+    const int lim = min(p.S_real - 1, p.causal ? i0 + p.off : p.S_real - 1);
+    k_full1 = (lim - r_lo - (BN - 1)) >= 0 ? (lim - r_lo - (BN - 1)) / BN : -1;
+    if (p.window > 0) {
+      const int need = i_last + p.off - p.window + 1 - r_lo;  // first ra allowed
+      k_full0 = need > 0 ? (need + BN - 1) / BN : 0;
+    }
+    k_full1 = min(k_full1, n_real_tiles - 1);
+    if (k_full0 > k_full1) {
+      k_full0 = 0;
+      k_full1 = -1;
+    }
   }
+  const int t_full0 = n_reg_tiles + k_full0, t_full1 = n_reg_tiles + k_full1 + 1;  // [t_full0, t_full1)
 
-  // Epilogue: O = acc / l (0 for an empty row), LSE in natural-log units.
-  const float ltot = lsum + xor_lane(lsum, 32);
-  if (qvalid) {
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    uint16_t* orow = p.o + (((size_t)n * p.Hq + h) * p.L + qi) * E;
+  auto step = [&](int t, auto masked_tag) {
+    compute_tile(t, t & 1, masked_tag);
+    if (t + 1 < T) {
+      store_tile((t + 1) & 1);
+      if (t + 2 < T) load_tile(t + 2);
+    }
+    __syncthreads();
+  };
+
+  if (T > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  // Q and tile 0 have landed (the stores above consumed tile 0; loads return in
+  // order).  Say so explicitly, so that no wait on the Q registers is left
+  // inside the loop, where it would also wait for the prefetch of later tiles.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt and lgkmcnt untouched
+  if (T > 1) load_tile(1);
+  __syncthreads();
+  const int head_end = (t_full1 > t_full0) ? t_full0 : T;
+  for (int t = 0; t < head_end; ++t) step(t, std::true_type{});
+  for (int t = head_end; t < t_full1; ++t) step(t, std::false_type{});
+  for (int t = max(head_end, t_full1); t < T; ++t) step(t, std::true_type{});
+
+  // Epilogue: O = acc / l (0 for an empty row) staged through LDS (free after
+  // the last barrier) so that global stores are whole rows; LSE in natural log.
+  const float ltot = pair32_sum(lsum);
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  uint16_t* sO = sKV + wave * 32 * OSTR;
 #pragma unroll
-    for (int c = 0; c < EB; ++c)
+  for (int c = 0; c < EB; ++c)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const bf16x4 pk = pack_bf16x4(acc[c][4 * rq + 0] * inv, acc[c][4 * rq + 1] * inv,
-                                      acc[c][4 * rq + 2] * inv, acc[c][4 * rq + 3] * inv);
-        *reinterpret_cast<bf16x4*>(orow + 32 * c + 8 * rq + 4 * g) = pk;
-      }
-    if (g == 0) {
-      float l = kNegInf;
-      if (ltot > 0.f) {
-        l = (m + log2f(ltot)) * kLn2;
-        if (RBF) l -= p.gamma * qn2;
-      }
-      p.lse[((size_t)n * p.Hq + h) * p.L + qi] = l;
+    for (int rq = 0; rq < 4; ++rq) {
+      const bf16x4 pk = pack_bf16x4(acc[c][4 * rq + 0] * inv, acc[c][4 * rq + 1] * inv,
+                                    acc[c][4 * rq + 2] * inv, acc[c][4 * rq + 3] * inv);
+      *reinterpret_cast<bf16x4*>(&sO[l32 * OSTR + 32 * c + 8 * rq + 4 * g]) = pk;
+    }
+  if (g == 0 && qvalid) {
+    float l = kNegInf;
+    if (ltot > 0.f) {
+      l = (m + log2f(ltot)) * kLn2;
+      if (RBF) l -= p.gamma * qn2;
+    }
+    p.lse[((size_t)n * p.Hq + h) * p.L + qi] = l;
+  }
+  __syncthreads();
+  const size_t obase = ((size_t)n * p.Hq + h) * p.L;
+#pragma unroll
+  for (int it = 0; it < (32 * ECH) / 64; ++it) {
+    const int id = lane + 64 * it;
+    const int rloc = id / ECH, c = id % ECH;
+    const int row = qa + rloc;
+    if (row < p.L) {
+      const u32x4 val = *reinterpret_cast<const u32x4*>(&sO[rloc * OSTR + 8 * c]);
+      *reinterpret_cast<u32x4*>(p.o + (obase + row) * E + 8 * c) = val;
     }
   }
 }
 
-template <int E, bool RBF>
+template <int E, int MODE>
 hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
   const long long blocks = (long long)p.num_q_tiles * p.N * p.Hq;
-  hipLaunchKernelGGL((prefill_bf16_kernel<E, RBF>), dim3((unsigned)blocks), dim3(NT), 0, stream, p);
+  hipLaunchKernelGGL((prefill_bf16_kernel<E, MODE>), dim3((unsigned)blocks), dim3(NT), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int E>
+hipError_t launch_e(const PrefillParams& p, bool rbf, hipStream_t stream) {
+  if (rbf) return launch_t<E, kRbf>(p, stream);
+  if (p.c_logit > 0.f) return launch_t<E, kDotPos>(p, stream);
+  return launch_t<E, kDotAny>(p, stream);
 }
 
 }  // namespace
@@ -381,8 +503,8 @@ hipError_t launch_prefill_bf16(const FwdArgs& a, hipStream_t stream) {
   p.num_q_tiles = (a.L + BM - 1) / BM;
   p.xcd_groups = ((a.N * a.Hkv) % 8 == 0) ? 1 : 0;
   p.heavy_first = p.causal;
-  if (a.E == 128) return a.rbf ? launch_t<128, true>(p, stream) : launch_t<128, false>(p, stream);
-  return a.rbf ? launch_t<64, true>(p, stream) : launch_t<64, false>(p, stream);
+  if (a.E == 128) return launch_e<128>(p, a.rbf != 0, stream);
+  return launch_e<64>(p, a.rbf != 0, stream);
 }
 
 }  // namespace attn_impl
