@@ -130,8 +130,7 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams p) {
         // |k|^2 of key vb + 16b + l16, then fetched for keys 4g + r.
 #pragma unroll
         for (int s = 0; s < QS; ++s) nk += sumsq8(kr[b][s]);
-        nk += xor_lane(nk, 16);
-        nk += xor_lane(nk, 32);
+        nk = pair32_sum(pair16_sum(nk));
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -142,8 +141,7 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams p) {
         mx = fmaxf(mx, xv);
       }
     }
-    mx = fmaxf(mx, xor_lane(mx, 16));
-    mx = fmaxf(mx, xor_lane(mx, 32));
+    mx = pair32_max(pair16_max(mx));
     const float m_new = fmaxf(m, mx);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
     const float alpha = fast_exp2(m - m_use);

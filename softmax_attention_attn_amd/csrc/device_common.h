@@ -34,6 +34,22 @@ __device__ __forceinline__ float sumsq8(u32x4 c) {
   return s;
 }
 
+// Sum of v over aligned groups of N consecutive lanes (N = 8 or 16), result in
+// every lane of the group; DPP row permutes, no LDS traffic.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp_mov<0x141>(v);  // row_half_mirror: the other quad of the 8
+  if (N == 16) v += dpp_mov<0x140>(v);  // row_mirror: the other 8 of the row
+  return v;
+}
+
 // Round 8 floats to bf16 (nearest-even, v_cvt_pk_bf16_f32) as an MFMA operand.
 __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3,
                                               float a4, float a5, float a6, float a7) {
@@ -64,6 +80,31 @@ __device__ __forceinline__ float pair32_max(float v) {
 __device__ __forceinline__ float pair32_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Same for the pair {l, l ^ 16} (v_permlane16_swap).
+__device__ __forceinline__ float pair16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw addressing, gfx9 data format
+// word).  Loads through it whose byte offset lies at or past `bytes` return
+// zeros without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+
+// Two bf16 halves (low halves when hi == false, else high halves) of a and b
+// packed as {a_half, b_half} (v_perm_b32).
+__device__ __forceinline__ uint32_t pack_halves(uint32_t a, uint32_t b, bool hi) {
+  return __builtin_amdgcn_perm(b, a, hi ? 0x07060302u : 0x05040100u);
 }
 
 // 16-byte global load that returns zeros when `ok` is false (no access is made then).

@@ -95,8 +95,16 @@ __device__ __forceinline__ void map_block(int bid, const PrefillParams& p, int& 
 //   kRbf:    x = c*s + bias_k with bias_k = -gamma*log2(e)*|k|^2 from the staged tile.
 enum { kDotPos = 0, kDotAny = 1, kRbf = 2 };
 
+// Waves per SIMD the register budget allows: E = 128 needs ~230 VGPRs (2 waves),
+// E = 64 fits under 168 (3 waves, i.e. 3 workgroups per CU).
+template <int E>
+struct Occupancy {
+  static constexpr int kWaves = E == 64 ? 3 : 2;
+};
+
 template <int E, int MODE>
-__global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(PrefillParams p) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Occupancy<E>::kWaves, Occupancy<E>::kWaves)))
+void prefill_bf16_kernel(PrefillParams p) {
   constexpr bool RBF = MODE == kRbf;
   constexpr bool FAST = MODE == kDotPos;
   constexpr int KSTR = E + 8;   // K tile row stride (elements): +16 B against bank conflicts
@@ -170,9 +178,11 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(PrefillParams p) {
   const int n_reg_tiles = (p.n_reg + BN - 1) / BN;
   const int T = n_reg_tiles + n_real_tiles;
 
+  // K and V of this (batch, kv head): one buffer resource each over exactly the
+  // S rows of the slice, so rows past the end load as zeros.
   const size_t kvoff = ((size_t)n * p.Hkv + kh) * (size_t)p.S * E;
-  const uint16_t* kbase = p.k + kvoff;
-  const uint16_t* vbase = p.v + kvoff;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + kvoff, (uint32_t)p.S * E * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + kvoff, (uint32_t)p.S * E * 2);
 
   // Staging roles.  K: chunk id = tid + NT*i is row id/ECH, dims 8*(id%ECH)..+8.
   // V: thread (va, vc) stages rows 4va..4va+3, dims 8vc..8vc+7, transposed.
@@ -195,23 +205,27 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(PrefillParams p) {
     }
   };
 
-  // Rows past the tile's last key re-read that key (always masked later), so
-  // every load is unconditional and in bounds.
+  // Byte offsets within a tile of this thread's K chunks and V rows.  Rows past
+  // the tile's last key are loaded anyway (they are real keys of the slice, or
+  // zeros past its end) and masked in the softmax.
+  uint32_t koff[KCH], voff[4];
+#pragma unroll
+  for (int i = 0; i < KCH; ++i) {
+    const int id = tid + NT * i;
+    koff[i] = (uint32_t)((id / ECH) * E * 2 + 16 * (id % ECH));
+  }
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) voff[ii] = (uint32_t)((4 * va + ii) * E * 2 + 16 * vc);
+
   auto load_tile = [&](int t) {
     int j0, kc;
     tile_keys(t, j0, kc);
+    const uint32_t tb = (uint32_t)j0 * E * 2;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int id = tid + NT * i;
-      const int row = min(id / ECH, kc - 1), c = id % ECH;
-      kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)(j0 + row) * E + 8 * c);
-    }
+    for (int i = 0; i < KCH; ++i) kreg[i] = buffer_load16(krs, tb + koff[i]);
     if (vrole) {
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int row = min(4 * va + ii, kc - 1);
-        vreg[ii] = *reinterpret_cast<const u32x4*>(vbase + (size_t)(j0 + row) * E + 8 * vc);
-      }
+      for (int ii = 0; ii < 4; ++ii) vreg[ii] = buffer_load16(vrs, tb + voff[ii]);
     }
   };
 
@@ -224,19 +238,17 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(PrefillParams p) {
       const int row = id / ECH, c = id % ECH;
       *reinterpret_cast<u32x4*>(&k_s[row * KSTR + 8 * c]) = kreg[i];
       if (RBF) {
-        float ss = sumsq8(kreg[i]);
-#pragma unroll
-        for (int o = 1; o < ECH; o <<= 1) ss += xor_lane(ss, o);
+        // |k|^2 of this key row: its ECH chunks sit in ECH consecutive lanes.
+        const float ss = group_sum<ECH>(sumsq8(kreg[i]));
         if (c == 0) sBias[buf][row] = p.c_bias * ss;
       }
     }
     if (vrole) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int w = j >> 1, sh = (j & 1) * 16;
-        const uint32_t e0 = (vreg[0][w] >> sh) & 0xffffu, e1 = (vreg[1][w] >> sh) & 0xffffu;
-        const uint32_t e2 = (vreg[2][w] >> sh) & 0xffffu, e3 = (vreg[3][w] >> sh) & 0xffffu;
-        u32x2 d = {e0 | (e1 << 16), e2 | (e3 << 16)};
+        const int w = j >> 1;
+        const bool hi = j & 1;
+        u32x2 d = {pack_halves(vreg[0][w], vreg[1][w], hi), pack_halves(vreg[2][w], vreg[3][w], hi)};
         *reinterpret_cast<u32x2*>(&v_s[(8 * vc + j) * VSTR + vpos]) = d;
       }
     }
