@@ -126,8 +126,10 @@ int attn_fwd(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, const v
   int rc = check_args(dt, N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o, lse);
   if (rc != ATTN_OK) return rc;
   if ((long long)N * Hq * L == 0) return ok();
-  if (dt == ATTN_BF16 && (long long)S * E * 2 > 0x7fffffffLL)
-    return fail(ATTN_ERR_UNSUPPORTED, "a (batch, kv head) slice of K/V above 2 GiB (S=%d, E=%d)", S, E);
+  // bf16 tiles are addressed with 32-bit byte offsets into one (batch, kv head)
+  // slice, including one tile of rows past its end.
+  if (dt == ATTN_BF16 && ((long long)S + 64) * E * 2 > 0x7fffffffLL)
+    return fail(ATTN_ERR_UNSUPPORTED, "a (batch, kv head) slice of K/V near or above 2 GiB (S=%d, E=%d)", S, E);
   const int tile = 64;  // smallest query tile of any kernel
   if ((long long)((L + tile - 1) / tile) * N * Hq > kMaxGrid) return fail(ATTN_ERR_SHAPE, "grid too large");
   const attn_impl::FwdArgs a =

@@ -12,9 +12,11 @@
 // row max and the rescale factor are then per-lane scalars; only one exchange
 // with lane^32 (the other half of the same query's keys) is needed per tile.
 // The output is accumulated the same way, O^T = V^T * P^T: P^T comes straight
-// from the S^T registers (rounded to bf16), V^T is read from an LDS copy of the
-// V tile that was transposed while staging, with its keys permuted into the
-// order in which the S^T accumulator hands them to each lane.
+// from the S^T registers (rounded to bf16), and the V^T operand is gathered
+// from the row-major V tile by ds_read_b64_tr_b16 (transposing LDS read: in
+// each 16-lane group, lane j's element e is element j%4 of the 8-byte row piece
+// addressed by lane 4e + j/4), pointed at the keys in the order in which the
+// S^T accumulator hands them to each lane.
 //
 // Logits are kept in log2 units: x = c_logit * (q.k) + c_bias * |k|^2 with
 //   dot: c_logit = scale*log2(e),     c_bias = 0
@@ -26,11 +28,16 @@
 // denominator, no value), shifted by gamma|q|^2 in RBF mode so that it competes
 // in the same frame; the LSE is reported for the unfolded logits.
 //
-// Pipeline.  K and V^T tiles are double-buffered in LDS: while tile t is
-// consumed from one buffer, tile t+1 (loaded into registers one tile earlier)
-// is written to the other, so one barrier per tile suffices.  Two workgroups
-// share a CU (2 waves per SIMD), so one wave's softmax overlaps the other's
-// MFMAs.  The running max moves lazily: the accumulator is rescaled only when
+// Pipeline.  K and V tiles are double-buffered in LDS and filled by
+// LDS-direct buffer loads (no register round trip, rows past the end of the
+// slice arrive as zeros): right after the barrier that frees buffer (t+1)%2,
+// tile t+1 is requested; tile t is consumed meanwhile; each wave waits for its
+// own requests before the next barrier, so one barrier per tile suffices.  In
+// RBF mode K still goes through registers, where |k|^2 is formed on its way to
+// LDS.  Tiles are stored row-major with the 16-byte chunks of row r permuted by
+// an XOR with swz(r), which keeps both the K reads (16 rows, one chunk) and the
+// transposing V reads (4 rows, two chunks) free of bank conflicts.  Several
+// workgroups share a CU, so one wave's softmax overlaps another's MFMAs.  The running max moves lazily: the accumulator is rescaled only when
 // a row max grows by more than 2^8 over the reference (O = acc / l does not
 // depend on the reference; it only bounds p by 256).  With a positive scale the
 // dot-mode max is taken on the raw scores and each weight costs one fma + exp2.
@@ -95,6 +102,48 @@ __device__ __forceinline__ void map_block(int bid, const PrefillParams& p, int& 
 //   kRbf:    x = c*s + bias_k with bias_k = -gamma*log2(e)*|k|^2 from the staged tile.
 enum { kDotPos = 0, kDotAny = 1, kRbf = 2 };
 
+// XOR permutation of the 16-byte chunks of tile row r (K and V tiles are
+// row-major, E*2 bytes per row).  E = 128: 16 consecutive rows map one chunk to
+// 16 different chunk slots (conflict-free K reads), and the 4 consecutive rows x
+// 4 chunks that a transposing V read touches in each half-wave land in 16
+// different slots.  E = 64 (two rows share a 64-bank span): the same two
+// properties per bank half.
+template <int E>
+__device__ __forceinline__ int tile_swz(int r) {
+  if (E == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+// The two helpers below wrap gfx950 builtins that take LDS pointers.  Their
+// bodies exist only in the device compilation pass: in the host pass clang
+// otherwise drops the launch stubs of the kernel templates that use them
+// (the host pass never executes device code; it only needs the declarations).
+
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16) at byte address a.
+__device__ __forceinline__ shortx4 lds_read_tr(const uint8_t* a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4*)(const_cast<uint8_t*>(a)));
+#else
+  (void)a;
+  return shortx4{0, 0, 0, 0};
+#endif
+}
+
+// Wave-wide LDS-direct load: lane l's 16 bytes at byte offset `off` of the
+// buffer land at lds + 16*l (zeros if `off` is past the buffer's range).
+__device__ __forceinline__ void buffer_load16_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, (int)off, 0, 0, 0);
+#else
+  (void)r;
+  (void)lds;
+  (void)off;
+#endif
+}
+
 // Waves per SIMD the register budget allows: E = 128 needs ~230 VGPRs (2 waves),
 // E = 64 fits under 168 (3 waves, i.e. 3 workgroups per CU).
 template <int E>
@@ -107,25 +156,25 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Occupancy<E>
 void prefill_bf16_kernel(PrefillParams p) {
   constexpr bool RBF = MODE == kRbf;
   constexpr bool FAST = MODE == kDotPos;
-  constexpr int KSTR = E + 8;   // K tile row stride (elements): +16 B against bank conflicts
-  constexpr int VSTR = BN + 8;  // V^T tile row stride (elements)
   constexpr int OSTR = E + 8;   // epilogue O row stride (elements)
   constexpr int QS = E / 16;    // MFMA steps over the head dimension
   constexpr int EB = E / 32;    // 32-row blocks of O^T
   constexpr int NB = BN / 32;   // 32-key blocks of S^T per tile
   constexpr int ECH = E / 8;    // 16-byte chunks per row
-  constexpr int KCH = BN * ECH / NT;          // K chunks staged per thread
-  constexpr int VTHREADS = (BN / 4) * ECH;    // threads staging a 4-key x 8-dim block of V
-  constexpr int KTILE = BN * KSTR;
-  constexpr int VTILE = E * VSTR;
+  constexpr int ROWB = E * 2;   // bytes per K/V row
+  constexpr int TILEB = BN * ROWB;         // bytes per K (or V) tile
+  constexpr int RPI = 1024 / ROWB;         // rows per 1 KB wave-wide LDS-direct load
+  constexpr int IPW = BN / RPI / 4;        // such loads per wave per tile (4 waves)
+  constexpr int KCH = BN * ECH / NT;       // K chunks per thread (RBF register staging)
+  static_assert(IPW * RPI * 4 == BN, "tile must split into whole 1 KB loads per wave");
   static_assert(KCH * NT == BN * ECH, "K staging must tile evenly");
-  static_assert(VTHREADS <= NT, "V staging needs at most one block per thread");
-  static_assert(BM * OSTR <= 2 * (KTILE + VTILE), "epilogue staging must fit the tile buffers");
+  static_assert(BM * OSTR * 2 <= 2 * 2 * TILEB, "epilogue staging must fit the tile buffers");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * (KTILE + VTILE)];
+  // [buf][K tile | V tile], each tile row-major with swizzled 16-byte chunks.
+  __shared__ __attribute__((aligned(16))) uint8_t sKV[2 * 2 * TILEB];
   __shared__ __attribute__((aligned(16))) float sBias[2][BN];
-  uint16_t* const sK = sKV;                // [2][KTILE]
-  uint16_t* const sVT = sKV + 2 * KTILE;   // [2][VTILE]
+  auto k_tile = [&](int buf) { return sKV + buf * 2 * TILEB; };
+  auto v_tile = [&](int buf) { return sKV + buf * 2 * TILEB + TILEB; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -181,19 +230,39 @@ void prefill_bf16_kernel(PrefillParams p) {
   // K and V of this (batch, kv head): one buffer resource each over exactly the
   // S rows of the slice, so rows past the end load as zeros.
   const size_t kvoff = ((size_t)n * p.Hkv + kh) * (size_t)p.S * E;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + kvoff, (uint32_t)p.S * E * 2);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + kvoff, (uint32_t)p.S * E * 2);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + kvoff, (uint32_t)p.S * ROWB);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + kvoff, (uint32_t)p.S * ROWB);
 
-  // Staging roles.  K: chunk id = tid + NT*i is row id/ECH, dims 8*(id%ECH)..+8.
-  // V: thread (va, vc) stages rows 4va..4va+3, dims 8vc..8vc+7, transposed.
-  const int va = tid % (BN / 4), vc = tid / (BN / 4);
-  const bool vrole = tid < VTHREADS;
-  // Position of key quad va in the permuted V^T row: within each 16-key group the
-  // order is keys {0-3, 8-11, 4-7, 12-15}, i.e. lane half g of the PV operand
-  // reads keys {4g..4g+3, 8+4g..8+4g+3} as 8 consecutive elements.
-  const int vpos = 16 * (va >> 2) + ((va & 1) ? 8 : 0) + ((va & 2) ? 4 : 0);
+  // LDS-direct loads: this wave's block b of a tile is rows RPI*(IPW*wave + b) ..;
+  // lane l fills physical chunk l % ECH of row l / ECH, i.e. logical chunk
+  // (l % ECH) ^ swz(row) of the global row.
+  uint32_t ld_off[IPW];
+#pragma unroll
+  for (int b = 0; b < IPW; ++b) {
+    const int row = RPI * (IPW * wave + b) + lane / ECH;
+    ld_off[b] = (uint32_t)(row * ROWB + (((lane % ECH) ^ tile_swz<E>(row)) * 16));
+  }
+  // K operand reads: row l32 (+32 for block 1), logical chunk 2s + g.
+  uint32_t krd[QS];
+#pragma unroll
+  for (int s = 0; s < QS; ++s) krd[s] = (uint32_t)(l32 * ROWB + (((2 * s + g) ^ tile_swz<E>(l32)) * 16));
+  // V^T operand reads (transposing): lane m of 16-lane group q points at key
+  // row 4*(q/2) + (m%16)/4 (+8 for the second half of the operand) of the
+  // current 16-key group, dims 32c + 16*(q%2) + 4*(m%4) .. +4.
+  uint32_t vrd[EB][2];
+  {
+    const int q16 = lane >> 4, m16 = lane & 15;
+#pragma unroll
+    for (int c = 0; c < EB; ++c)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int row = 4 * (q16 >> 1) + (m16 >> 2) + 8 * hh;
+        const int d = 32 * c + 16 * (q16 & 1) + 4 * (m16 & 3);
+        vrd[c][hh] = (uint32_t)(row * ROWB + (((d >> 3) ^ tile_swz<E>(row)) * 16) + (d & 7) * 2);
+      }
+  }
 
-  u32x4 kreg[KCH], vreg[4];
+  u32x4 kreg[KCH];  // RBF only: K chunks on their way to LDS
 
   auto tile_keys = [&](int t, int& j0, int& kc) {
     if (t < n_reg_tiles) {
@@ -205,57 +274,45 @@ void prefill_bf16_kernel(PrefillParams p) {
     }
   };
 
-  // Byte offsets within a tile of this thread's K chunks and V rows.  Rows past
-  // the tile's last key are loaded anyway (they are real keys of the slice, or
-  // zeros past its end) and masked in the softmax.
-  uint32_t koff[KCH], voff[4];
-#pragma unroll
-  for (int i = 0; i < KCH; ++i) {
-    const int id = tid + NT * i;
-    koff[i] = (uint32_t)((id / ECH) * E * 2 + 16 * (id % ECH));
-  }
-#pragma unroll
-  for (int ii = 0; ii < 4; ++ii) voff[ii] = (uint32_t)((4 * va + ii) * E * 2 + 16 * vc);
-
-  auto load_tile = [&](int t) {
+  // Request tile t into buffer `buf`.  Rows past the tile's last key are loaded
+  // anyway (real keys of the slice, or zeros past its end) and masked later.
+  auto issue_tile = [&](int t, int buf) {
     int j0, kc;
     tile_keys(t, j0, kc);
-    const uint32_t tb = (uint32_t)j0 * E * 2;
+    const uint32_t tb = (uint32_t)j0 * ROWB;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) kreg[i] = buffer_load16(krs, tb + koff[i]);
-    if (vrole) {
+    for (int b = 0; b < IPW; ++b) {
+      const int blk = IPW * wave + b;
+      buffer_load16_to_lds(vrs, v_tile(buf) + blk * 1024, tb + ld_off[b]);
+      if (!RBF) buffer_load16_to_lds(krs, k_tile(buf) + blk * 1024, tb + ld_off[b]);
+    }
+    if (RBF) {
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) vreg[ii] = buffer_load16(vrs, tb + voff[ii]);
+      for (int i = 0; i < KCH; ++i) {
+        const int id = tid + NT * i;
+        kreg[i] = buffer_load16(krs, tb + (uint32_t)((id / ECH) * ROWB + (id % ECH) * 16));
+      }
     }
   };
 
-  auto store_tile = [&](int buf) {
-    uint16_t* k_s = sK + buf * KTILE;
-    uint16_t* v_s = sVT + buf * VTILE;
+  // Complete the requested tile in `buf`: in RBF mode write the K registers
+  // (swizzled) and the per-key bias c_bias * |k|^2; then wait until this wave's
+  // LDS-direct requests have landed.
+  auto finish_tile = [&](int buf) {
+    if (RBF) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int id = tid + NT * i;
-      const int row = id / ECH, c = id % ECH;
-      *reinterpret_cast<u32x4*>(&k_s[row * KSTR + 8 * c]) = kreg[i];
-      if (RBF) {
+      for (int i = 0; i < KCH; ++i) {
+        const int id = tid + NT * i;
+        const int row = id / ECH, c = id % ECH;
+        *reinterpret_cast<u32x4*>(k_tile(buf) + row * ROWB + ((c ^ tile_swz<E>(row)) * 16)) = kreg[i];
         // |k|^2 of this key row: its ECH chunks sit in ECH consecutive lanes.
         const float ss = group_sum<ECH>(sumsq8(kreg[i]));
         if (c == 0) sBias[buf][row] = p.c_bias * ss;
       }
     }
-    if (vrole) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int w = j >> 1;
-        const bool hi = j & 1;
-        u32x2 d = {pack_halves(vreg[0][w], vreg[1][w], hi), pack_halves(vreg[2][w], vreg[3][w], hi)};
-        *reinterpret_cast<u32x2*>(&v_s[(8 * vc + j) * VSTR + vpos]) = d;
-      }
-    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   };
 
-  // MASKED is a compile-time flag: false only for tiles every row of the
-  // workgroup sees completely, whose code then carries no visibility test.
   auto compute_tile = [&](int t, int buf, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     int j0, kc;
@@ -279,8 +336,8 @@ void prefill_bf16_kernel(PrefillParams p) {
              (p.window <= 0 || qb + p.off - ra < p.window);
     }
     if (!any) return;
-    const uint16_t* k_s = sK + buf * KTILE;
-    const uint16_t* v_s = sVT + buf * VTILE;
+    const uint8_t* k_s = k_tile(buf);
+    const uint8_t* v_s = v_tile(buf);
 
     // S^T = K * Q^T for NB blocks of 32 keys; the NB accumulation chains are
     // interleaved so that consecutive MFMAs never depend on each other.
@@ -294,7 +351,7 @@ void prefill_bf16_kernel(PrefillParams p) {
       bf16x8 a[NB];
 #pragma unroll
       for (int b = 0; b < NB; ++b)
-        a[b] = *reinterpret_cast<const bf16x8*>(&k_s[(32 * b + l32) * KSTR + 16 * s + 8 * g]);
+        a[b] = *reinterpret_cast<const bf16x8*>(k_s + krd[s] + 32 * b * ROWB);
 #pragma unroll
       for (int b = 0; b < NB; ++b) st[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[b], qf[s], st[b], 0, 0, 0);
     }
@@ -381,15 +438,15 @@ void prefill_bf16_kernel(PrefillParams p) {
         const int u = 2 * b + s2;
 #pragma unroll
         for (int c = 0; c < EB; ++c) {
-          const bf16x8 vt = *reinterpret_cast<const bf16x8*>(&v_s[(32 * c + l32) * VSTR + 16 * u + 8 * g]);
+          const shortx4 lo = lds_read_tr(v_s + vrd[c][0] + 16 * u * ROWB);
+          const shortx4 hi = lds_read_tr(v_s + vrd[c][1] + 16 * u * ROWB);
+          const bf16x8 vt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pf, acc[c], 0, 0, 0);
         }
       }
     }
   };
 
-  // Tile t lives in buffer t % 2.  Iteration t computes it while tile t+1
-  // (already in registers) goes to the other buffer and tile t+2 is loaded.
   // Real tiles k in [k_full0, k_full1] are seen completely by every row of the
   // workgroup and run without visibility code; the tiles before and after them
   // (and the register tiles) run with it.
@@ -409,24 +466,20 @@ void prefill_bf16_kernel(PrefillParams p) {
   }
   const int t_full0 = n_reg_tiles + k_full0, t_full1 = n_reg_tiles + k_full1 + 1;  // [t_full0, t_full1)
 
+  // Tile t lives in buffer t % 2: right after the barrier that frees the other
+  // buffer, tile t+1 is requested into it; tile t is consumed; the wave waits
+  // for its own requests; one barrier publishes tile t+1 to every wave.
   auto step = [&](int t, auto masked_tag) {
+    if (t + 1 < T) issue_tile(t + 1, (t + 1) & 1);
     compute_tile(t, t & 1, masked_tag);
-    if (t + 1 < T) {
-      store_tile((t + 1) & 1);
-      if (t + 2 < T) load_tile(t + 2);
-    }
+    if (t + 1 < T) finish_tile((t + 1) & 1);
     __syncthreads();
   };
 
   if (T > 0) {
-    load_tile(0);
-    store_tile(0);
+    issue_tile(0, 0);
+    finish_tile(0);  // also waits for the Q loads issued above
   }
-  // Q and tile 0 have landed (the stores above consumed tile 0; loads return in
-  // order).  Say so explicitly, so that no wait on the Q registers is left
-  // inside the loop, where it would also wait for the prefetch of later tiles.
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt and lgkmcnt untouched
-  if (T > 1) load_tile(1);
   __syncthreads();
   const int head_end = (t_full1 > t_full0) ? t_full0 : T;
   for (int t = 0; t < head_end; ++t) step(t, std::true_type{});
@@ -437,7 +490,7 @@ void prefill_bf16_kernel(PrefillParams p) {
   // the last barrier) so that global stores are whole rows; LSE in natural log.
   const float ltot = pair32_sum(lsum);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  uint16_t* sO = sKV + wave * 32 * OSTR;
+  uint16_t* sO = reinterpret_cast<uint16_t*>(sKV) + wave * 32 * OSTR;
 #pragma unroll
   for (int c = 0; c < EB; ++c)
 #pragma unroll
