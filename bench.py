@@ -188,8 +188,8 @@ def cpu_baseline(w, inp, o_gpu, lse_gpu, seconds: float):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=configs.C2.name, choices=sorted(configs.BY_NAME))
     ap.add_argument("--extras", default="all", choices=["all", "none"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

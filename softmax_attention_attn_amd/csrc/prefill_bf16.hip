@@ -144,15 +144,16 @@ __device__ __forceinline__ void buffer_load16_to_lds(__amdgpu_buffer_rsrc_t r, u
 #endif
 }
 
-// Waves per SIMD the register budget allows: E = 128 needs ~230 VGPRs (2 waves),
-// E = 64 fits under 168 (3 waves, i.e. 3 workgroups per CU).
-template <int E>
+// Waves per SIMD the register budget allows: E = 128 needs ~230 VGPRs (2 waves);
+// E = 64 fits in 128 VGPRs in dot mode (4 waves = 4 workgroups per CU, 128 KB of
+// LDS) and under 168 in RBF mode (3 waves), where 128 would spill.
+template <int E, int MODE>
 struct Occupancy {
-  static constexpr int kWaves = E == 64 ? 3 : 2;
+  static constexpr int kWaves = E == 64 ? (MODE == kRbf ? 3 : 4) : 2;
 };
 
 template <int E, int MODE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Occupancy<E>::kWaves, Occupancy<E>::kWaves)))
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Occupancy<E, MODE>::kWaves, Occupancy<E, MODE>::kWaves)))
 void prefill_bf16_kernel(PrefillParams p) {
   constexpr bool RBF = MODE == kRbf;
   constexpr bool FAST = MODE == kDotPos;
@@ -346,6 +347,9 @@ void prefill_bf16_kernel(PrefillParams p) {
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[b][r] = 0.f;
+    // Raised wave priority while a wave issues its MFMA chains, so that a wave
+    // holding matrix work is picked over one doing softmax arithmetic.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < QS; ++s) {
       bf16x8 a[NB];
@@ -355,6 +359,7 @@ void prefill_bf16_kernel(PrefillParams p) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) st[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[b], qf[s], st[b], 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
 
     // Accumulator row of register r in block b = key 32b + 8(r/4) + 4g + r%4 of
     // the tile.  FAST keeps raw scores (the scale goes into the exponent);
@@ -428,6 +433,7 @@ void prefill_bf16_kernel(PrefillParams p) {
     lsum += ps;
 
     // O^T += V^T * P^T, 16 keys per MFMA step.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
 #pragma unroll
@@ -445,6 +451,7 @@ void prefill_bf16_kernel(PrefillParams p) {
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Real tiles k in [k_full0, k_full1] are seen completely by every row of the
