@@ -8,7 +8,9 @@ resident in HBM.  The headline workload is the causal bf16 prefill
 N=4, H=16, L=S=2048, E=128 (dot_causal_bf16_4x16x2048x128); its value is
 TFLOP/s over the visible (query, key) pairs, 4*E flops each.  The other
 workloads are timed the same way and reported under "extras" (prefill in
-TFLOP/s, decode in HBM GB/s over the K/V bytes read once).
+TFLOP/s, decode in HBM GB/s over the K/V bytes read once), as is one step of
+streaming decode over a rolling cache (append the newest token, decode it; HBM
+GB/s over the kept rows read once).
 
 The CPU baseline leg times the fp64 oracle on a bounded sample of rows of the
 headline workload, on this host's cores, and checks the GPU output on those
@@ -130,6 +132,51 @@ def time_workload(w, steps: int, warmup: int, rotate: int, torch, attn, keep_fir
     return ms, inp, first
 
 
+def time_stream(sw, steps: int, warmup: int, rotate: int, torch, attn):
+    """Average ms per streaming step (append the newest token, decode its query) over a
+    rolling cache deep into the stream; `rotate` cache sets defeat the on-die cache."""
+    dev = torch.device("cuda:0")
+    log(f"[bench] {sw.name}: generating inputs")
+    base = configs.Workload(sw.name, "bf16", sw.N, sw.Hq, sw.Hkv, 1, sw.rows, sw.E, sw.mode, sw.scale, sw.gamma,
+                            True, 0, 0, sw.sink, True, sw.seed)
+    q, kc, vc, sink = to_device(gen.generate(base), torch, dev)
+    _, kn, vn, _ = to_device(gen.generate(base.with_(S_real=1, seed=sw.seed + 1000)), torch, dev)
+    cap = sw.n_sink + sw.window
+    if kc.shape[2] != cap:  # early in the stream: pad the cache to its capacity
+        pad = torch.zeros((sw.N, sw.Hkv, cap - kc.shape[2], sw.E), dtype=kc.dtype, device=dev)
+        kc, vc = torch.cat([kc, pad], 2).contiguous(), torch.cat([vc, pad], 2).contiguous()
+    sets = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(max(0, rotate - 1))]
+    o = torch.empty_like(q)
+    lse = torch.empty((sw.N, sw.Hq, 1), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(16, attn.stream_decode_workspace_bytes(sw.N, sw.Hq, sw.Hkv, sw.E, sw.n_sink, sw.window,
+                                                                sw.pos)), dtype=torch.uint8, device=dev)
+    kw = dict(n_sink=sw.n_sink, window=sw.window, pos=sw.pos)
+
+    def call(i):
+        k_c, v_c = sets[i % len(sets)]
+        attn.stream_append(kn, vn, k_c, v_c, **kw)
+        attn.stream_decode(q, k_c, v_c, scale=sw.scale, mode=sw.mode, gamma=sw.gamma, sink=sink, workspace=ws,
+                           out=o, lse=lse, **kw)
+
+    for i in range(warmup + 1):
+        call(i)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        call(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def stream_rate(sw, ms: float):
+    gbs = configs.stream_bytes(sw) / (ms * 1e-3) / 1e9
+    return {"value": gbs, "unit": "GB/s", "bound": "hbm", "peak": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS}
+
+
 def rate(w, ms: float):
     if w.decode:
         gbs = configs.algorithmic_bytes(w) / (ms * 1e-3) / 1e9
@@ -190,7 +237,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default=configs.C2.name, choices=sorted(configs.BY_NAME))
+    ap.add_argument("--workload", default=configs.C2.name,
+                    choices=sorted(configs.BY_NAME) + sorted(configs.STREAM_BY_NAME))
     ap.add_argument("--extras", default="all", choices=["all", "none"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -231,6 +279,19 @@ def main() -> int:
                           "GBps_read_plus_write": 2 * args.copy_bytes / (ms * 1e-3) / 1e9}), flush=True)
         return 0
 
+    if args.workload in configs.STREAM_BY_NAME:
+        # one streaming step (append + decode) on its own, for profiling
+        sw = configs.STREAM_BY_NAME[args.workload]
+        ms = time_stream(sw, args.steps, args.warmup, 3, torch, attn)
+        r = stream_rate(sw, ms)
+        print(json.dumps({"metric": "streaming decode HBM GB/s", "value": r["value"], "unit": r["unit"],
+                          "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+                          "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                          "data": "synthetic (seeded generator, workloads/gen.py)",
+                          "config": {"workload": sw.name},
+                          "roofline": {"bound": "hbm", "achieved": r["value"], "peak": r["peak"], "unit": "GB/s",
+                                       "frac": r["frac"], "traffic": None, "kernel": "decode_bf16"}}), flush=True)
+        return 0
     w = configs.BY_NAME[args.workload]
     ms, inp, first = time_workload(w, args.steps, args.warmup, 1, torch, attn, keep_first_output=True)
     r = rate(w, ms)
@@ -277,6 +338,14 @@ def main() -> int:
             xr["kernel"] = kernel_of(x)
             xr["rotated_buffer_sets"] = rot
             extras[x.name] = xr
+        for sw in configs.STREAM_BY_NAME.values():
+            xms = time_stream(sw, max(5, args.steps // 2), max(2, args.warmup // 2), 3, torch, attn)
+            torch.cuda.empty_cache()
+            xr = stream_rate(sw, xms)
+            xr["ms"] = xms
+            xr["kernel"] = "stream_append + decode_bf16"
+            xr["rotated_buffer_sets"] = 3
+            extras[sw.name] = xr
         result["extras"] = extras
     print(json.dumps(result), flush=True)
     return 0

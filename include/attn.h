@@ -1,7 +1,8 @@
 /*
  * attn.h -- C ABI of the MI355X (gfx950) fused softmax-attention library.
  *
- * One operation, two entry points:
+ * One operation, computed by attn_fwd (prefill), attn_decode (split-K
+ * decode) and attn_stream_decode (decode over a rolling cache):
  *
  *   O = softmax(Z) V,  Z_ij = logit(q_i, k_j) + B_ij,  B_ij in {0, -inf}
  *
@@ -115,6 +116,54 @@ int attn_decode_num_splits(int N, int Hq, int Hkv, int S, int E, int causal, int
  * (0 = the automatic count); 0 if the sizes are invalid. */
 size_t attn_decode_workspace_bytes(int N, int Hq, int Hkv, int S, int E, int causal, int window,
                                    int n_reg, int num_splits);
+
+/*
+ * Rolling key/value cache for streaming decode ("Attention Sink LLM..." page,
+ * section 3.2, StreamingLLM): the key/value rows of the first n_sink tokens
+ * stay in the cache for good, and only the `window` most recent tokens after
+ * them are kept, in a ring.  A cache holds C = n_sink + window rows per
+ * (batch, kv head): k_cache and v_cache are (N, Hkv, C, E).  The token at
+ * absolute position p (0-based) lives in row
+ *     slot(p) = p                                 if p < n_sink,
+ *     slot(p) = n_sink + (p - n_sink) % window    otherwise.
+ * Once the tokens up to position `pos` have been appended, rows
+ * [0, min(pos + 1, C)) hold exactly the kept tokens
+ *     { p < n_sink }  U  { pos - window < p <= pos }
+ * (positions are whatever the caller's keys encode; the kernels never look
+ * at them, and attention over a set of keys does not depend on their order).
+ * Requirements for both calls: n_sink >= 0, window >= 1, pos >= 0
+ * (ATTN_ERR_ARG otherwise); k_cache / v_cache 16-byte aligned.
+ */
+
+/*
+ * attn_stream_append -- write the T tokens at positions pos .. pos+T-1 into the
+ * cache.  k_new, v_new: (N, Hkv, T, E) of element type dt (bf16 or f32), 16-byte
+ * aligned.  Only tokens still kept after the whole append are written, so a
+ * block longer than the window is fine and rows of evicted tokens are
+ * overwritten in place.  Rows of tokens at positions below pos are left as they
+ * are: the caller appends positions in order (the library keeps no position
+ * state).  N*T == 0 succeeds without launching anything.
+ */
+int attn_stream_append(attn_dtype dt, int N, int Hkv, int E, int n_sink, int window, long long pos, int T,
+                       const void* k_new, const void* v_new, void* k_cache, void* v_cache, void* stream);
+
+/*
+ * attn_stream_decode -- the query of the token at position `pos` (whose key and
+ * value are already in the cache) against every kept token: q (N, Hq, 1, E),
+ * o (N, Hq, 1, E), lse (N, Hq, 1).  The result equals attn_decode over the full
+ * history of pos + 1 keys with n_reg = n_sink, window = window, causal = 1.
+ * mode, scale, gamma, sink, num_splits, workspace: as for attn_decode, with
+ * workspace size from attn_stream_decode_workspace_bytes.  bf16 only.
+ */
+int attn_stream_decode(attn_dtype dt, int N, int Hq, int Hkv, int E, int n_sink, int window, long long pos,
+                       const void* q, const void* k_cache, const void* v_cache,
+                       attn_mode mode, float scale, float gamma, const float* sink,
+                       void* o, float* lse,
+                       int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_stream_decode needs (0 if the sizes are invalid). */
+size_t attn_stream_decode_workspace_bytes(int N, int Hq, int Hkv, int E, int n_sink, int window, long long pos,
+                                          int num_splits);
 
 /* Static text for a status code. */
 const char* attn_status_string(int status);

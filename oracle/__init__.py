@@ -147,3 +147,29 @@ def attn_workload(inp, rows: Optional[Sequence[int]] = None, want_p: bool = Fals
     w = inp.workload
     return attn(inp.q, inp.k, inp.v, mode=w.mode, scale=w.scale, gamma=w.gamma, causal=w.causal,
                 window=w.window, n_reg=w.n_reg, sink=inp.sink, rows=rows, want_p=want_p, threads=threads)
+
+
+# ----------------------------------------------------------------------------- rolling (StreamingLLM) cache
+
+
+def stream_kept_positions(n_sink: int, window: int, pos: int) -> np.ndarray:
+    """Absolute positions a StreamingLLM cache holds once the token at `pos` is in it:
+    the first n_sink tokens for good, plus the `window` most recent tokens ("Attention Sink
+    LLM..." page, section 3.2: keep the initial tokens' KV, roll the recent ones)."""
+    p = np.arange(pos + 1, dtype=np.int64)
+    return p[(p < n_sink) | (p > pos - window)]
+
+
+def stream_decode(q: np.ndarray, k_hist: np.ndarray, v_hist: np.ndarray, *, n_sink: int, window: int, pos: int,
+                  mode: str = "dot", scale: Optional[float] = None, gamma: float = 0.0,
+                  sink: Optional[np.ndarray] = None, threads: int = 0, lib=None):
+    """Decode of the token at position `pos` over what the cache keeps.
+
+    q (N,Hq,1,E); k_hist, v_hist (N,Hkv,>pos,E) with row p = the token at absolute
+    position p.  The kept rows are gathered and attended to with no mask: every
+    kept token precedes (or is) the query.  Returns (o (N,Hq,1,E), lse (N,Hq,1))."""
+    kept = stream_kept_positions(n_sink, window, pos)
+    k = np.ascontiguousarray(k_hist[:, :, kept])
+    v = np.ascontiguousarray(v_hist[:, :, kept])
+    return attn(q, k, v, mode=mode, scale=scale, gamma=gamma, causal=False, window=0, n_reg=0, sink=sink,
+                threads=threads, lib=lib)

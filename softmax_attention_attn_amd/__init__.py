@@ -8,6 +8,8 @@ or a call is rejected, an exception is raised.
     o, lse = fwd(q, k, v, scale=..., mode="dot"|"rbf", gamma=..., causal=...,
                  window=..., n_reg=..., sink=...)
     o, lse = decode(q, k, v, ..., num_splits=0)
+    stream_append(k_new, v_new, k_cache, v_cache, n_sink=4, window=W, pos=p)
+    o, lse = stream_decode(q, k_cache, v_cache, n_sink=4, window=W, pos=p, ...)
 
 q (N, Hq, L, E), k and v (N, Hkv, S, E), all bf16 (or all float32 for fwd),
 contiguous, on one GPU; sink (Hq,) float32.  Returns o like q and lse
@@ -32,6 +34,7 @@ BF16, F32 = 0, 1
 MODES = {"dot": 0, "rbf": 1}
 
 EXPORTS = ("attn_fwd", "attn_decode", "attn_decode_num_splits", "attn_decode_workspace_bytes",
+           "attn_stream_append", "attn_stream_decode", "attn_stream_decode_workspace_bytes",
            "attn_status_string", "attn_last_error")
 
 
@@ -60,6 +63,13 @@ def load() -> ctypes.CDLL:
         lib.attn_decode_num_splits.argtypes = [I] * 8
         lib.attn_decode_workspace_bytes.restype = Z
         lib.attn_decode_workspace_bytes.argtypes = [I] * 9
+        LL = ctypes.c_longlong
+        lib.attn_stream_append.restype = I
+        lib.attn_stream_append.argtypes = [I, I, I, I, I, I, LL, I, P, P, P, P, P]
+        lib.attn_stream_decode.restype = I
+        lib.attn_stream_decode.argtypes = [I, I, I, I, I, I, I, LL, P, P, P, I, F, F, P, P, P, I, P, Z, P]
+        lib.attn_stream_decode_workspace_bytes.restype = Z
+        lib.attn_stream_decode_workspace_bytes.argtypes = [I, I, I, I, I, I, LL, I]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_status_string.argtypes = [I]
         lib.attn_last_error.restype = ctypes.c_char_p
@@ -169,5 +179,65 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional
                          scale, gamma, int(bool(causal)), int(window), int(n_reg), _ptr(sink),
                          _ptr(out), _ptr(lse), int(num_splits), _ptr(workspace),
                          workspace.numel() * workspace.element_size(), _stream(q.device, stream))
+    _check(rc)
+    return out, lse
+
+
+def _cache_check(k_cache, v_cache, n_sink: int, window: int):
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dim() != 4 or not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a contiguous 4-D GPU tensor")
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype or k_cache.device != v_cache.device:
+        raise ValueError("k_cache and v_cache must match in shape, element type and device")
+    if k_cache.shape[2] != n_sink + window:
+        raise ValueError(f"cache has {k_cache.shape[2]} rows per head, expected n_sink + window = {n_sink + window}")
+
+
+def stream_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *,
+                  n_sink: int, window: int, pos: int, stream=None) -> None:
+    """Write the tokens at positions pos .. pos+T-1 (k_new, v_new: (N, Hkv, T, E)) into the rolling
+    cache (N, Hkv, n_sink + window, E) through attn_stream_append."""
+    _cache_check(k_cache, v_cache, n_sink, window)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t.dim() != 4 or not t.is_contiguous() or t.device != k_cache.device or t.dtype != k_cache.dtype:
+            raise ValueError(f"{name} must be a contiguous 4-D tensor like the cache")
+    if k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new must have the same shape")
+    N, Hkv, T, E = k_new.shape
+    if (k_cache.shape[0], k_cache.shape[1], k_cache.shape[3]) != (N, Hkv, E):
+        raise ValueError(f"new tokens {tuple(k_new.shape)} do not match the cache {tuple(k_cache.shape)}")
+    rc = load().attn_stream_append(_dtype_code(k_new), N, Hkv, E, int(n_sink), int(window), int(pos), T,
+                                   _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                   _stream(k_new.device, stream))
+    _check(rc)
+
+
+def stream_decode_workspace_bytes(N: int, Hq: int, Hkv: int, E: int, n_sink: int, window: int, pos: int,
+                                  num_splits: int = 0) -> int:
+    return int(load().attn_stream_decode_workspace_bytes(N, Hq, Hkv, E, n_sink, window, pos, num_splits))
+
+
+def stream_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *, n_sink: int, window: int,
+                  pos: int, scale: Optional[float] = None, mode: str = "dot", gamma: Optional[float] = None,
+                  sink: Optional[torch.Tensor] = None, num_splits: int = 0,
+                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Decode of the token at position `pos` (q: (N, Hq, 1, E)) against every token the rolling
+    cache keeps, through attn_stream_decode; returns (o, lse)."""
+    _cache_check(k_cache, v_cache, n_sink, window)
+    N, Hq, Hkv, L, _, E, scale, gamma = _common(q, k_cache, v_cache, sink, scale, mode, gamma)
+    if L != 1:
+        raise ValueError(f"stream_decode takes one query per sequence, got q {tuple(q.shape)}")
+    need = stream_decode_workspace_bytes(N, Hq, Hkv, E, n_sink, window, pos, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((N, Hq, L), dtype=torch.float32, device=q.device)
+    rc = load().attn_stream_decode(_dtype_code(q), N, Hq, Hkv, E, int(n_sink), int(window), int(pos),
+                                   _ptr(q), _ptr(k_cache), _ptr(v_cache), MODES[mode], scale, gamma, _ptr(sink),
+                                   _ptr(out), _ptr(lse), int(num_splits), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(q.device, stream))
     _check(rc)
     return out, lse

@@ -82,6 +82,7 @@ attn_impl::FwdArgs make_args(int N, int Hq, int Hkv, int L, int S, int E, const 
   a.L = L;
   a.S = S;
   a.E = E;
+  a.kv_rows = S;
   a.n_reg = n_reg;
   a.causal = causal ? 1 : 0;
   a.window = window;
@@ -113,6 +114,14 @@ int resolve_splits(int N, int Hq, int Hkv, int S, int causal, int window, int n_
 size_t workspace_for(int N, int Hq, int E, int splits) {
   const size_t parts = (size_t)N * Hq * splits;
   return parts * E * sizeof(float) + parts * 2 * sizeof(float);
+}
+
+// Rows of the rolling cache that hold kept tokens once position `pos` has been
+// appended (they are rows [0, n) of every slice); -1 for invalid arguments.
+long long stream_rows(int n_sink, int window, long long pos) {
+  if (n_sink < 0 || window < 1 || pos < 0) return -1;
+  const long long cap = (long long)n_sink + window;
+  return pos + 1 < cap ? pos + 1 : cap;
 }
 
 }  // namespace
@@ -179,6 +188,79 @@ int attn_decode(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, cons
   d.part_o = static_cast<float*>(workspace);
   d.part_ml = d.part_o + (size_t)N * Hq * splits * E;
   return hip_status(attn_impl::launch_decode_bf16(d, static_cast<hipStream_t>(stream)), "attn_decode launch");
+}
+
+// ----------------------------------------------------------------------------- rolling cache
+
+int attn_stream_append(attn_dtype dt, int N, int Hkv, int E, int n_sink, int window, long long pos, int T,
+                       const void* k_new, const void* v_new, void* k_cache, void* v_cache, void* stream) {
+  if (dt != ATTN_BF16 && dt != ATTN_F32) return fail(ATTN_ERR_DTYPE, "unknown dtype %d", (int)dt);
+  if (N < 0 || Hkv <= 0 || T < 0) return fail(ATTN_ERR_SHAPE, "invalid sizes (N=%d Hkv=%d T=%d)", N, Hkv, T);
+  if (E != 64 && E != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension E=%d (supported: 64, 128)", E);
+  if (n_sink < 0 || window < 1) return fail(ATTN_ERR_ARG, "need n_sink >= 0 and window >= 1 (n_sink=%d window=%d)", n_sink, window);
+  if (pos < 0) return fail(ATTN_ERR_ARG, "pos=%lld must be >= 0", pos);
+  const long long cap = (long long)n_sink + window;
+  if ((long long)N * Hkv * cap * E > kMaxElems || (long long)N * Hkv * T * E > kMaxElems)
+    return fail(ATTN_ERR_SHAPE, "tensor too large");
+  if ((long long)N * T == 0) return ok();
+  if (!k_new || !v_new || !k_cache || !v_cache) return fail(ATTN_ERR_NULL, "k_new, v_new, k_cache and v_cache must not be NULL");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(ATTN_ERR_ALIGN, "k_new, v_new, k_cache and v_cache must be 16-byte aligned");
+  const int eb = dt == ATTN_BF16 ? 2 : 4;
+  if ((long long)N * Hkv * T * (E * eb / 16) / 256 + 1 > kMaxGrid) return fail(ATTN_ERR_SHAPE, "grid too large");
+  attn_impl::StreamAppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.N = N;
+  a.Hkv = Hkv;
+  a.E = E;
+  a.elem_bytes = eb;
+  a.n_sink = n_sink;
+  a.window = window;
+  a.T = T;
+  a.pos = pos;
+  return hip_status(attn_impl::launch_stream_append(a, static_cast<hipStream_t>(stream)), "attn_stream_append launch");
+}
+
+size_t attn_stream_decode_workspace_bytes(int N, int Hq, int Hkv, int E, int n_sink, int window, long long pos,
+                                          int num_splits) {
+  const long long rows = stream_rows(n_sink, window, pos);
+  if (rows < 0 || rows > 0x7fffffffLL) return 0;
+  return attn_decode_workspace_bytes(N, Hq, Hkv, (int)rows, E, 1, 0, 0, num_splits);
+}
+
+int attn_stream_decode(attn_dtype dt, int N, int Hq, int Hkv, int E, int n_sink, int window, long long pos,
+                       const void* q, const void* k_cache, const void* v_cache, attn_mode mode, float scale,
+                       float gamma, const float* sink, void* o, float* lse, int num_splits, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (n_sink < 0 || window < 1) return fail(ATTN_ERR_ARG, "need n_sink >= 0 and window >= 1 (n_sink=%d window=%d)", n_sink, window);
+  if (pos < 0) return fail(ATTN_ERR_ARG, "pos=%lld must be >= 0", pos);
+  const long long cap = (long long)n_sink + window;
+  if (cap > 0x7fffffffLL - 64) return fail(ATTN_ERR_SHAPE, "n_sink + window too large");
+  const int S = (int)stream_rows(n_sink, window, pos);
+  // Every kept row is visible to the newest token (its own row included), in
+  // any order: plain decode over rows [0, S) of slices that are `cap` rows apart.
+  int rc = check_args(dt, N, Hq, Hkv, 1, (int)cap, E, q, k_cache, v_cache, mode, scale, gamma, 1, 0, 0, sink, o, lse);
+  if (rc != ATTN_OK) return rc;
+  if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode is implemented for bf16 only");
+  if (num_splits < 0) return fail(ATTN_ERR_ARG, "num_splits=%d must be >= 0", num_splits);
+  if (N == 0) return ok();
+  const int splits = resolve_splits(N, Hq, Hkv, S, 1, 0, 0, num_splits);
+  const size_t need = workspace_for(N, Hq, E, splits);
+  if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (workspace_bytes < need) return fail(ATTN_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, need);
+  if (!aligned(workspace, 16)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if ((long long)N * Hkv * ((Hq / Hkv + 15) / 16) > 65535LL || (long long)N * Hq > kMaxGrid)
+    return fail(ATTN_ERR_SHAPE, "grid too large");
+  attn_impl::DecodeArgs d;
+  d.f = make_args(N, Hq, Hkv, 1, S, E, q, k_cache, v_cache, mode, scale, gamma, 1, 0, 0, sink, o, lse);
+  d.f.kv_rows = (int)cap;
+  d.num_splits = splits;
+  d.part_o = static_cast<float*>(workspace);
+  d.part_ml = d.part_o + (size_t)N * Hq * splits * E;
+  return hip_status(attn_impl::launch_decode_bf16(d, static_cast<hipStream_t>(stream)), "attn_stream_decode launch");
 }
 
 const char* attn_status_string(int status) {

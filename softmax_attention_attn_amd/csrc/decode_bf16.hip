@@ -35,7 +35,7 @@ struct DecodeParams {
   const uint16_t* v;
   float* part_o;
   float* part_ml;
-  int N, Hq, Hkv, S, n_reg;
+  int N, Hq, Hkv, kv_rows, n_reg;
   int first_real;  // keys n_reg .. n_reg+first_real-1 are outside the window
   int nkeys;       // n_reg + visible real keys
   int chunk;       // keys per split (multiple of KSTEP)
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
   for (int s = 0; s < QS; ++s) qf[s] = as_bf16x8(load16_or_zero(qrow + 32 * s + 8 * g, qvalid));
 
-  const size_t kvoff = ((size_t)n * p.Hkv + kvh) * (size_t)p.S * E;
+  const size_t kvoff = ((size_t)n * p.Hkv + kvh) * (size_t)p.kv_rows * E;
   const uint16_t* kbase = p.k + kvoff;
   const uint16_t* vbase = p.v + kvoff;
 
@@ -325,7 +325,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   p.N = f.N;
   p.Hq = f.Hq;
   p.Hkv = f.Hkv;
-  p.S = f.S;
+  p.kv_rows = f.kv_rows;
   p.n_reg = f.n_reg;
   p.first_real = dk.first_real;
   p.nkeys = dk.count;

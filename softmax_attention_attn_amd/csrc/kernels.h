@@ -21,6 +21,7 @@ struct FwdArgs {
   float* lse;
   const float* sink;  // Hq logits or nullptr
   int N, Hq, Hkv, L, S, E;
+  int kv_rows;        // rows between consecutive (batch, kv head) slices of k/v (>= S)
   int n_reg;          // register rows at the start of K/V
   int causal;
   int window;         // 0 = none
@@ -40,6 +41,20 @@ struct DecodeArgs {
 hipError_t launch_prefill_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+
+// Rolling key/value cache append: tokens at positions pos .. pos+T-1 from
+// k_new / v_new (N, Hkv, T, E) into k_cache / v_cache (N, Hkv, n_sink+window, E);
+// only the tokens still kept after the append are written (see slot rule in attn.h).
+struct StreamAppendArgs {
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  int N, Hkv, E, elem_bytes;
+  int n_sink, window, T;
+  long long pos;
+};
+hipError_t launch_stream_append(const StreamAppendArgs& a, hipStream_t stream);
 
 // Key range attn_decode streams: registers [0, n_reg) followed by the visible
 // real keys [n_reg + first_real, S); `count` = number of keys in that list.

@@ -45,7 +45,7 @@ def sample_rows(w: Workload, per_head: int = 4, extra: int = 256, seed: int = 0)
     for n in range(w.N):
         for h in range(w.Hq):
             base = (n * w.Hq + h) * w.L
-            for i in {0, w.L - 1, min(w.L - 1, 127), min(w.L - 1, 128)}:
+            for i in {0, w.L - 1, min(w.L - 1, 127), min(w.L - 1, 128), min(w.L - 1, 255), min(w.L - 1, 256)}:
                 rows.add(base + i)
             for i in r.integers(0, w.L, per_head):
                 rows.add(base + int(i))

@@ -115,6 +115,63 @@ def test_decode_split_and_workspace_sizes(lib):
     assert lib.attn_decode_workspace_bytes(1, 4, 3, 100, 64, 1, 0, 0, 0) == 0
 
 
+def app(lib, dt=0, N=1, Hkv=2, E=64, n_sink=4, window=16, pos=0, T=3, kn=A, vn=A, kc=A, vc=A):
+    return lib.attn_stream_append(dt, N, Hkv, E, n_sink, window, pos, T, kn, vn, kc, vc, None)
+
+
+def sdec(lib, dt=0, N=1, Hq=4, Hkv=2, E=64, n_sink=4, window=16, pos=40, q=A, kc=A, vc=A, mode=0, scale=0.125,
+         gamma=0.0, sink=None, o=A, lse=A, splits=0, ws=A, wsb=1 << 30):
+    return lib.attn_stream_decode(dt, N, Hq, Hkv, E, n_sink, window, pos, q, kc, vc, mode, scale, gamma, sink, o,
+                                  lse, splits, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=5), -3),
+    (dict(Hkv=0), -2),
+    (dict(T=-1), -2),
+    (dict(E=80), -4),
+    (dict(window=0), -8),
+    (dict(n_sink=-1), -8),
+    (dict(pos=-2), -8),
+    (dict(kn=None), -1),
+    (dict(vc=None), -1),
+    (dict(kc=A + 8), -5),
+])
+def test_stream_append_rejects(lib, kw, code):
+    assert app(lib, **kw) == code
+
+
+def test_stream_append_empty_is_a_no_op(lib):
+    assert app(lib, T=0, kn=None, vn=None, kc=None, vc=None) == 0
+    assert app(lib, N=0, kn=None, vn=None, kc=None, vc=None) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=1), -4),
+    (dict(window=0), -8),
+    (dict(n_sink=-4), -8),
+    (dict(pos=-1), -8),
+    (dict(Hq=6, Hkv=4), -2),
+    (dict(E=32), -4),
+    (dict(q=None), -1),
+    (dict(kc=None), -1),
+    (dict(ws=None), -6),
+    (dict(wsb=8), -6),
+    (dict(splits=-2), -8),
+    (dict(mode=1, gamma=-0.5), -8),
+])
+def test_stream_decode_rejects(lib, kw, code):
+    assert sdec(lib, **kw) == code
+
+
+def test_stream_decode_workspace_matches_decode_over_kept_rows(lib):
+    # kept rows = min(pos + 1, n_sink + window)
+    for pos, rows in ((0, 1), (10, 11), (19, 20), (20, 20), (10 ** 9, 20)):
+        assert lib.attn_stream_decode_workspace_bytes(2, 8, 2, 128, 4, 16, pos, 0) == \
+            lib.attn_decode_workspace_bytes(2, 8, 2, rows, 128, 1, 0, 0, 0)
+    assert lib.attn_stream_decode_workspace_bytes(2, 8, 2, 128, 4, 0, 5, 0) == 0
+
+
 def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(attn, "LIB_PATH", "/nonexistent/libattn.so")
     monkeypatch.setattr(attn, "_lib", None)

@@ -49,6 +49,19 @@ PREFILL_CASES = [
     W("f32_dot_L_gt_S", dtype="f32", L=90, S_real=40, E=64),
 ]
 
+# Wider shapes (hundreds of workgroups, more heads than the small cases) with
+# ragged tails; checked on sampled rows.
+PREFILL_WIDE_CASES = [
+    W("wide_dot_causal_gqa_e128_ragged", Hq=64, Hkv=16, L=1000, S_real=1000, E=128),
+    W("wide_dot_noncausal_sink_L_lt_S", N=2, Hq=48, Hkv=48, L=700, S_real=900, causal=False, sink=True),
+    W("wide_rbf_causal_registers", Hq=64, Hkv=8, L=777, S_real=777, mode="rbf", n_reg=4, k_dist="dir_lognormal"),
+    W("wide_rbf_noncausal_many_registers_sink_e128", Hq=128, Hkv=64, L=300, S_real=200, E=128, mode="rbf",
+      n_reg=70, causal=False, sink=True, gamma=0.05),
+    W("wide_dot_causal_L_gt_S_empty_rows_e128", Hq=96, Hkv=96, L=600, S_real=200, E=128),
+    W("wide_dot_negative_scale_e128", Hq=128, Hkv=32, L=512, S_real=512, E=128, causal=False, scale=-0.06),
+    W("wide_dot_causal_registers_e64", N=4, Hq=32, Hkv=4, L=520, S_real=520, n_reg=3, sink=True),
+]
+
 DECODE_CASES = [
     (W("dec_dot_sink_gqa4_e128", N=2, Hq=8, Hkv=2, L=1, S_real=5000, E=128, sink=True, decode=True), [0, 1, 3, 64]),
     (W("dec_rbf_registers", N=2, Hq=4, Hkv=2, L=1, S_real=3000, mode="rbf", n_reg=4, decode=True,
@@ -69,6 +82,16 @@ def test_prefill_small(w):
     o, lse = run_gpu(w, q, k, v, sink)
     torch.cuda.synchronize()
     check(w, inp, o, lse)
+
+
+@pytest.mark.parametrize("w", PREFILL_WIDE_CASES, ids=[w.name for w in PREFILL_WIDE_CASES])
+def test_prefill_wide(w):
+    say(f"[prefill wide] {w}")
+    inp = gen.generate(w)
+    q, k, v, sink = to_device(inp)
+    o, lse = run_gpu(w, q, k, v, sink)
+    torch.cuda.synchronize()
+    check(w, inp, o, lse, rows=sample_rows(w, per_head=3, extra=128))
 
 
 @pytest.mark.parametrize("w,splits", DECODE_CASES, ids=[c[0].name for c in DECODE_CASES])

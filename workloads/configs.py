@@ -98,3 +98,47 @@ def algorithmic_bytes(w: Workload) -> float:
     lse = w.N * w.Hq * w.L * 4
     sink = w.Hq * 4 if w.sink else 0
     return float(q + kv + o + lse + sink)
+
+
+@dataclass(frozen=True)
+class StreamWorkload:
+    """One step of streaming decode over a rolling (StreamingLLM) cache: append the
+    newest token's key/value, then decode its query against the n_sink first
+    tokens and the `window` most recent ones ("Attention Sink LLM..." page,
+    section 3.2).  `pos` is the newest token's absolute position; the cache
+    holds n_sink + window rows per (batch, kv head)."""
+    name: str
+    N: int
+    Hq: int
+    Hkv: int
+    E: int
+    n_sink: int
+    window: int
+    pos: int
+    sink: bool
+    seed: int
+    mode: str = "dot"
+    scale: float = 0.0
+    gamma: float = 0.0
+    dtype: str = "bf16"
+
+    @property
+    def rows(self) -> int:
+        return min(self.pos + 1, self.n_sink + self.window)
+
+
+# StreamingLLM-sized cache (4 sink tokens + a 4092-token window) deep into a
+# stream, with the long-context decode shape's heads (32 query over 8 kv heads).
+STREAM1 = StreamWorkload("stream_sink4_win4092_bf16_8x32to8x128_pos100000", 8, 32, 8, 128, 4, 4092, 100000,
+                         True, 6, scale=1.0 / math.sqrt(128.0))
+STREAM_BY_NAME = {STREAM1.name: STREAM1}
+
+
+def stream_bytes(w: StreamWorkload) -> float:
+    """Per step: the new token's key/value read and written once, every kept row of
+    the cache read once, q read, o and lse written, sink read."""
+    esz = 2
+    new = 2 * w.N * w.Hkv * w.E * esz
+    kv = 2 * w.N * w.Hkv * w.rows * w.E * esz
+    q = w.N * w.Hq * w.E * esz
+    return float(2 * new + kv + 2 * q + w.N * w.Hq * 4 + (w.Hq * 4 if w.sink else 0))
