@@ -244,10 +244,33 @@ struct CombineParams {
   float gamma;
 };
 
-// One workgroup per (batch, query head), one thread per output dim.
+// One workgroup per (batch, query head), one thread per output dim.  The
+// partial maxima are reduced first (all splits read at once, strided over the
+// threads); then, in chunks of kCombineChunk splits, the split weights
+// 2^(m_s - M) go to LDS and every thread sums its output column over the chunk
+// with independent loads, so the merge costs a few memory round trips rather
+// than one per split.
+constexpr int kCombineChunk = 1024;
+
+template <int E>
+__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
+  const int e = threadIdx.x;
+  red[e] = v;
+  __syncthreads();
+#pragma unroll
+  for (int s = E / 2; s > 0; s >>= 1) {
+    if (e < s) red[e] = is_max ? fmaxf(red[e], red[e + s]) : red[e] + red[e + s];
+    __syncthreads();
+  }
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
 template <int E>
 __global__ __launch_bounds__(E) void decode_combine_kernel(CombineParams p) {
   __shared__ float sRed[E];
+  __shared__ float sW[kCombineChunk];
   const int nh = blockIdx.x;
   const int h = nh % p.Hq;
   const int e = threadIdx.x;
@@ -255,28 +278,33 @@ __global__ __launch_bounds__(E) void decode_combine_kernel(CombineParams p) {
   float qn2 = 0.f;
   if (p.rbf) {
     const float qe = bf16_lo(p.q[(size_t)nh * E + e]);
-    sRed[e] = qe * qe;
-    __syncthreads();
-    for (int s = E / 2; s > 0; s >>= 1) {
-      if (e < s) sRed[e] += sRed[e + s];
-      __syncthreads();
-    }
-    qn2 = sRed[0];
+    qn2 = block_reduce<E>(qe * qe, sRed, false);
   }
 
   const size_t base = (size_t)nh * p.num_splits;
   float sink2 = kNegInf;
   if (p.sink) sink2 = (p.sink[h] + (p.rbf ? p.gamma * qn2 : 0.f)) * kLog2e;
-  float M = sink2;
-  for (int s = 0; s < p.num_splits; ++s) M = fmaxf(M, p.part_ml[(base + s) * 2]);
+  float mloc = kNegInf;
+  for (int s = e; s < p.num_splits; s += E) mloc = fmaxf(mloc, p.part_ml[(base + s) * 2]);
+  const float M = fmaxf(sink2, block_reduce<E>(mloc, sRed, true));
   const float Mu = (M == kNegInf) ? 0.f : M;
-  float l = p.sink ? exp2f(sink2 - Mu) : 0.f;
-  float acc = 0.f;
-  for (int s = 0; s < p.num_splits; ++s) {
-    const float w = exp2f(p.part_ml[(base + s) * 2] - Mu);
-    l += w * p.part_ml[(base + s) * 2 + 1];
-    acc += w * p.part_o[(base + s) * E + e];
+
+  float lloc = 0.f, acc = 0.f;
+  for (int c0 = 0; c0 < p.num_splits; c0 += kCombineChunk) {
+    const int n = min(kCombineChunk, p.num_splits - c0);
+    for (int s = e; s < n; s += E) {
+      const float w = exp2f(p.part_ml[(base + c0 + s) * 2] - Mu);
+      sW[s] = w;
+      lloc += w * p.part_ml[(base + c0 + s) * 2 + 1];
+    }
+    __syncthreads();
+    const float* po = p.part_o + (base + c0) * E + e;
+#pragma unroll 8
+    for (int s = 0; s < n; ++s) acc += sW[s] * po[(size_t)s * E];
+    __syncthreads();
   }
+  float l = block_reduce<E>(lloc, sRed, false);
+  if (p.sink) l += exp2f(sink2 - Mu);
   const float ov = l > 0.f ? acc / l : 0.f;
   p.o[(size_t)nh * E + e] = __builtin_bit_cast(uint16_t, (__bf16)ov);
   if (e == 0) {
