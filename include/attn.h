@@ -1,8 +1,9 @@
 /*
  * attn.h -- C ABI of the MI355X (gfx950) fused softmax-attention library.
  *
- * One operation, computed by attn_fwd (prefill), attn_decode (split-K
- * decode) and attn_stream_decode (decode over a rolling cache):
+ * One operation, computed by attn_fwd (prefill), attn_fwd_biased (prefill
+ * with a general bias), attn_decode (split-K decode) and attn_stream_decode
+ * (decode over a rolling cache):
  *
  *   O = softmax(Z) V,  Z_ij = logit(q_i, k_j) + B_ij,  B_ij in {0, -inf}
  *
@@ -68,6 +69,7 @@ typedef enum {
 
 typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype;
 typedef enum { ATTN_MODE_DOT = 0, ATTN_MODE_RBF = 1 } attn_mode;
+typedef enum { ATTN_BIAS_NONE = 0, ATTN_BIAS_F32 = 1, ATTN_BIAS_BOOL = 2 } attn_bias_kind;
 
 /*
  * attn_fwd -- prefill / general forward.
@@ -85,6 +87,38 @@ int attn_fwd(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E,
              attn_mode mode, float scale, float gamma,
              int causal, int window, int n_reg, const float* sink,
              void* o, float* lse, void* stream);
+
+/*
+ * attn_fwd_biased -- attn_fwd with a general bias B on top of the visibility
+ * rule ("SDPA란 무엇인가?" section 1: B is an L x S matrix added to the logits;
+ * section 4: a boolean attn_mask is True where a pair is used -- the opposite
+ * of a key-padding mask -- and padding and causal masks combine with AND).
+ * Same arguments as attn_fwd, plus:
+ *   bias_kind  ATTN_BIAS_NONE: no bias (bias is ignored)
+ *              ATTN_BIAS_F32:  bias is float32, added to the logit of every
+ *                              visible pair, in natural-log units like the
+ *                              logits; -inf hides the pair; +inf and NaN are
+ *                              not allowed (the result is then undefined)
+ *              ATTN_BIAS_BOOL: bias is uint8; 0 hides the pair, any other
+ *                              value keeps it
+ *   bias       device pointer; the entry of pair (n, h, i, j) is
+ *              bias[n*bias_stride_n + h*bias_stride_h + i*S + j] (strides in
+ *              elements; 0 broadcasts, e.g. one (L, S) matrix for every
+ *              batch and head); float32 bias 4-byte aligned
+ *   key_len    NULL, or N int32 device values: in sequence n the real keys
+ *              r >= key_len[n] are padding (hidden); registers are unaffected
+ *              and the causal / window alignment is unchanged
+ * A row with no visible pair left gives O = 0, LSE = -inf (LSE = s_h with a
+ * sink).  Errors as attn_fwd, plus ATTN_ERR_ARG for an unknown bias kind or a
+ * negative stride and ATTN_ERR_NULL for a missing bias.
+ */
+int attn_fwd_biased(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E,
+                    const void* q, const void* k, const void* v,
+                    attn_mode mode, float scale, float gamma,
+                    int causal, int window, int n_reg, const float* sink,
+                    attn_bias_kind bias_kind, const void* bias, long long bias_stride_n, long long bias_stride_h,
+                    const int* key_len,
+                    void* o, float* lse, void* stream);
 
 /*
  * attn_decode -- one query token per sequence (L must be 1) against a long

@@ -49,6 +49,13 @@ def _bind(path: str):
         vp, vp, vp, ctypes.c_int, ctypes.c_double, ctypes.c_double,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, dp,
         ctypes.c_longlong, llp, dp, dp, dp, ctypes.c_int]
+    lib.oracle_attn_rows_ex.restype = ctypes.c_int
+    lib.oracle_attn_rows_ex.argtypes = [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        vp, vp, vp, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, dp,
+        ctypes.c_int, vp, ctypes.c_longlong, ctypes.c_longlong, ctypes.POINTER(ctypes.c_int),
+        ctypes.c_longlong, llp, dp, dp, dp, ctypes.c_int]
     lib.oracle_visible.restype = ctypes.c_int
     lib.oracle_visible.argtypes = [ctypes.c_int] * 7
     lib.oracle_num_threads.restype = ctypes.c_int
@@ -83,14 +90,29 @@ def num_threads(threads: int = 0, lib=None) -> int:
     return (lib or _load()).oracle_num_threads(threads)
 
 
+BIAS_NONE, BIAS_F32, BIAS_BOOL = 0, 1, 2
+
+
+def bias_strides(bias: np.ndarray, N: int, Hq: int, L: int, S: int):
+    """Element strides (batch, head) of a bias of shape (N or 1, Hq or 1, L, S); 0 = broadcast."""
+    if bias.ndim != 4 or bias.shape[2:] != (L, S) or bias.shape[0] not in (1, N) or bias.shape[1] not in (1, Hq):
+        raise ValueError(f"bias shape {bias.shape} does not broadcast to ({N}, {Hq}, {L}, {S})")
+    sh = L * S if (bias.shape[1] == Hq and Hq > 1) else 0
+    sn = bias.shape[1] * L * S if (bias.shape[0] == N and N > 1) else 0
+    return sn, sh
+
+
 def attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, mode: str = "dot", scale: Optional[float] = None,
          gamma: float = 0.0, causal: bool = False, window: int = 0, n_reg: int = 0,
-         sink: Optional[np.ndarray] = None, rows: Optional[Sequence[int]] = None,
+         sink: Optional[np.ndarray] = None, bias: Optional[np.ndarray] = None,
+         key_len: Optional[Sequence[int]] = None, rows: Optional[Sequence[int]] = None,
          want_p: bool = False, threads: int = 0, lib=None):
     """Attention rows in fp64.
 
     q (N,Hq,L,E), k and v (N,Hkv,S,E): uint16 (bf16 bits), float32 or float64,
     all the same type.  rows: flat indices (n*Hq+h)*L+i, or None for all rows.
+    bias: None, a float32 additive bias or a bool mask (True = use the pair),
+    shape (N or 1, Hq or 1, L, S).  key_len: None or N valid real-key counts.
     Returns (o, lse[, p]): o has shape (N,Hq,L,E) when rows is None, else
     (len(rows), E); lse matches without E; p has S columns.
     lib: a handle from bind() to use instead of the default build.
@@ -126,11 +148,29 @@ def attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, mode: str = "dot", scal
     lse = np.empty(nrows, dtype=np.float64)
     p = np.empty((nrows, S), dtype=np.float64) if want_p else None
     dp = ctypes.POINTER(ctypes.c_double)
-    rc = (lib or _load()).oracle_attn_rows(
+    kind, bptr, sn, sh = BIAS_NONE, None, 0, 0
+    if bias is not None:
+        if bias.dtype == np.float32:
+            kind = BIAS_F32
+            b = np.ascontiguousarray(bias)
+        elif bias.dtype in (np.bool_, np.uint8):
+            kind = BIAS_BOOL
+            b = np.ascontiguousarray(bias.astype(np.uint8))
+        else:
+            raise TypeError("oracle: bias must be float32 or bool")
+        sn, sh = bias_strides(b, N, Hq, L, S)
+        bptr = b.ctypes.data
+    kl = None
+    if key_len is not None:
+        kl = np.ascontiguousarray(np.asarray(key_len, dtype=np.int32).reshape(-1))
+        if kl.shape[0] != N:
+            raise ValueError("oracle: key_len must hold N values")
+    rc = (lib or _load()).oracle_attn_rows_ex(
         dt, N, Hq, Hkv, L, S, E,
         q.ctypes.data, k.ctypes.data, v.ctypes.data, md, float(scale), float(gamma),
         int(bool(causal)), int(window), int(n_reg),
         sk.ctypes.data_as(dp) if sk is not None else None,
+        kind, bptr, sn, sh, kl.ctypes.data_as(ctypes.POINTER(ctypes.c_int)) if kl is not None else None,
         nrows, rptr, o.ctypes.data_as(dp), lse.ctypes.data_as(dp),
         p.ctypes.data_as(dp) if p is not None else None, int(threads))
     if rc != 0:

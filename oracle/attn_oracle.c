@@ -67,7 +67,30 @@ int oracle_attn_rows(int dtype, int N, int Hq, int Hkv, int L, int S, int E,
                      int causal, int window, int n_reg, const double* sink,
                      long long nrows, const long long* rows,
                      double* o, double* lse, double* p, int threads) {
+  return oracle_attn_rows_ex(dtype, N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg,
+                             sink, ORACLE_BIAS_NONE, NULL, 0, 0, NULL, nrows, rows, o, lse, p, threads);
+}
+
+/* user bias of pair (n, h, i, j): 0 when absent; -inf for a masked-out pair */
+static double user_bias(int kind, const void* bias, long long sn, long long sh, int S, int n, int h, int i,
+                        int j) {
+  if (kind == ORACLE_BIAS_NONE) return 0.0;
+  const long long idx = (long long)n * sn + (long long)h * sh + (long long)i * S + j;
+  if (kind == ORACLE_BIAS_F32) return (double)((const float*)bias)[idx];
+  return ((const unsigned char*)bias)[idx] ? 0.0 : -INFINITY;
+}
+
+int oracle_attn_rows_ex(int dtype, int N, int Hq, int Hkv, int L, int S, int E,
+                        const void* q, const void* k, const void* v,
+                        int mode, double scale, double gamma,
+                        int causal, int window, int n_reg, const double* sink,
+                        int bias_kind, const void* bias, long long bias_sn, long long bias_sh,
+                        const int* key_len,
+                        long long nrows, const long long* rows,
+                        double* o, double* lse, double* p, int threads) {
   if (dtype < ORACLE_BF16 || dtype > ORACLE_F64) return -1;
+  if (bias_kind < ORACLE_BIAS_NONE || bias_kind > ORACLE_BIAS_BOOL) return -1;
+  if (bias_kind != ORACLE_BIAS_NONE && (!bias || bias_sn < 0 || bias_sh < 0)) return -3;
   if (mode != ORACLE_DOT && mode != ORACLE_RBF) return -1;
   if (N <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || S < 0 || E <= 0) return -2;
   if (Hq % Hkv != 0) return -2;
@@ -103,11 +126,14 @@ int oracle_attn_rows(int dtype, int N, int Hq, int Hkv, int L, int S, int E,
       double* orow = o + (size_t)r * E;
       double* prow = p ? p + (size_t)r * S : NULL;
 
-      /* z_ij = l_ij + B_ij with B_ij in {0, -inf}; M_i = row max (with sink) */
+      /* z_ij = l_ij + B_ij: B_ij = -inf for a pair the rule hides or a padding
+         key, else the user bias (0 without one); M_i = row max (with sink) */
       double M = -INFINITY;
       for (int j = 0; j < S; ++j) {
-        if (oracle_visible(L, S, causal, window, n_reg, i, j))
-          z[j] = logit(dtype, q, qoff, k, (kvrow0 + j) * E, E, mode, scale, gamma);
+        const int padded = key_len && j >= n_reg && (j - n_reg) >= key_len[n];
+        const double b = user_bias(bias_kind, bias, bias_sn, bias_sh, S, n, h, i, j);
+        if (oracle_visible(L, S, causal, window, n_reg, i, j) && !padded && b != -INFINITY)
+          z[j] = logit(dtype, q, qoff, k, (kvrow0 + j) * E, E, mode, scale, gamma) + b;
         else
           z[j] = -INFINITY;
         if (z[j] > M) M = z[j];

@@ -70,6 +70,30 @@ int oracle_attn_rows(int dtype, int N, int Hq, int Hkv, int L, int S, int E,
                      long long nrows, const long long* rows,
                      double* o, double* lse, double* p, int threads);
 
+/*
+ * Same, with a general bias B on top of the rule above ("SDPA란 무엇인가?"
+ * section 1: B is an L x S matrix added to the logits before the softmax;
+ * section 4: a boolean attn_mask is True where a pair is used, the opposite of
+ * a key-padding mask, and masks are combined with AND):
+ *   bias_kind ORACLE_BIAS_F32:  float32 b[n*bias_sn + h*bias_sh + i*S + j] is
+ *                               added to the logit of a visible pair (natural-
+ *                               log units; -inf hides the pair)
+ *   bias_kind ORACLE_BIAS_BOOL: uint8 m[...] at the same index; 0 hides the pair
+ *   key_len (may be NULL):      key_len[n] real keys are valid in sequence n;
+ *                               real keys r >= key_len[n] are padding (hidden)
+ * Strides are in elements; 0 broadcasts over that dimension.  The causal and
+ * window rule keeps its bottom-right alignment over all S keys.
+ */
+enum { ORACLE_BIAS_NONE = 0, ORACLE_BIAS_F32 = 1, ORACLE_BIAS_BOOL = 2 };
+int oracle_attn_rows_ex(int dtype, int N, int Hq, int Hkv, int L, int S, int E,
+                        const void* q, const void* k, const void* v,
+                        int mode, double scale, double gamma,
+                        int causal, int window, int n_reg, const double* sink,
+                        int bias_kind, const void* bias, long long bias_sn, long long bias_sh,
+                        const int* key_len,
+                        long long nrows, const long long* rows,
+                        double* o, double* lse, double* p, int threads);
+
 /* Number of OpenMP threads oracle_attn_rows uses for a given `threads`. */
 int oracle_num_threads(int threads);
 

@@ -33,7 +33,7 @@ STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR
 BF16, F32 = 0, 1
 MODES = {"dot": 0, "rbf": 1}
 
-EXPORTS = ("attn_fwd", "attn_decode", "attn_decode_num_splits", "attn_decode_workspace_bytes",
+EXPORTS = ("attn_fwd", "attn_fwd_biased", "attn_decode", "attn_decode_num_splits", "attn_decode_workspace_bytes",
            "attn_stream_append", "attn_stream_decode", "attn_stream_decode_workspace_bytes",
            "attn_status_string", "attn_last_error")
 
@@ -57,6 +57,9 @@ def load() -> ctypes.CDLL:
         I, F, P, Z = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
         lib.attn_fwd.restype = I
         lib.attn_fwd.argtypes = [I, I, I, I, I, I, I, P, P, P, I, F, F, I, I, I, P, P, P, P]
+        LLb = ctypes.c_longlong
+        lib.attn_fwd_biased.restype = I
+        lib.attn_fwd_biased.argtypes = [I, I, I, I, I, I, I, P, P, P, I, F, F, I, I, I, P, I, P, LLb, LLb, P, P, P, P]
         lib.attn_decode.restype = I
         lib.attn_decode.argtypes = [I, I, I, I, I, I, I, P, P, P, I, F, F, I, I, I, P, P, P, I, P, Z, P]
         lib.attn_decode_num_splits.restype = I
@@ -129,20 +132,59 @@ def _stream(dev: torch.device, stream) -> int:
     return s.cuda_stream
 
 
+BIAS_NONE, BIAS_F32, BIAS_BOOL = 0, 1, 2
+
+
+def _bias_args(bias: torch.Tensor, N: int, Hq: int, L: int, S: int, dev):
+    """(kind, tensor, stride_n, stride_h) for a bias of shape (L, S) or (N or 1, Hq or 1, L, S)."""
+    if bias.dim() == 2:
+        bias = bias.reshape(1, 1, *bias.shape)
+    if bias.dim() != 4 or tuple(bias.shape[2:]) != (L, S) or bias.shape[0] not in (1, N) or \
+            bias.shape[1] not in (1, Hq):
+        raise ValueError(f"bias {tuple(bias.shape)} does not broadcast to ({N}, {Hq}, {L}, {S})")
+    if not bias.is_contiguous() or bias.device != dev:
+        raise ValueError("bias must be contiguous and on q's device")
+    if bias.dtype == torch.float32:
+        kind = BIAS_F32
+    elif bias.dtype in (torch.bool, torch.uint8):
+        kind = BIAS_BOOL
+        bias = bias.view(torch.uint8)
+    else:
+        raise TypeError(f"bias must be float32 (added to the logits) or bool (True = attend), got {bias.dtype}")
+    sh = L * S if (bias.shape[1] == Hq and Hq > 1) else 0
+    sn = bias.shape[1] * L * S if (bias.shape[0] == N and N > 1) else 0
+    return kind, bias, sn, sh
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
         mode: str = "dot", gamma: Optional[float] = None, causal: bool = False, window: int = 0,
-        n_reg: int = 0, sink: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+        n_reg: int = 0, sink: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+        key_len: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
         lse: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Attention forward through attn_fwd; returns (o, lse)."""
+    """Attention forward through attn_fwd (or attn_fwd_biased when a bias or key lengths are given);
+    returns (o, lse).  bias: float32 addend or bool mask (True = attend), shape (L, S) or
+    (N or 1, Hq or 1, L, S); key_len: (N,) int32, real keys past key_len[n] are padding."""
     N, Hq, Hkv, L, S, E, scale, gamma = _common(q, k, v, sink, scale, mode, gamma)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((N, Hq, L), dtype=torch.float32, device=q.device)
     lib = load()
-    rc = lib.attn_fwd(_dtype_code(q), N, Hq, Hkv, L, S, E, _ptr(q), _ptr(k), _ptr(v), MODES[mode],
-                      scale, gamma, int(bool(causal)), int(window), int(n_reg), _ptr(sink),
-                      _ptr(out), _ptr(lse), _stream(q.device, stream))
+    if bias is None and key_len is None:
+        rc = lib.attn_fwd(_dtype_code(q), N, Hq, Hkv, L, S, E, _ptr(q), _ptr(k), _ptr(v), MODES[mode],
+                          scale, gamma, int(bool(causal)), int(window), int(n_reg), _ptr(sink),
+                          _ptr(out), _ptr(lse), _stream(q.device, stream))
+        _check(rc)
+        return out, lse
+    kind, bt, sn, sh = (BIAS_NONE, None, 0, 0) if bias is None else _bias_args(bias, N, Hq, L, S, q.device)
+    if key_len is not None:
+        if key_len.dtype != torch.int32 or key_len.numel() != N or key_len.device != q.device or \
+                not key_len.is_contiguous():
+            raise ValueError("key_len must be a contiguous int32 tensor of N values on q's device")
+    rc = lib.attn_fwd_biased(_dtype_code(q), N, Hq, Hkv, L, S, E, _ptr(q), _ptr(k), _ptr(v), MODES[mode],
+                             scale, gamma, int(bool(causal)), int(window), int(n_reg), _ptr(sink),
+                             kind, _ptr(bt), sn, sh, _ptr(key_len), _ptr(out), _ptr(lse),
+                             _stream(q.device, stream))
     _check(rc)
     return out, lse
 

@@ -83,6 +83,11 @@ attn_impl::FwdArgs make_args(int N, int Hq, int Hkv, int L, int S, int E, const 
   a.S = S;
   a.E = E;
   a.kv_rows = S;
+  a.key_len = nullptr;
+  a.bias = nullptr;
+  a.bias_kind = 0;
+  a.bias_sn = 0;
+  a.bias_sh = 0;
   a.n_reg = n_reg;
   a.causal = causal ? 1 : 0;
   a.window = window;
@@ -146,6 +151,44 @@ int attn_fwd(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, const v
   hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e = dt == ATTN_BF16 ? attn_impl::launch_prefill_bf16(a, st) : attn_impl::launch_prefill_f32(a, st);
   return hip_status(e, "attn_fwd launch");
+}
+
+int attn_fwd_biased(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, const void* q, const void* k,
+                    const void* v, attn_mode mode, float scale, float gamma, int causal, int window, int n_reg,
+                    const float* sink, attn_bias_kind bias_kind, const void* bias, long long bias_stride_n,
+                    long long bias_stride_h, const int* key_len, void* o, float* lse, void* stream) {
+  int rc = check_args(dt, N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o, lse);
+  if (rc != ATTN_OK) return rc;
+  if (bias_kind != ATTN_BIAS_NONE && bias_kind != ATTN_BIAS_F32 && bias_kind != ATTN_BIAS_BOOL)
+    return fail(ATTN_ERR_ARG, "unknown bias kind %d", (int)bias_kind);
+  if (bias_kind != ATTN_BIAS_NONE && (bias_stride_n < 0 || bias_stride_h < 0))
+    return fail(ATTN_ERR_ARG, "bias strides must be >= 0 (got %lld, %lld)", bias_stride_n, bias_stride_h);
+  if ((long long)N * Hq * L == 0) return ok();
+  if (bias_kind != ATTN_BIAS_NONE) {
+    if (!bias) return fail(ATTN_ERR_NULL, "bias must not be NULL for bias kind %d", (int)bias_kind);
+    if (bias_kind == ATTN_BIAS_F32 && !aligned(bias, 4)) return fail(ATTN_ERR_ALIGN, "a float32 bias must be 4-byte aligned");
+    // the last element addressed must stay within an int64 element index
+    const long long last = (long long)(N - 1) * bias_stride_n + (long long)(Hq - 1) * bias_stride_h +
+                           (long long)L * S;
+    if (bias_stride_n > kMaxElems || bias_stride_h > kMaxElems || last > (1LL << 50))
+      return fail(ATTN_ERR_SHAPE, "bias strides too large");
+  }
+  if (key_len && !aligned(key_len, 4)) return fail(ATTN_ERR_ALIGN, "key_len must be 4-byte aligned");
+  if (dt == ATTN_BF16 && ((long long)S + 64) * E * 2 > 0x7fffffffLL)
+    return fail(ATTN_ERR_UNSUPPORTED, "a (batch, kv head) slice of K/V near or above 2 GiB (S=%d, E=%d)", S, E);
+  if ((long long)((L + 63) / 64) * N * Hq > kMaxGrid) return fail(ATTN_ERR_SHAPE, "grid too large");
+  attn_impl::FwdArgs a =
+      make_args(N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o, lse);
+  a.key_len = key_len;
+  if (bias_kind != ATTN_BIAS_NONE) {
+    a.bias = bias;
+    a.bias_kind = (int)bias_kind;
+    a.bias_sn = bias_stride_n;
+    a.bias_sh = bias_stride_h;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = dt == ATTN_BF16 ? attn_impl::launch_prefill_bf16(a, st) : attn_impl::launch_prefill_f32(a, st);
+  return hip_status(e, "attn_fwd_biased launch");
 }
 
 int attn_decode_num_splits(int N, int Hq, int Hkv, int S, int E, int causal, int window, int n_reg) {

@@ -28,6 +28,14 @@ struct FwdArgs {
   int rbf;            // 0 = dot, 1 = rbf
   float scale;        // dot logit scale
   float gamma;        // rbf width
+  // General bias (prefill only): key_len (N ints) marks real keys r >= key_len[n]
+  // as padding; bias is a float32 addend (bias_kind 1, natural-log units) or a
+  // uint8 mask (bias_kind 2, 0 hides the pair) at bias[n*bias_sn + h*bias_sh +
+  // i*S + j].  nullptr = none.
+  const int* key_len;
+  const void* bias;
+  int bias_kind;
+  long long bias_sn, bias_sh;
 };
 
 // Split-K decode: workspace holds the per-split partial results.

@@ -65,6 +65,9 @@ struct PrefillParams {
   const float* sink;
   int N, Hq, Hkv, L, S, n_reg, S_real, off, causal, window;
   float c_logit, c_bias, gamma;
+  const int* key_len;     // N valid real-key counts, or nullptr
+  const void* ubias;      // user bias: float32 (log2 units after scaling) or uint8 mask, or nullptr
+  long long ub_sn, ub_sh; // its element strides over batch and head (0 = broadcast); rows are S apart
   int num_q_tiles;
   int xcd_groups;   // 1: the 8 XCDs each take whole K/V heads (needs N*Hkv % 8 == 0)
   int heavy_first;  // 1: causal, dispatch the query tiles with the most keys first
@@ -144,19 +147,25 @@ __device__ __forceinline__ void buffer_load16_to_lds(__amdgpu_buffer_rsrc_t r, u
 #endif
 }
 
+// User bias kinds (a compile-time parameter): none, float32 added to the
+// logits, uint8 mask (0 hides the pair).
+enum { kBiasNone = 0, kBiasF32 = 1, kBiasBool = 2 };
+
 // Waves per SIMD the register budget allows: E = 128 needs ~230 VGPRs (2 waves);
 // E = 64 fits in 128 VGPRs in dot mode (4 waves = 4 workgroups per CU, 128 KB of
-// LDS) and under 168 in RBF mode (3 waves), where 128 would spill.
-template <int E, int MODE>
+// LDS) and under 168 in RBF mode or with a user bias (3 waves), where 128 would
+// spill.
+template <int E, int MODE, int UB>
 struct Occupancy {
-  static constexpr int kWaves = E == 64 ? (MODE == kRbf ? 3 : 4) : 2;
+  static constexpr int kWaves = E == 64 ? ((MODE == kRbf || UB != 0) ? 3 : 4) : 2;
 };
 
-template <int E, int MODE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Occupancy<E, MODE>::kWaves, Occupancy<E, MODE>::kWaves)))
+template <int E, int MODE, int UB>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Occupancy<E, MODE, UB>::kWaves, Occupancy<E, MODE, UB>::kWaves)))
 void prefill_bf16_kernel(PrefillParams p) {
   constexpr bool RBF = MODE == kRbf;
   constexpr bool FAST = MODE == kDotPos;
+  static_assert(UB == kBiasNone || !FAST, "a user bias needs the logits formed before the max");
   constexpr int OSTR = E + 8;   // epilogue O row stride (elements)
   constexpr int QS = E / 16;    // MFMA steps over the head dimension
   constexpr int EB = E / 32;    // 32-row blocks of O^T
@@ -221,8 +230,10 @@ void prefill_bf16_kernel(PrefillParams p) {
     for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
 
   // Tiles: register rows first, then the real keys some row of this workgroup sees.
+  // Real keys at or past kl are padding of this sequence (no key lengths: none).
+  const int kl = p.key_len ? max(0, min(p.S_real, p.key_len[n])) : p.S_real;
   const int i_last = min(i0 + BM, p.L) - 1;
-  const int r_hi = p.causal ? min(p.S_real - 1, i_last + p.off) : p.S_real - 1;
+  const int r_hi = p.causal ? min(kl - 1, i_last + p.off) : kl - 1;
   const int r_lo = p.window > 0 ? max(0, i0 + p.off - p.window + 1) : 0;
   const int n_real_tiles = r_hi >= r_lo ? (r_hi - r_lo + BN) / BN : 0;
   const int n_reg_tiles = (p.n_reg + BN - 1) / BN;
@@ -331,14 +342,32 @@ void prefill_bf16_kernel(PrefillParams p) {
       full = (kc == BN);
     } else {
       const int ra = j0 - p.n_reg, rb = ra + BN - 1;
-      any = !((ra >= p.S_real) || (p.causal && ra > qb + p.off) ||
+      any = !((ra >= kl) || (p.causal && ra > qb + p.off) ||
               (p.window > 0 && qa + p.off - rb >= p.window));
-      full = rb < p.S_real && (!p.causal || rb <= qa + p.off) &&
+      full = rb < kl && (!p.causal || rb <= qa + p.off) &&
              (p.window <= 0 || qb + p.off - ra < p.window);
     }
     if (!any) return;
     const uint8_t* k_s = k_tile(buf);
     const uint8_t* v_s = v_tile(buf);
+
+    // User bias of this lane's row for the tile's keys, in log2 units (a masked
+    // pair gets -inf), loaded before the MFMAs so that the loads overlap them.
+    // Keys past the end of K read the last column; the rule hides those pairs.
+    float ubv[UB != kBiasNone ? NB : 1][16];
+    if (UB != kBiasNone) {
+      const long long rowoff = (long long)n * p.ub_sn + (long long)h * p.ub_sh + (long long)min(qi, p.L - 1) * p.S;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const long long j = rowoff + min(j0 + 32 * b + 8 * (r >> 2) + 4 * g + (r & 3), p.S - 1);
+          if (UB == kBiasF32)
+            ubv[b][r] = static_cast<const float*>(p.ubias)[j] * kLog2e;
+          else
+            ubv[b][r] = static_cast<const uint8_t*>(p.ubias)[j] ? 0.f : kNegInf;
+        }
+    }
 
     // S^T = K * Q^T for NB blocks of 32 keys; the NB accumulation chains are
     // interleaved so that consecutive MFMAs never depend on each other.
@@ -371,6 +400,7 @@ void prefill_bf16_kernel(PrefillParams p) {
         for (int r = 0; r < 16; ++r) {
           float x = st[b][r] * p.c_logit;
           if (RBF) x += sBias[buf][32 * b + 8 * (r >> 2) + 4 * g + (r & 3)];
+          if (UB != kBiasNone) x += ubv[b][r];
           st[b][r] = x;
         }
     }
@@ -384,7 +414,7 @@ void prefill_bf16_kernel(PrefillParams p) {
       } else {
         const int base = j0 - p.n_reg;  // real position of tile key 0
         const int ip = qi + p.off;      // this row's aligned position
-        hi = min(p.S_real - 1, p.causal ? ip : p.S_real - 1) - base;
+        hi = min(kl - 1, p.causal ? ip : kl - 1) - base;
         lo = (p.window > 0 ? ip - p.window + 1 : 0) - base;
       }
       lo -= 4 * g;
@@ -459,7 +489,7 @@ void prefill_bf16_kernel(PrefillParams p) {
   // (and the register tiles) run with it.
   int k_full0 = 0, k_full1 = -1;
   {
-    const int lim = min(p.S_real - 1, p.causal ? i0 + p.off : p.S_real - 1);
+    const int lim = min(kl - 1, p.causal ? i0 + p.off : kl - 1);
     k_full1 = (lim - r_lo - (BN - 1)) >= 0 ? (lim - r_lo - (BN - 1)) / BN : -1;
     if (p.window > 0) {
       const int need = i_last + p.off - p.window + 1 - r_lo;  // first ra allowed
@@ -528,18 +558,20 @@ void prefill_bf16_kernel(PrefillParams p) {
   }
 }
 
-template <int E, int MODE>
+template <int E, int MODE, int UB>
 hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
   const long long blocks = (long long)p.num_q_tiles * p.N * p.Hq;
-  hipLaunchKernelGGL((prefill_bf16_kernel<E, MODE>), dim3((unsigned)blocks), dim3(NT), 0, stream, p);
+  hipLaunchKernelGGL((prefill_bf16_kernel<E, MODE, UB>), dim3((unsigned)blocks), dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int E>
-hipError_t launch_e(const PrefillParams& p, bool rbf, hipStream_t stream) {
-  if (rbf) return launch_t<E, kRbf>(p, stream);
-  if (p.c_logit > 0.f) return launch_t<E, kDotPos>(p, stream);
-  return launch_t<E, kDotAny>(p, stream);
+hipError_t launch_e(const PrefillParams& p, bool rbf, int ub, hipStream_t stream) {
+  if (ub == kBiasF32) return rbf ? launch_t<E, kRbf, kBiasF32>(p, stream) : launch_t<E, kDotAny, kBiasF32>(p, stream);
+  if (ub == kBiasBool) return rbf ? launch_t<E, kRbf, kBiasBool>(p, stream) : launch_t<E, kDotAny, kBiasBool>(p, stream);
+  if (rbf) return launch_t<E, kRbf, kBiasNone>(p, stream);
+  if (p.c_logit > 0.f) return launch_t<E, kDotPos, kBiasNone>(p, stream);
+  return launch_t<E, kDotAny, kBiasNone>(p, stream);
 }
 
 }  // namespace
@@ -572,11 +604,16 @@ hipError_t launch_prefill_bf16(const FwdArgs& a, hipStream_t stream) {
     p.c_logit = a.scale * 1.4426950408889634f;
     p.c_bias = 0.f;
   }
+  p.key_len = a.key_len;
+  p.ubias = a.bias;
+  p.ub_sn = a.bias_sn;
+  p.ub_sh = a.bias_sh;
   p.num_q_tiles = (a.L + BM - 1) / BM;
   p.xcd_groups = ((a.N * a.Hkv) % 8 == 0) ? 1 : 0;
   p.heavy_first = p.causal;
-  if (a.E == 128) return launch_e<128>(p, a.rbf != 0, stream);
-  return launch_e<64>(p, a.rbf != 0, stream);
+  const int ub = a.bias ? a.bias_kind : kBiasNone;
+  if (a.E == 128) return launch_e<128>(p, a.rbf != 0, ub, stream);
+  return launch_e<64>(p, a.rbf != 0, ub, stream);
 }
 
 }  // namespace attn_impl

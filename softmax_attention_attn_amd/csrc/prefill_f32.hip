@@ -26,6 +26,10 @@ struct PrefillF32Params {
   const float* sink;
   int N, Hq, Hkv, L, S, n_reg, S_real, off, causal, window;
   float c_logit, c_bias, gamma;
+  const int* key_len;     // N valid real-key counts, or nullptr
+  const void* ubias;      // user bias (float32 addend or uint8 mask), or nullptr
+  int ub_kind;            // 1 = float32, 2 = uint8 mask
+  long long ub_sn, ub_sh; // element strides over batch and head (0 = broadcast); rows are S apart
   int num_q_tiles;
 };
 
@@ -61,8 +65,11 @@ __global__ __launch_bounds__(BQ) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     lsum = 1.f;
   }
 
+  // Real keys at or past kl are padding of this sequence (no key lengths: none).
+  const int kl = p.key_len ? max(0, min(p.S_real, p.key_len[n])) : p.S_real;
+  const long long ub_row = (long long)n * p.ub_sn + (long long)h * p.ub_sh + (long long)(qvalid ? qi : 0) * p.S;
   const int i_last = min(i0 + BQ, p.L) - 1;
-  const int r_hi = p.causal ? min(p.S_real - 1, i_last + p.off) : p.S_real - 1;
+  const int r_hi = p.causal ? min(kl - 1, i_last + p.off) : kl - 1;
   const int r_lo = p.window > 0 ? max(0, i0 + p.off - p.window + 1) : 0;
   const int n_real_tiles = r_hi >= r_lo ? (r_hi - r_lo + BK) / BK : 0;
   const int n_reg_tiles = (p.n_reg + BK - 1) / BK;
@@ -110,8 +117,17 @@ __global__ __launch_bounds__(BQ) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         vis = kt < kc;
       } else {
         const int rr = j0 - p.n_reg + kt;
-        vis = rr < p.S_real && (!p.causal || rr <= qi + p.off) &&
+        vis = rr < kl && (!p.causal || rr <= qi + p.off) &&
               (p.window <= 0 || qi + p.off - rr < p.window);
+      }
+      if (vis && p.ubias) {  // user bias: natural-log addend, or a mask where 0 hides the pair
+        if (p.ub_kind == 1) {
+          const float b = static_cast<const float*>(p.ubias)[ub_row + j0 + kt];
+          vis = b != kNegInf;
+          x = __builtin_fmaf(b, kLog2e, x);
+        } else {
+          vis = static_cast<const uint8_t*>(p.ubias)[ub_row + j0 + kt] != 0;
+        }
       }
       if (!vis) continue;  // weight exactly zero
       if (x > m) {         // new running max: rescale what was accumulated
@@ -173,6 +189,11 @@ hipError_t launch_prefill_f32(const FwdArgs& a, hipStream_t stream) {
   p.S_real = a.S - a.n_reg;
   p.off = a.S - a.n_reg - a.L;
   p.causal = a.causal ? 1 : 0;
+  p.key_len = a.key_len;
+  p.ubias = a.bias;
+  p.ub_kind = a.bias_kind;
+  p.ub_sn = a.bias_sn;
+  p.ub_sh = a.bias_sh;
   p.window = a.window;
   p.gamma = a.gamma;
   if (a.rbf) {

@@ -55,9 +55,16 @@ def sample_rows(w: Workload, per_head: int = 4, extra: int = 256, seed: int = 0)
     return np.array(sorted(rows), dtype=np.int64)
 
 
-def compare(w: Workload, inp: gen.Inputs, o_gpu: torch.Tensor, lse_gpu: torch.Tensor, rows=None, threads=0):
-    """Max-abs errors of O and LSE against the oracle (all rows or the given flat rows)."""
-    o_ref, lse_ref = oracle.attn_workload(inp, rows=rows, threads=threads)
+def compare(w: Workload, inp: gen.Inputs, o_gpu: torch.Tensor, lse_gpu: torch.Tensor, rows=None, threads=0,
+            bias=None, key_len=None):
+    """Max-abs errors of O and LSE against the oracle (all rows or the given flat rows);
+    bias / key_len (numpy) are passed to the oracle as the general bias."""
+    if bias is None and key_len is None:
+        o_ref, lse_ref = oracle.attn_workload(inp, rows=rows, threads=threads)
+    else:
+        o_ref, lse_ref = oracle.attn(inp.q, inp.k, inp.v, mode=w.mode, scale=w.scale, gamma=w.gamma,
+                                     causal=w.causal, window=w.window, n_reg=w.n_reg, sink=inp.sink, bias=bias,
+                                     key_len=key_len, rows=rows, threads=threads)
     og = o_gpu.float().cpu().numpy().astype(np.float64).reshape(-1, w.E)
     lg = lse_gpu.cpu().numpy().astype(np.float64).reshape(-1)
     o_ref = o_ref.reshape(-1, w.E)
@@ -75,8 +82,8 @@ def compare(w: Workload, inp: gen.Inputs, o_gpu: torch.Tensor, lse_gpu: torch.Te
     return float(eo.max()) if eo.size else 0.0, float(el.max()) if el.size else 0.0, worst
 
 
-def check(w: Workload, inp: gen.Inputs, o_gpu, lse_gpu, rows=None, threads=0):
-    eo, el, worst = compare(w, inp, o_gpu, lse_gpu, rows=rows, threads=threads)
+def check(w: Workload, inp: gen.Inputs, o_gpu, lse_gpu, rows=None, threads=0, bias=None, key_len=None):
+    eo, el, worst = compare(w, inp, o_gpu, lse_gpu, rows=rows, threads=threads, bias=bias, key_len=key_len)
     say(f"  {w.name}: max|dO|={eo:.3e} (worst row/col {worst}) max|dLSE|={el:.3e}")
     assert eo <= TOL_O[w.dtype], f"{w.name}: O error {eo:.3e} > {TOL_O[w.dtype]}"
     assert el <= TOL_LSE, f"{w.name}: LSE error {el:.3e} > {TOL_LSE}"

@@ -441,4 +441,34 @@ def pin_row_sampling(lib):
     _bitwise(part[1], full[1].reshape(-1)[rows], "sampled LSE")
 
 
+def pin_float_bias_matches_sdpa_mask(lib):
+    # SDPA page section 1: softmax(QK^T*scale + B) V with a float B (torch's attn_mask)
+    q, k, v = _qkv(61, 2, 3, 3, 6, 9, 8)
+    b = _rng(62).standard_normal((2, 1, 6, 9)).astype(np.float32)
+    b[1, 0, 2, [1, 4]] = -np.inf
+    o, _ = oracle.attn(q, k, v, scale=0.3, bias=b, lib=lib)
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                                         attn_mask=torch.from_numpy(b.astype(np.float64)), scale=0.3)
+    assert np.max(np.abs(o - ref.numpy())) < 1e-12
+
+
+def pin_bool_mask_true_means_attend(lib):
+    # SDPA page section 4: in attn_mask, True = the pair takes part
+    q, k, v = _qkv(63, 1, 2, 2, 5, 7, 8)
+    m = _rng(64).random((1, 2, 5, 7)) < 0.5
+    m[..., 3] = True
+    o, _ = oracle.attn(q, k, v, bias=m, lib=lib)
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                                         attn_mask=torch.from_numpy(m))
+    assert np.max(np.abs(o - ref.numpy())) < 1e-12
+
+
+def pin_key_padding_equals_slicing(lib):
+    # padded keys take no part: same as cutting K/V after the valid ones
+    q, k, v = _qkv(65, 2, 2, 2, 4, 10, 8)
+    o, lse = oracle.attn(q, k, v, key_len=[6, 10], lib=lib)
+    o1, l1 = oracle.attn(q[:1], k[:1, :, :6], v[:1, :, :6], lib=lib)
+    assert np.max(np.abs(o[:1] - o1)) < 1e-12 and np.max(np.abs(lse[:1] - l1)) < 1e-12
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

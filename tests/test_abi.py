@@ -115,6 +115,34 @@ def test_decode_split_and_workspace_sizes(lib):
     assert lib.attn_decode_workspace_bytes(1, 4, 3, 100, 64, 1, 0, 0, 0) == 0
 
 
+def fwdb(lib, dt=0, N=2, Hq=4, Hkv=2, L=8, S=8, E=64, q=A, k=A, v=A, mode=0, scale=0.125, gamma=0.0, causal=1,
+         window=0, n_reg=0, sink=None, kind=1, bias=A, sn=0, sh=64, key_len=None, o=A, lse=A):
+    return lib.attn_fwd_biased(dt, N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink,
+                               kind, bias, sn, sh, key_len, o, lse, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kind=3), -8),
+    (dict(kind=-1), -8),
+    (dict(sn=-64), -8),
+    (dict(sh=-1), -8),
+    (dict(bias=None), -1),
+    (dict(bias=A + 2), -5),
+    (dict(key_len=A + 2), -5),
+    (dict(Hq=3), -2),
+    (dict(E=48), -4),
+    (dict(sn=1 << 45), -2),
+])
+def test_fwd_biased_rejects(lib, kw, code):
+    assert fwdb(lib, **kw) == code
+
+
+def test_fwd_biased_accepts_unaligned_mask_and_empty(lib):
+    # a uint8 mask needs no alignment; nothing to compute -> no launch
+    assert fwdb(lib, kind=2, bias=A + 3, N=0, q=None, k=None, v=None, o=None, lse=None) == 0
+    assert fwdb(lib, kind=0, bias=None, L=0) == 0
+
+
 def app(lib, dt=0, N=1, Hkv=2, E=64, n_sink=4, window=16, pos=0, T=3, kn=A, vn=A, kc=A, vc=A):
     return lib.attn_stream_append(dt, N, Hkv, E, n_sink, window, pos, T, kn, vn, kc, vc, None)
 

@@ -25,8 +25,14 @@ MUTANTS = {
     "rbf_plus": ("double d = load_elem(dtype, q, qoff + e) - load_elem(dtype, k, koff + e);",
                  "double d = load_elem(dtype, q, qoff + e) + load_elem(dtype, k, koff + e);"),
     "scale_dropped": ("return scale * acc;", "return acc;"),
-    "key_row_reversed": ("z[j] = logit(dtype, q, qoff, k, (kvrow0 + j) * E, E, mode, scale, gamma);",
-                         "z[j] = logit(dtype, q, qoff, k, (kvrow0 + (S - 1 - j)) * E, E, mode, scale, gamma);"),
+    "key_row_reversed": ("z[j] = logit(dtype, q, qoff, k, (kvrow0 + j) * E, E, mode, scale, gamma) + b;",
+                         "z[j] = logit(dtype, q, qoff, k, (kvrow0 + (S - 1 - j)) * E, E, mode, scale, gamma) + b;"),
+    "bias_sign": ("scale, gamma) + b;", "scale, gamma) - b;"),
+    "bool_mask_inverted": ("((const unsigned char*)bias)[idx] ? 0.0 : -INFINITY;",
+                           "((const unsigned char*)bias)[idx] ? -INFINITY : 0.0;"),
+    "key_len_ignored": ("const int padded = key_len && j >= n_reg && (j - n_reg) >= key_len[n];",
+                        "const int padded = 0;"),
+    "bias_head_stride_dropped": ("(long long)h * sh +", ""),
     "head_dim_truncated": ("for (int e = 0; e < E; ++e) acc += load_elem", "for (int e = 0; e < E - 1; ++e) acc += load_elem"),
     "lse_without_max": ("lse[r] = M + log(D);", "lse[r] = log(D);"),
     "empty_row_nan": ("if (M == -INFINITY) {", "if (0) {"),

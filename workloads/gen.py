@@ -138,3 +138,27 @@ def generate(w: Workload, threads: Optional[int] = None) -> Inputs:
         with ThreadPoolExecutor(nthr) as ex:
             list(ex.map(run, jobs))
     return Inputs(w, q, k, v, sink_logits(w))
+
+
+# ----------------------------------------------------------------------------- general bias inputs
+
+
+def bias_f32(seed: int, shape, scale: float = 1.0, p_neg_inf: float = 0.0) -> np.ndarray:
+    """Float32 bias N(0, scale); a fraction p_neg_inf of the entries is -inf (hidden pairs)."""
+    r = _rng(seed, 7)
+    b = (r.standard_normal(shape) * scale).astype(np.float32)
+    if p_neg_inf > 0.0:
+        b[r.random(shape) < p_neg_inf] = -np.inf
+    return b
+
+
+def mask_bool(seed: int, shape, p_keep: float) -> np.ndarray:
+    """Boolean mask (True = the pair is used) with each entry kept with probability p_keep."""
+    return _rng(seed, 8).random(shape) < p_keep
+
+
+def key_lengths(seed: int, N: int, S_real: int) -> np.ndarray:
+    """Per-sequence valid key counts in [0, S_real] (int32); the first one is always S_real."""
+    k = _rng(seed, 9).integers(0, S_real + 1, size=N).astype(np.int32)
+    k[0] = S_real
+    return k
