@@ -94,6 +94,8 @@ def time_workload(w, steps: int, warmup: int, rotate: int, torch, attn, keep_fir
     inp = gen.generate(w)
     log(f"[bench] {w.name}: inputs ready in {time.time() - t0:.1f}s, copying to the GPU")
     q, k, v, sink = to_device(inp, torch, dev)
+    ub = torch.from_numpy(inp.bias).to(dev) if inp.bias is not None else None
+    kl = torch.from_numpy(inp.key_len).to(dev) if inp.key_len is not None else None
     sets = [(q, k, v)]
     for _ in range(max(0, rotate - 1)):
         sets.append((q.clone(), k.clone(), v.clone()))
@@ -112,7 +114,7 @@ def time_workload(w, steps: int, warmup: int, rotate: int, torch, attn, keep_fir
         if w.decode:
             attn.decode(qq, kk, vv, workspace=ws, out=oo, lse=ll, **kw)
         else:
-            attn.fwd(qq, kk, vv, out=oo, lse=ll, **kw)
+            attn.fwd(qq, kk, vv, out=oo, lse=ll, bias=ub, key_len=kl, **kw)
 
     call(0)
     torch.cuda.synchronize()
@@ -326,7 +328,7 @@ def main() -> int:
     del inp, first
     if args.extras == "all":
         extras = {}
-        for x in configs.ALL:
+        for x in configs.ALL + configs.EXTRA:
             if x.name == w.name:
                 continue
             rot = 3 if (not x.decode and configs.algorithmic_bytes(x) < 256e6 and x.name == configs.C4.name) else 1

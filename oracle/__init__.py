@@ -186,7 +186,8 @@ def attn_workload(inp, rows: Optional[Sequence[int]] = None, want_p: bool = Fals
     """Run the oracle on a workloads.gen.Inputs bundle (same flags as its workload)."""
     w = inp.workload
     return attn(inp.q, inp.k, inp.v, mode=w.mode, scale=w.scale, gamma=w.gamma, causal=w.causal,
-                window=w.window, n_reg=w.n_reg, sink=inp.sink, rows=rows, want_p=want_p, threads=threads)
+                window=w.window, n_reg=w.n_reg, sink=inp.sink, bias=getattr(inp, "bias", None),
+                key_len=getattr(inp, "key_len", None), rows=rows, want_p=want_p, threads=threads)
 
 
 # ----------------------------------------------------------------------------- rolling (StreamingLLM) cache

@@ -354,19 +354,43 @@ void prefill_bf16_kernel(PrefillParams p) {
     // User bias of this lane's row for the tile's keys, in log2 units (a masked
     // pair gets -inf), loaded before the MFMAs so that the loads overlap them.
     // Keys past the end of K read the last column; the rule hides those pairs.
+    // Each lane's keys come in runs of 4 consecutive columns; when every run is
+    // 4-element aligned and inside the row (uniform test), one 16-byte (float)
+    // or 4-byte (mask) load fetches a run.
     float ubv[UB != kBiasNone ? NB : 1][16];
     if (UB != kBiasNone) {
-      const long long rowoff = (long long)n * p.ub_sn + (long long)h * p.ub_sh + (long long)min(qi, p.L - 1) * p.S;
+      const long long base_nh = (long long)n * p.ub_sn + (long long)h * p.ub_sh;
+      const long long rowoff = base_nh + (long long)min(qi, p.L - 1) * p.S;
+      const bool vec = (p.S % 4 == 0) && ((base_nh + j0) % 4 == 0) && (j0 + BN <= p.S) &&
+                       (reinterpret_cast<uintptr_t>(p.ubias) % (UB == kBiasF32 ? 16 : 4) == 0);
+      if (vec) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const long long j = rowoff + min(j0 + 32 * b + 8 * (r >> 2) + 4 * g + (r & 3), p.S - 1);
-          if (UB == kBiasF32)
-            ubv[b][r] = static_cast<const float*>(p.ubias)[j] * kLog2e;
-          else
-            ubv[b][r] = static_cast<const uint8_t*>(p.ubias)[j] ? 0.f : kNegInf;
-        }
+          for (int rq = 0; rq < 4; ++rq) {
+            const long long j = rowoff + j0 + 32 * b + 8 * rq + 4 * g;
+            if (UB == kBiasF32) {
+              const f32x4 x = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.ubias) + j);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) ubv[b][4 * rq + e] = x[e] * kLog2e;
+            } else {
+              const uint32_t x = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(p.ubias) + j);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) ubv[b][4 * rq + e] = ((x >> (8 * e)) & 0xffu) ? 0.f : kNegInf;
+            }
+          }
+      } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const long long j = rowoff + min(j0 + 32 * b + 8 * (r >> 2) + 4 * g + (r & 3), p.S - 1);
+            if (UB == kBiasF32)
+              ubv[b][r] = static_cast<const float*>(p.ubias)[j] * kLog2e;
+            else
+              ubv[b][r] = static_cast<const uint8_t*>(p.ubias)[j] ? 0.f : kNegInf;
+          }
+      }
     }
 
     // S^T = K * Q^T for NB blocks of 32 keys; the NB accumulation chains are

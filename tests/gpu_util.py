@@ -77,7 +77,8 @@ def compare(w: Workload, inp: gen.Inputs, o_gpu: torch.Tensor, lse_gpu: torch.Te
     assert np.array_equal(np.isneginf(lg), np.isneginf(lse_ref)), "LSE -inf pattern differs"
     assert not np.any(np.isnan(lg)), "NaN LSE"
     eo = np.abs(og - o_ref)
-    el = np.where(both_ninf, 0.0, np.abs(lg - lse_ref))
+    with np.errstate(invalid="ignore"):
+        el = np.where(both_ninf, 0.0, np.abs(lg - lse_ref))
     worst = np.unravel_index(int(np.argmax(eo)), eo.shape) if eo.size else None
     return float(eo.max()) if eo.size else 0.0, float(el.max()) if el.size else 0.0, worst
 

@@ -11,7 +11,7 @@ import torch
 
 import softmax_attention_attn_amd as attn
 from gpu_util import check, sample_rows, say, to_device
-from workloads import gen
+from workloads import configs, gen
 from workloads.configs import Workload
 
 pytestmark = pytest.mark.gpu
@@ -95,3 +95,14 @@ def test_zero_bias_and_all_true_mask_match_plain_forward():
     for o, l in ((o1, l1), (o2, l2)):
         assert (o.float() - o0.float()).abs().max().item() <= 2e-2
         assert (l - l0).abs().max().item() <= 1e-3
+
+
+def test_full_b1_bias_and_key_padding_sampled_rows():
+    w = configs.B1
+    say(f"[full] {w.name}: generating inputs")
+    inp = gen.generate(w)
+    q, k, v, sink = to_device(inp)
+    o, lse = attn.fwd(q, k, v, scale=w.scale, causal=w.causal, bias=torch.from_numpy(inp.bias).to("cuda:0"),
+                      key_len=torch.from_numpy(inp.key_len).to("cuda:0"))
+    torch.cuda.synchronize()
+    check(w, inp, o, lse, rows=sample_rows(w), bias=inp.bias, key_len=inp.key_len)

@@ -38,6 +38,9 @@ class Workload:
     decode: bool          # uses the split-K decode entry point (L == 1)
     seed: int
     k_dist: str = "normal"  # "normal" or "dir_lognormal"
+    bias: str = "none"      # general bias: "none", "f32" (N(0,1) addend) or "bool" (mask)
+    bias_dims: str = "11"   # bias batch / head dims: "N" or "1", then "H" or "1"
+    key_len: tuple = ()     # per-sequence valid real keys (empty: no padding)
 
     @property
     def S(self) -> int:
@@ -64,28 +67,42 @@ C5 = Workload("decode_splitk_sink_bf16_8x32to8x131072x128", "bf16", 8, 32, 8, 1,
               "dot", 1.0 / math.sqrt(128.0), 0.0, True, 0, 0, True, True, 5)
 
 ALL = (C1, C2, C3, C4, C5)
-BY_NAME = {w.name: w for w in ALL}
+
+# The headline prefill shape with the SDPA page's general bias: a float32 bias
+# per sequence (broadcast over heads) added to the logits, and key padding
+# (right-padded sequences of 2048, 1792, 1536 and 1024 valid keys).
+B1 = Workload("dot_causal_bias_keypad_bf16_4x16x2048x128", "bf16", 4, 16, 16, 2048, 2048, 128,
+              "dot", 1.0 / math.sqrt(128.0), 0.0, True, 0, 0, False, False, 7,
+              bias="f32", bias_dims="N1", key_len=(2048, 1792, 1536, 1024))
+EXTRA = (B1,)
+BY_NAME = {w.name: w for w in ALL + EXTRA}
 
 
-def visible_pairs_per_head(w: Workload) -> int:
+def visible_pairs_per_head(w: Workload, key_len: int = -1) -> int:
     """Count (query, key) pairs that the visibility rule lets through, per head.
 
     Register keys are always visible; real key r is visible to query i (aligned
     bottom-right, i' = i + S_real - L) iff (not causal or r <= i') and
-    (window <= 0 or i' - r < window).  Closed-form per query row.
+    (window <= 0 or i' - r < window), and r < key_len when a sequence's key
+    length is given.  Closed-form per query row.
     """
     total = 0
     off = w.S_real - w.L
+    kl = w.S_real if key_len < 0 else min(w.S_real, key_len)
     for i in range(w.L):
         ip = i + off
-        hi = min(w.S_real - 1, ip) if w.causal else w.S_real - 1
+        hi = min(kl - 1, ip) if w.causal else kl - 1
         lo = max(0, ip - w.window + 1) if w.window > 0 else 0
         total += max(0, hi - lo + 1) + w.n_reg
     return total
 
 
 def algorithmic_flops(w: Workload) -> float:
-    """4*E flops per visible pair (2E for q.k, 2E for p*v), times N*Hq heads."""
+    """4*E flops per visible pair (2E for q.k, 2E for p*v), times the heads; with key
+    lengths, each sequence counts its own pairs (padding and a user bias's -inf
+    entries are not credited; the f32 bias here has none)."""
+    if w.key_len:
+        return 4.0 * w.E * w.Hq * sum(visible_pairs_per_head(w, kl) for kl in w.key_len)
     return 4.0 * w.E * visible_pairs_per_head(w) * w.N * w.Hq
 
 
@@ -97,7 +114,11 @@ def algorithmic_bytes(w: Workload) -> float:
     o = q
     lse = w.N * w.Hq * w.L * 4
     sink = w.Hq * 4 if w.sink else 0
-    return float(q + kv + o + lse + sink)
+    bias = 0
+    if w.bias != "none":
+        bias = ((w.N if w.bias_dims[0] == "N" else 1) * (w.Hq if w.bias_dims[1] == "H" else 1) * w.L * w.S *
+                (4 if w.bias == "f32" else 1))
+    return float(q + kv + o + lse + sink + bias + 4 * len(w.key_len))
 
 
 @dataclass(frozen=True)

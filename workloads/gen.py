@@ -102,6 +102,8 @@ class Inputs:
     k: np.ndarray                # (N,Hkv,S,E)
     v: np.ndarray                # (N,Hkv,S,E)
     sink: Optional[np.ndarray]   # (Hq,) float32 or None
+    bias: Optional[np.ndarray] = None     # general bias (N|1, Hq|1, L, S): float32 or bool, or None
+    key_len: Optional[np.ndarray] = None  # (N,) int32 valid real keys, or None
 
 
 def _default_threads() -> int:
@@ -137,7 +139,12 @@ def generate(w: Workload, threads: Optional[int] = None) -> Inputs:
     else:
         with ThreadPoolExecutor(nthr) as ex:
             list(ex.map(run, jobs))
-    return Inputs(w, q, k, v, sink_logits(w))
+    bias = None
+    if w.bias != "none":
+        shape = (w.N if w.bias_dims[0] == "N" else 1, w.Hq if w.bias_dims[1] == "H" else 1, w.L, w.S)
+        bias = bias_f32(w.seed, shape) if w.bias == "f32" else mask_bool(w.seed, shape, 0.9)
+    key_len = np.asarray(w.key_len, dtype=np.int32) if w.key_len else None
+    return Inputs(w, q, k, v, sink_logits(w), bias, key_len)
 
 
 # ----------------------------------------------------------------------------- general bias inputs
