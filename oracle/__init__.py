@@ -56,6 +56,12 @@ def _bind(path: str):
         ctypes.c_int, ctypes.c_int, ctypes.c_int, dp,
         ctypes.c_int, vp, ctypes.c_longlong, ctypes.c_longlong, ctypes.POINTER(ctypes.c_int),
         ctypes.c_longlong, llp, dp, dp, dp, ctypes.c_int]
+    lib.oracle_attn_bwd.restype = ctypes.c_int
+    lib.oracle_attn_bwd.argtypes = [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        vp, vp, vp, vp, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, dp,
+        ctypes.c_longlong, llp, dp, ctypes.c_longlong, llp, dp, dp, dp, dp, dp, ctypes.c_int]
     lib.oracle_visible.restype = ctypes.c_int
     lib.oracle_visible.argtypes = [ctypes.c_int] * 7
     lib.oracle_num_threads.restype = ctypes.c_int
@@ -214,3 +220,58 @@ def stream_decode(q: np.ndarray, k_hist: np.ndarray, v_hist: np.ndarray, *, n_si
     v = np.ascontiguousarray(v_hist[:, :, kept])
     return attn(q, k, v, mode=mode, scale=scale, gamma=gamma, causal=False, window=0, n_reg=0, sink=sink,
                 threads=threads, lib=lib)
+
+
+# ----------------------------------------------------------------------------- backward
+
+
+def attn_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, *, mode: str = "dot",
+             scale: Optional[float] = None, gamma: float = 0.0, causal: bool = False, window: int = 0,
+             n_reg: int = 0, sink: Optional[np.ndarray] = None, qrows: Optional[Sequence[int]] = None,
+             krows: Optional[Sequence[int]] = None, threads: int = 0, lib=None):
+    """Gradients of O (for the upstream gradient dout, shaped like q) in fp64.
+
+    Returns a dict: dq (N,Hq,L,E) or (len(qrows),E); dk, dv (N,Hkv,S,E) or
+    (len(krows),E); dsink (Hq,) (zeros without a sink); lse, delta (N,Hq,L):
+    the forward LSE and D_i = dO_i . O_i.  qrows: flat (n*Hq+h)*L+i;
+    krows: flat (n*Hkv+kh)*S+j; None = all."""
+    q, k, v, dout = (np.ascontiguousarray(a) for a in (q, k, v, dout))
+    dt = _dtype_code(q)
+    if any(_dtype_code(a) != dt for a in (k, v, dout)):
+        raise TypeError("oracle: q, k, v, dout must share one element type")
+    N, Hq, L, E = q.shape
+    _, Hkv, S, _ = k.shape
+    if dout.shape != q.shape or v.shape != k.shape:
+        raise ValueError("oracle: shape mismatch")
+    if scale is None:
+        scale = 1.0 / np.sqrt(E)
+    md = {"dot": DOT, "rbf": RBF}[mode]
+    dp = ctypes.POINTER(ctypes.c_double)
+    llp = ctypes.POINTER(ctypes.c_longlong)
+    sk = None if sink is None else np.ascontiguousarray(np.asarray(sink, dtype=np.float64).reshape(-1))
+    qr = None if qrows is None else np.ascontiguousarray(np.asarray(qrows, dtype=np.int64).reshape(-1))
+    kr = None if krows is None else np.ascontiguousarray(np.asarray(krows, dtype=np.int64).reshape(-1))
+    nq = N * Hq * L if qr is None else qr.shape[0]
+    nk = N * Hkv * S if kr is None else kr.shape[0]
+    dq = np.zeros((nq, E))
+    dk = np.zeros((nk, E))
+    dv = np.zeros((nk, E))
+    dsink = np.zeros(Hq)
+    lse = np.zeros(N * Hq * L)
+    delta = np.zeros(N * Hq * L)
+    rc = (lib or _load()).oracle_attn_bwd(
+        dt, N, Hq, Hkv, L, S, E, q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+        md, float(scale), float(gamma), int(bool(causal)), int(window), int(n_reg),
+        sk.ctypes.data_as(dp) if sk is not None else None,
+        nq, qr.ctypes.data_as(llp) if qr is not None else None, dq.ctypes.data_as(dp),
+        nk, kr.ctypes.data_as(llp) if kr is not None else None, dk.ctypes.data_as(dp), dv.ctypes.data_as(dp),
+        dsink.ctypes.data_as(dp), lse.ctypes.data_as(dp), delta.ctypes.data_as(dp), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_bwd failed with code {rc}")
+    if qr is None:
+        dq = dq.reshape(N, Hq, L, E)
+    if kr is None:
+        dk = dk.reshape(N, Hkv, S, E)
+        dv = dv.reshape(N, Hkv, S, E)
+    return {"dq": dq, "dk": dk, "dv": dv, "dsink": dsink, "lse": lse.reshape(N, Hq, L),
+            "delta": delta.reshape(N, Hq, L)}

@@ -164,3 +164,188 @@ int oracle_attn_rows_ex(int dtype, int N, int Hq, int Hkv, int L, int S, int E,
   }
   return failed ? -4 : 0;
 }
+
+/* ------------------------------------------------------------------------ backward */
+
+/* d z_ij / d q_i (into g[E], scaled by w): dot: scale*k_j; rbf: -2*gamma*(q_i - k_j) */
+static void dlogit_dq(int dtype, const void* q, size_t qoff, const void* k, size_t koff, int E, int mode,
+                      double scale, double gamma, double w, double* g) {
+  for (int e = 0; e < E; ++e) {
+    const double ke = load_elem(dtype, k, koff + e);
+    if (mode == ORACLE_DOT)
+      g[e] += w * scale * ke;
+    else
+      g[e] += w * (-2.0 * gamma) * (load_elem(dtype, q, qoff + e) - ke);
+  }
+}
+
+/* d z_ij / d k_j (into g[E], scaled by w): dot: scale*q_i; rbf: 2*gamma*(q_i - k_j) */
+static void dlogit_dk(int dtype, const void* q, size_t qoff, const void* k, size_t koff, int E, int mode,
+                      double scale, double gamma, double w, double* g) {
+  for (int e = 0; e < E; ++e) {
+    const double qe = load_elem(dtype, q, qoff + e);
+    if (mode == ORACLE_DOT)
+      g[e] += w * scale * qe;
+    else
+      g[e] += w * (2.0 * gamma) * (qe - load_elem(dtype, k, koff + e));
+  }
+}
+
+int oracle_attn_bwd(int dtype, int N, int Hq, int Hkv, int L, int S, int E,
+                    const void* q, const void* k, const void* v, const void* dout,
+                    int mode, double scale, double gamma,
+                    int causal, int window, int n_reg, const double* sink,
+                    long long nq, const long long* qrows, double* dq,
+                    long long nk, const long long* krows, double* dk, double* dv,
+                    double* dsink, double* lse_out, double* delta_out, int threads) {
+  if (dtype < ORACLE_BF16 || dtype > ORACLE_F64) return -1;
+  if (mode != ORACLE_DOT && mode != ORACLE_RBF) return -1;
+  if (N <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || S < 0 || E <= 0) return -2;
+  if (Hq % Hkv != 0) return -2;
+  if (n_reg < 0 || n_reg > S) return -2;
+  if (!q || !k || !v || !dout) return -3;
+  const long long total_q = (long long)N * Hq * L;
+  const long long total_k = (long long)N * Hkv * S;
+  if (!qrows && dq && nq != total_q) return -2;
+  if (!krows && (dk || dv) && nk != total_k) return -2;
+  for (long long r = 0; qrows && r < nq; ++r)
+    if (qrows[r] < 0 || qrows[r] >= total_q) return -2;
+  for (long long r = 0; krows && r < nk; ++r)
+    if (krows[r] < 0 || krows[r] >= total_k) return -2;
+  const int G = Hq / Hkv;
+  const int nt = oracle_num_threads(threads);
+
+  /* Phase 1, every row: LSE_i of the forward (definition form, sink included)
+     and D_i = dO_i . O_i with O_i the exact forward output. */
+  double* LSE = (double*)malloc(sizeof(double) * (size_t)total_q);
+  double* DEL = (double*)malloc(sizeof(double) * (size_t)total_q);
+  if (!LSE || !DEL) {
+    free(LSE);
+    free(DEL);
+    return -4;
+  }
+  int failed = 0;
+#pragma omp parallel num_threads(nt)
+  {
+    double* z = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+    double* o = (double*)malloc(sizeof(double) * (size_t)E);
+    if (!z || !o) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (long long flat = 0; flat < total_q; ++flat) {
+      if (!z || !o) continue;
+      const int i = (int)(flat % L);
+      const long long nh = flat / L;
+      const int h = (int)(nh % Hq), n = (int)(nh / Hq);
+      const size_t kvrow0 = ((size_t)n * Hkv + h / G) * (size_t)S;
+      double M = -INFINITY;
+      for (int j = 0; j < S; ++j) {
+        z[j] = oracle_visible(L, S, causal, window, n_reg, i, j)
+                   ? logit(dtype, q, (size_t)flat * E, k, (kvrow0 + j) * E, E, mode, scale, gamma)
+                   : -INFINITY;
+        if (z[j] > M) M = z[j];
+      }
+      if (sink && sink[h] > M) M = sink[h];
+      if (M == -INFINITY) { /* empty row: O = 0, no gradient flows */
+        LSE[flat] = -INFINITY;
+        DEL[flat] = 0.0;
+        continue;
+      }
+      double Dn = 0.0;
+      for (int j = 0; j < S; ++j) Dn += exp(z[j] - M);
+      if (sink) Dn += exp(sink[h] - M);
+      for (int e = 0; e < E; ++e) o[e] = 0.0;
+      for (int j = 0; j < S; ++j) {
+        const double p = exp(z[j] - M) / Dn;
+        if (p == 0.0) continue;
+        for (int e = 0; e < E; ++e) o[e] += p * load_elem(dtype, v, (kvrow0 + j) * E + e);
+      }
+      double d = 0.0;
+      for (int e = 0; e < E; ++e) d += load_elem(dtype, dout, (size_t)flat * E + e) * o[e];
+      LSE[flat] = M + log(Dn);
+      DEL[flat] = d;
+    }
+    free(z);
+    free(o);
+  }
+  if (failed) {
+    free(LSE);
+    free(DEL);
+    return -4;
+  }
+
+  /* dsink_h = -sum over (n, i) of p_sink * D_i, p_sink = exp(s_h - LSE_i) */
+  if (dsink) {
+    for (int h = 0; h < Hq; ++h) dsink[h] = 0.0;
+    if (sink)
+      for (long long flat = 0; flat < total_q; ++flat) {
+        const int h = (int)((flat / L) % Hq);
+        if (LSE[flat] != -INFINITY) dsink[h] -= exp(sink[h] - LSE[flat]) * DEL[flat];
+      }
+  }
+
+  /* Phase 2a, requested query rows: dq_i = sum_j dZ_ij dz_ij/dq_i,
+     dZ_ij = p_ij (dP_ij - D_i), dP_ij = dO_i . v_j */
+  if (dq) {
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nt)
+    for (long long r = 0; r < nq; ++r) {
+      const long long flat = qrows ? qrows[r] : r;
+      const int i = (int)(flat % L);
+      const long long nh = flat / L;
+      const int h = (int)(nh % Hq), n = (int)(nh / Hq);
+      const size_t kvrow0 = ((size_t)n * Hkv + h / G) * (size_t)S;
+      double* g = dq + (size_t)r * E;
+      for (int e = 0; e < E; ++e) g[e] = 0.0;
+      if (LSE[flat] == -INFINITY) continue;
+      for (int j = 0; j < S; ++j) {
+        if (!oracle_visible(L, S, causal, window, n_reg, i, j)) continue;
+        const size_t koff = (kvrow0 + j) * E;
+        const double p = exp(logit(dtype, q, (size_t)flat * E, k, koff, E, mode, scale, gamma) - LSE[flat]);
+        double dp = 0.0;
+        for (int e = 0; e < E; ++e) dp += load_elem(dtype, dout, (size_t)flat * E + e) * load_elem(dtype, v, koff + e);
+        dlogit_dq(dtype, q, (size_t)flat * E, k, koff, E, mode, scale, gamma, p * (dp - DEL[flat]), g);
+      }
+    }
+  }
+
+  /* Phase 2b, requested key rows (n, kv head, j): sums over the G query heads
+     of the group and every query row that sees key j */
+  if (dk || dv) {
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nt)
+    for (long long r = 0; r < nk; ++r) {
+      const long long kflat = krows ? krows[r] : r;
+      const int j = (int)(kflat % S);
+      const long long nkh = kflat / S;
+      const int kh = (int)(nkh % Hkv), n = (int)(nkh / Hkv);
+      const size_t koff = (size_t)kflat * E;
+      double* gk = dk ? dk + (size_t)r * E : NULL;
+      double* gv = dv ? dv + (size_t)r * E : NULL;
+      for (int e = 0; e < E; ++e) {
+        if (gk) gk[e] = 0.0;
+        if (gv) gv[e] = 0.0;
+      }
+      for (int h = kh * G; h < (kh + 1) * G; ++h)
+        for (int i = 0; i < L; ++i) {
+          if (!oracle_visible(L, S, causal, window, n_reg, i, j)) continue;
+          const long long flat = ((long long)n * Hq + h) * L + i;
+          if (LSE[flat] == -INFINITY) continue;
+          const size_t qoff = (size_t)flat * E;
+          const double p = exp(logit(dtype, q, qoff, k, koff, E, mode, scale, gamma) - LSE[flat]);
+          if (gv)
+            for (int e = 0; e < E; ++e) gv[e] += p * load_elem(dtype, dout, qoff + e);
+          if (gk) {
+            double dp = 0.0;
+            for (int e = 0; e < E; ++e) dp += load_elem(dtype, dout, qoff + e) * load_elem(dtype, v, koff + e);
+            dlogit_dk(dtype, q, qoff, k, koff, E, mode, scale, gamma, p * (dp - DEL[flat]), gk);
+          }
+        }
+    }
+  }
+  if (lse_out) memcpy(lse_out, LSE, sizeof(double) * (size_t)total_q);
+  if (delta_out) memcpy(delta_out, DEL, sizeof(double) * (size_t)total_q);
+  free(LSE);
+  free(DEL);
+  return 0;
+}

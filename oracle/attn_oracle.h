@@ -94,6 +94,33 @@ int oracle_attn_rows_ex(int dtype, int N, int Hq, int Hkv, int L, int S, int E,
                         long long nrows, const long long* rows,
                         double* o, double* lse, double* p, int threads);
 
+/*
+ * Gradients of the forward above (no user bias) for an upstream gradient dO
+ * of O (LSE is an auxiliary output: no gradient flows into it).  With
+ * P_ij the attention weights, D_i = dO_i . O_i (the exact forward O),
+ * dP_ij = dO_i . v_j and dZ_ij = P_ij (dP_ij - D_i) (the softmax Jacobian;
+ * "어텐션 메커니즘" section 2 defines the row softmax it differentiates):
+ *   dv_j = sum_i P_ij dO_i
+ *   dq_i = sum_j dZ_ij dz_ij/dq_i,  dk_j = sum_i dZ_ij dz_ij/dk_j
+ *          dot: dz/dq = scale k_j, dz/dk = scale q_i
+ *          rbf: dz/dq = -2 gamma (q_i - k_j), dz/dk = 2 gamma (q_i - k_j)
+ *               (the definition form -gamma |q - k|^2 of the RBF digest, paragraph 2)
+ *   dsink_h = -sum_i p_sink_i D_i,  p_sink_i = exp(s_h - LSE_i)
+ *            (the sink only enters the denominator: "Attention Sink" section 4.2)
+ * Sums for dk / dv run over the G query heads sharing the key/value head.
+ * Rows of dq: qrows (flat (n*Hq+h)*L+i) or all (qrows NULL, nq = N*Hq*L);
+ * rows of dk and dv: krows (flat (n*Hkv+kh)*S+j) or all.  Any of dq, dk, dv,
+ * dsink, lse_out, delta_out may be NULL.  Every row's LSE and D are computed
+ * first (the gradients of any row need them).  Returns 0 or a negative value.
+ */
+int oracle_attn_bwd(int dtype, int N, int Hq, int Hkv, int L, int S, int E,
+                    const void* q, const void* k, const void* v, const void* dout,
+                    int mode, double scale, double gamma,
+                    int causal, int window, int n_reg, const double* sink,
+                    long long nq, const long long* qrows, double* dq,
+                    long long nk, const long long* krows, double* dk, double* dv,
+                    double* dsink, double* lse_out, double* delta_out, int threads);
+
 /* Number of OpenMP threads oracle_attn_rows uses for a given `threads`. */
 int oracle_num_threads(int threads);
 

@@ -471,4 +471,92 @@ def pin_key_padding_equals_slicing(lib):
     assert np.max(np.abs(o[:1] - o1)) < 1e-12 and np.max(np.abs(lse[:1] - l1)) < 1e-12
 
 
+# ----------------------------------------------------------------------------- backward
+
+
+def _visible_mask(L, S, causal, window, n_reg):
+    m = np.zeros((L, S), bool)
+    for i in range(L):
+        for j in range(S):
+            if j < n_reg:
+                m[i, j] = True
+                continue
+            r, ip = j - n_reg, i + (S - n_reg - L)
+            m[i, j] = (not causal or r <= ip) and (window <= 0 or ip - r < window)
+    return m
+
+
+def pin_bwd_dot_matches_sdpa_autograd(lib):
+    # the gradient formulas against automatic differentiation of the library routine
+    q, k, v = _qkv(71, 2, 4, 2, 6, 9, 8)
+    do = _rng(72).standard_normal(q.shape)
+    g = oracle.attn_bwd(q, k, v, do, scale=0.3, causal=True, lib=lib)
+    qt, kt, vt = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    m = torch.from_numpy(_visible_mask(6, 9, True, 0, 0))
+    o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=0.3, enable_gqa=True)
+    o.backward(torch.from_numpy(do))
+    for name, t in (("dq", qt), ("dk", kt), ("dv", vt)):
+        assert np.max(np.abs(g[name] - t.grad.numpy())) < 1e-12, name
+
+
+def pin_bwd_rbf_matches_cdist_autograd(lib):
+    q, k, v = _qkv(73, 1, 2, 2, 5, 8, 6)
+    do = _rng(74).standard_normal(q.shape)
+    g = oracle.attn_bwd(q, k, v, do, mode="rbf", gamma=0.2, causal=True, window=3, n_reg=2, lib=lib)
+    qt, kt, vt = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    z = -0.2 * torch.cdist(qt, kt) ** 2
+    z = z.masked_fill(~torch.from_numpy(_visible_mask(5, 8, True, 3, 2)), float("-inf"))
+    o = torch.softmax(z, -1) @ vt
+    o.backward(torch.from_numpy(do))
+    for name, t in (("dq", qt), ("dk", kt), ("dv", vt)):
+        assert np.max(np.abs(g[name] - t.grad.numpy())) < 1e-10, name
+
+
+def pin_bwd_finite_differences_with_sink(lib):
+    # central differences of L = sum(dO * O) in fp64, every input and the sink
+    q, k, v = _qkv(75, 1, 4, 2, 4, 6, 3)
+    do = _rng(76).standard_normal(q.shape)
+    sink = _rng(77).standard_normal(4)
+    kw = dict(mode="rbf", gamma=0.3, causal=True, window=3, n_reg=1)
+    g = oracle.attn_bwd(q, k, v, do, sink=sink, lib=lib, **kw)
+
+    def loss(q_, k_, v_, s_):
+        o, _ = oracle.attn(q_, k_, v_, sink=s_, lib=lib, **kw)
+        return float(np.sum(o * do))
+    h = 1e-6
+    for name, arr in (("dq", q), ("dk", k), ("dv", v)):
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            a1, a2 = arr.copy(), arr.copy()
+            a1[idx] += h
+            a2[idx] -= h
+            args1 = [q, k, v, sink]
+            args2 = [q, k, v, sink]
+            pos = {"dq": 0, "dk": 1, "dv": 2}[name]
+            args1[pos], args2[pos] = a1, a2
+            fd = (loss(*args1) - loss(*args2)) / (2 * h)
+            assert abs(fd - g[name][idx]) < 1e-6, (name, idx, fd, g[name][idx])
+    for hh in range(4):
+        s1, s2 = sink.copy(), sink.copy()
+        s1[hh] += h
+        s2[hh] -= h
+        fd = (loss(q, k, v, s1) - loss(q, k, v, s2)) / (2 * h)
+        assert abs(fd - g["dsink"][hh]) < 1e-6
+
+
+def pin_bwd_row_subsets_and_delta(lib):
+    q, k, v = _qkv(78, 2, 2, 1, 5, 7, 4)
+    do = _rng(79).standard_normal(q.shape)
+    full = oracle.attn_bwd(q, k, v, do, causal=True, n_reg=1, lib=lib)
+    qr, kr = [3, 7, 19], [0, 5, 13]
+    part = oracle.attn_bwd(q, k, v, do, causal=True, n_reg=1, qrows=qr, krows=kr, lib=lib)
+    assert np.array_equal(part["dq"], full["dq"].reshape(-1, 4)[qr])
+    assert np.array_equal(part["dk"], full["dk"].reshape(-1, 4)[kr])
+    assert np.array_equal(part["dv"], full["dv"].reshape(-1, 4)[kr])
+    o, lse = oracle.attn(q, k, v, causal=True, n_reg=1, lib=lib)
+    assert np.max(np.abs(full["delta"] - np.sum(o * do, -1))) < 1e-12
+    assert np.max(np.abs(full["lse"] - lse)) < 1e-12
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

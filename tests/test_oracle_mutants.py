@@ -33,9 +33,16 @@ MUTANTS = {
     "key_len_ignored": ("const int padded = key_len && j >= n_reg && (j - n_reg) >= key_len[n];",
                         "const int padded = 0;"),
     "bias_head_stride_dropped": ("(long long)h * sh +", ""),
+    "bwd_delta_dropped": ("dlogit_dq(dtype, q, (size_t)flat * E, k, koff, E, mode, scale, gamma, p * (dp - DEL[flat]), g);",
+                          "dlogit_dq(dtype, q, (size_t)flat * E, k, koff, E, mode, scale, gamma, p * dp, g);"),
+    "bwd_rbf_dk_sign": ("g[e] += w * (2.0 * gamma) * (qe - load_elem(dtype, k, koff + e));",
+                        "g[e] += w * (2.0 * gamma) * (load_elem(dtype, k, koff + e) - qe);"),
+    "bwd_dsink_sign": ("dsink[h] -= exp(sink[h] - LSE[flat]) * DEL[flat];", "dsink[h] += exp(sink[h] - LSE[flat]) * DEL[flat];"),
+    "bwd_gqa_one_head": ("for (int h = kh * G; h < (kh + 1) * G; ++h)", "for (int h = kh * G; h < kh * G + 1; ++h)"),
+    "bwd_dv_unweighted": ("gv[e] += p * load_elem(dtype, dout, qoff + e);", "gv[e] += load_elem(dtype, dout, qoff + e);"),
     "head_dim_truncated": ("for (int e = 0; e < E; ++e) acc += load_elem", "for (int e = 0; e < E - 1; ++e) acc += load_elem"),
     "lse_without_max": ("lse[r] = M + log(D);", "lse[r] = log(D);"),
-    "empty_row_nan": ("if (M == -INFINITY) {", "if (0) {"),
+    "empty_row_nan": ("if (M == -INFINITY) { /* nothing visible", "if (0) { /* nothing visible"),
     "bf16_shift": ("<< 16;", "<< 15;"),
     "value_row_index": ("const size_t voff = (kvrow0 + j) * E;", "const size_t voff = (kvrow0 + (S - 1 - j)) * E;"),
 }
