@@ -3,7 +3,7 @@
  *
  * One operation, computed by attn_fwd (prefill), attn_fwd_biased (prefill
  * with a general bias), attn_decode (split-K decode) and attn_stream_decode
- * (decode over a rolling cache):
+ * (decode over a rolling cache), with its gradients from attn_bwd:
  *
  *   O = softmax(Z) V,  Z_ij = logit(q_i, k_j) + B_ij,  B_ij in {0, -inf}
  *
@@ -119,6 +119,40 @@ int attn_fwd_biased(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E,
                     attn_bias_kind bias_kind, const void* bias, long long bias_stride_n, long long bias_stride_h,
                     const int* key_len,
                     void* o, float* lse, void* stream);
+
+/*
+ * attn_bwd -- gradients of attn_fwd's O for an upstream gradient dout (LSE is
+ * an auxiliary output; no gradient flows into it).  With P recomputed from the
+ * saved LSE (the flash-attention recomputation: the L x S matrices never exist
+ * in memory, "어텐션 메커니즘" section 6), D_i = dout_i . o_i and
+ * dS_ij = P_ij (dout_i . v_j - D_i):
+ *   dv_j = sum_i P_ij dout_i;  dq_i = sum_j dS_ij dz_ij/dq_i;  dk_j = sum_i dS_ij dz_ij/dk_j
+ *   (DOT: dz/dq = scale k_j, dz/dk = scale q_i; RBF: dz/dq = 2 gamma (k_j - q_i),
+ *   dz/dk = 2 gamma (q_i - k_j), the derivative of -gamma |q - k|^2 that also
+ *   covers the |k|^2 term formed on chip);
+ *   dsink_h = -sum over rows of exp(s_h - LSE_i) D_i  ("Attention Sink" section 4.2:
+ *   the sink only enters the denominator).
+ * dk and dv of a key/value head sum over the query heads of its group.
+ *   q, k, v, sink, sizes, mode, scale, gamma, causal, window, n_reg: exactly as
+ *             passed to attn_fwd
+ *   o, lse    attn_fwd's outputs for those inputs
+ *   dout      (N,Hq,L,E) upstream gradient, element type dt
+ *   dq        (N,Hq,L,E); dk, dv (N,Hkv,S,E); element type dt; written whole
+ *   dsink     Hq float32 values, or NULL; 0 when sink is NULL
+ *   workspace device scratch of attn_bwd_workspace_bytes(N, Hq, L) bytes,
+ *             16-byte aligned, caller-owned; contents on entry do not matter
+ * bf16 only (ATTN_ERR_UNSUPPORTED for f32).  Results are deterministic (no
+ * atomics).  The general bias of attn_fwd_biased has no backward here.
+ */
+int attn_bwd(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E,
+             const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+             attn_mode mode, float scale, float gamma,
+             int causal, int window, int n_reg, const float* sink,
+             void* dq, void* dk, void* dv, float* dsink,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_bwd needs (0 for invalid sizes). */
+size_t attn_bwd_workspace_bytes(int N, int Hq, int L);
 
 /*
  * attn_decode -- one query token per sequence (L must be 1) against a long

@@ -33,7 +33,7 @@ STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR
 BF16, F32 = 0, 1
 MODES = {"dot": 0, "rbf": 1}
 
-EXPORTS = ("attn_fwd", "attn_fwd_biased", "attn_decode", "attn_decode_num_splits", "attn_decode_workspace_bytes",
+EXPORTS = ("attn_fwd", "attn_fwd_biased", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_num_splits", "attn_decode_workspace_bytes",
            "attn_stream_append", "attn_stream_decode", "attn_stream_decode_workspace_bytes",
            "attn_status_string", "attn_last_error")
 
@@ -60,6 +60,10 @@ def load() -> ctypes.CDLL:
         LLb = ctypes.c_longlong
         lib.attn_fwd_biased.restype = I
         lib.attn_fwd_biased.argtypes = [I, I, I, I, I, I, I, P, P, P, I, F, F, I, I, I, P, I, P, LLb, LLb, P, P, P, P]
+        lib.attn_bwd.restype = I
+        lib.attn_bwd.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, I, F, F, I, I, I, P, P, P, P, P, P, Z, P]
+        lib.attn_bwd_workspace_bytes.restype = Z
+        lib.attn_bwd_workspace_bytes.argtypes = [I, I, I]
         lib.attn_decode.restype = I
         lib.attn_decode.argtypes = [I, I, I, I, I, I, I, P, P, P, I, F, F, I, I, I, P, P, P, I, P, Z, P]
         lib.attn_decode_num_splits.restype = I
@@ -283,3 +287,31 @@ def stream_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                    workspace.numel() * workspace.element_size(), _stream(q.device, stream))
     _check(rc)
     return out, lse
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+        dout: torch.Tensor, *, scale: Optional[float] = None, mode: str = "dot", gamma: Optional[float] = None,
+        causal: bool = False, window: int = 0, n_reg: int = 0, sink: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None, stream=None):
+    """Gradients of fwd's o (for the upstream gradient dout) through attn_bwd.
+    Returns (dq, dk, dv, dsink); dsink is None without a sink."""
+    N, Hq, Hkv, L, S, E, scale, gamma = _common(q, k, v, sink, scale, mode, gamma)
+    for name, t in (("o", o), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+    if lse.shape != (N, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (N, Hq, L) tensor")
+    lib = load()
+    need = int(lib.attn_bwd_workspace_bytes(N, Hq, L))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dsink = torch.empty(Hq, dtype=torch.float32, device=q.device) if sink is not None else None
+    rc = lib.attn_bwd(_dtype_code(q), N, Hq, Hkv, L, S, E, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                      MODES[mode], scale, gamma, int(bool(causal)), int(window), int(n_reg), _ptr(sink),
+                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsink), _ptr(workspace),
+                      workspace.numel() * workspace.element_size(), _stream(q.device, stream))
+    _check(rc)
+    return dq, dk, dv, dsink

@@ -191,6 +191,47 @@ int attn_fwd_biased(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, 
   return hip_status(e, "attn_fwd_biased launch");
 }
 
+size_t attn_bwd_workspace_bytes(int N, int Hq, int L) {
+  if (N < 0 || Hq <= 0 || L < 0) return 0;
+  return attn_impl::backward_workspace_bytes(N, Hq, L);
+}
+
+int attn_bwd(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, const void* q, const void* k, const void* v,
+             const void* o, const float* lse, const void* dout, attn_mode mode, float scale, float gamma, int causal,
+             int window, int n_reg, const float* sink, void* dq, void* dk, void* dv, float* dsink, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  int rc = check_args(dt, N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o, lse);
+  if (rc != ATTN_OK) return rc;
+  if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "the backward pass is implemented for bf16 only");
+  if ((long long)N * Hq * L == 0 && (long long)N * Hkv * S == 0) return ok();
+  if ((long long)N * Hq * L == 0 || (long long)N * Hkv * S == 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "backward with an empty query or key side (L=%d, S=%d)", L, S);
+  if (!dout || !dq || !dk || !dv) return fail(ATTN_ERR_NULL, "dout, dq, dk and dv must not be NULL");
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return fail(ATTN_ERR_ALIGN, "dout, dq, dk and dv must be 16-byte aligned");
+  if (dsink && !aligned(dsink, 4)) return fail(ATTN_ERR_ALIGN, "dsink must be 4-byte aligned");
+  const size_t need = attn_impl::backward_workspace_bytes(N, Hq, L);
+  if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (workspace_bytes < need) return fail(ATTN_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, need);
+  if (!aligned(workspace, 16)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (((long long)S + 64) * E * 2 > 0x7fffffffLL || ((long long)L + 64) * E * 2 > 0x7fffffffLL)
+    return fail(ATTN_ERR_UNSUPPORTED, "a (batch, head) slice near or above 2 GiB (L=%d, S=%d, E=%d)", L, S, E);
+  if ((long long)((L + 127) / 128) * N * Hq > kMaxGrid || (long long)((S + 127) / 128) * N * Hkv > kMaxGrid ||
+      (long long)N * Hq > 65535LL)
+    return fail(ATTN_ERR_SHAPE, "grid too large");
+  attn_impl::BwdArgs a;
+  a.f = make_args(N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, nullptr, nullptr);
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dsink = dsink;
+  a.workspace = static_cast<float*>(workspace);
+  return hip_status(attn_impl::launch_backward_bf16(a, static_cast<hipStream_t>(stream)), "attn_bwd launch");
+}
+
 int attn_decode_num_splits(int N, int Hq, int Hkv, int S, int E, int causal, int window, int n_reg) {
   if (N < 0 || Hq <= 0 || Hkv <= 0 || S < 0 || Hq % Hkv != 0 || n_reg < 0 || n_reg > S || window < 0)
     return fail(ATTN_ERR_SHAPE, "invalid decode sizes");

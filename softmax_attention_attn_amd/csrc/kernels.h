@@ -50,6 +50,23 @@ hipError_t launch_prefill_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
+// Backward: gradients of O for the upstream gradient dout (bf16, no user bias).
+// workspace: backward_workspace_bytes(N, Hq, L) bytes (D_i, reference max per
+// row, sink partial sums).
+struct BwdArgs {
+  FwdArgs f;          // q, k, v, sizes, mode, flags, sink (o / lse of f unused)
+  const void* o;      // forward output (N,Hq,L,E)
+  const float* lse;   // forward LSE (N,Hq,L)
+  const void* dout;   // upstream gradient (N,Hq,L,E)
+  void* dq;           // (N,Hq,L,E)
+  void* dk;           // (N,Hkv,S,E)
+  void* dv;           // (N,Hkv,S,E)
+  float* dsink;       // Hq values or nullptr
+  float* workspace;
+};
+hipError_t launch_backward_bf16(const BwdArgs& a, hipStream_t stream);
+size_t backward_workspace_bytes(int N, int Hq, int L);
+
 // Rolling key/value cache append: tokens at positions pos .. pos+T-1 from
 // k_new / v_new (N, Hkv, T, E) into k_cache / v_cache (N, Hkv, n_sink+window, E);
 // only the tokens still kept after the append are written (see slot rule in attn.h).

@@ -143,6 +143,37 @@ def test_fwd_biased_accepts_unaligned_mask_and_empty(lib):
     assert fwdb(lib, kind=0, bias=None, L=0) == 0
 
 
+def bwd(lib, dt=0, N=1, Hq=4, Hkv=2, L=8, S=8, E=64, q=A, k=A, v=A, o=A, lse=A, do=A, mode=0, scale=0.125,
+        gamma=0.0, causal=1, window=0, n_reg=0, sink=None, dq=A, dk=A, dv=A, dsink=None, ws=A, wsb=1 << 30):
+    return lib.attn_bwd(dt, N, Hq, Hkv, L, S, E, q, k, v, o, lse, do, mode, scale, gamma, causal, window, n_reg,
+                        sink, dq, dk, dv, dsink, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=1), -4),
+    (dict(E=96), -4),
+    (dict(window=3, causal=0), -4),
+    (dict(Hq=3), -2),
+    (dict(do=None), -1),
+    (dict(dq=None), -1),
+    (dict(dv=None), -1),
+    (dict(o=None), -1),
+    (dict(dk=A + 4), -5),
+    (dict(dsink=A + 2), -5),
+    (dict(ws=None), -6),
+    (dict(wsb=64), -6),
+    (dict(L=0), -4),
+])
+def test_bwd_rejects(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
+def test_bwd_workspace_size(lib):
+    # D and the reference per row, plus one partial sink sum per (batch, head, 256 rows)
+    assert lib.attn_bwd_workspace_bytes(2, 4, 300) == (2 * 2 * 4 * 300 + 2 * 4 * 2) * 4
+    assert bwd(lib, N=0, L=0, S=0) == 0
+
+
 def app(lib, dt=0, N=1, Hkv=2, E=64, n_sink=4, window=16, pos=0, T=3, kn=A, vn=A, kc=A, vc=A):
     return lib.attn_stream_append(dt, N, Hkv, E, n_sink, window, pos, T, kn, vn, kc, vc, None)
 
