@@ -10,7 +10,8 @@ TFLOP/s over the visible (query, key) pairs, 4*E flops each.  The other
 workloads are timed the same way and reported under "extras" (prefill in
 TFLOP/s, decode in HBM GB/s over the K/V bytes read once), as is one step of
 streaming decode over a rolling cache (append the newest token, decode it; HBM
-GB/s over the kept rows read once).
+GB/s over the kept rows read once) and the backward pass on the C2 and C3
+shapes (TFLOP/s at 10*E flops per visible pair).
 
 The CPU baseline leg times the fp64 oracle on a bounded sample of rows of the
 headline workload, on this host's cores, and checks the GPU output on those
@@ -174,6 +175,34 @@ def time_stream(sw, steps: int, warmup: int, rotate: int, torch, attn):
     return start.elapsed_time(end) / steps
 
 
+def time_backward(w, steps: int, warmup: int, torch, attn):
+    """Average ms per backward step (all gradients of O for one upstream gradient); the
+    forward that produces O and LSE runs once before timing."""
+    dev = torch.device("cuda:0")
+    log(f"[bench] {w.name} backward: generating inputs")
+    inp = gen.generate(w)
+    q, k, v, sink = to_device(inp, torch, dev)
+    gbits = gen.bf16_bits_from_f32(gen.bias_f32(w.seed + 100, (w.N, w.Hq, w.L, w.E)))
+    import numpy as np
+    do = torch.from_numpy(gbits.view(np.int16)).view(torch.bfloat16).to(dev)
+    kw = dict(scale=w.scale, mode=w.mode, gamma=w.gamma, causal=w.causal, window=w.window, n_reg=w.n_reg, sink=sink)
+    o, lse = attn.fwd(q, k, v, **kw)
+    ws = torch.empty(max(16, int(attn.load().attn_bwd_workspace_bytes(w.N, w.Hq, w.L))), dtype=torch.uint8,
+                     device=dev)
+    for _ in range(warmup + 1):
+        attn.bwd(q, k, v, o, lse, do, workspace=ws, **kw)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        attn.bwd(q, k, v, o, lse, do, workspace=ws, **kw)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
 def stream_rate(sw, ms: float):
     gbs = configs.stream_bytes(sw) / (ms * 1e-3) / 1e9
     return {"value": gbs, "unit": "GB/s", "bound": "hbm", "peak": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS}
@@ -240,7 +269,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=configs.C2.name,
-                    choices=sorted(configs.BY_NAME) + sorted(configs.STREAM_BY_NAME))
+                    choices=sorted(configs.BY_NAME) + sorted(configs.STREAM_BY_NAME) +
+                    sorted(w.name + "__backward" for w in configs.BACKWARD))
     ap.add_argument("--extras", default="all", choices=["all", "none"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -281,6 +311,19 @@ def main() -> int:
                           "GBps_read_plus_write": 2 * args.copy_bytes / (ms * 1e-3) / 1e9}), flush=True)
         return 0
 
+    if args.workload.endswith("__backward"):
+        bw = configs.BY_NAME[args.workload[:-len("__backward")]]
+        ms = time_backward(bw, args.steps, args.warmup, torch, attn)
+        tf = configs.backward_flops(bw) / (ms * 1e-3) / 1e12
+        print(json.dumps({"metric": "backward TFLOP/s", "value": tf, "unit": "TFLOP/s", "n_gpus": 1,
+                          "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+                          "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                          "data": "synthetic (seeded generator, workloads/gen.py)",
+                          "config": {"workload": args.workload},
+                          "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": tf / PEAK_BF16_TFLOPS, "traffic": None,
+                                       "kernel": "bwd_pre + bwd_dq + bwd_dkdv"}}), flush=True)
+        return 0
     if args.workload in configs.STREAM_BY_NAME:
         # one streaming step (append + decode) on its own, for profiling
         sw = configs.STREAM_BY_NAME[args.workload]
@@ -340,6 +383,15 @@ def main() -> int:
             xr["kernel"] = kernel_of(x)
             xr["rotated_buffer_sets"] = rot
             extras[x.name] = xr
+        for bw in configs.BACKWARD:
+            xms = time_backward(bw, max(5, args.steps // 4), max(2, args.warmup // 4), torch, attn)
+            torch.cuda.empty_cache()
+            tf = configs.backward_flops(bw) / (xms * 1e-3) / 1e12
+            extras[bw.name + "__backward"] = {
+                "value": tf, "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_BF16_TFLOPS,
+                "frac": tf / PEAK_BF16_TFLOPS, "ms": xms, "kernel": "bwd_pre + bwd_dq + bwd_dkdv",
+                "hbm_GBps": configs.backward_bytes(bw) / (xms * 1e-3) / 1e9,
+                "algorithmic_per_step": configs.backward_flops(bw)}
         for sw in configs.STREAM_BY_NAME.values():
             xms = time_stream(sw, max(5, args.steps // 2), max(2, args.warmup // 2), 3, torch, attn)
             torch.cuda.empty_cache()

@@ -65,45 +65,52 @@ struct BwdParams {
 
 // ---------------------------------------------------------------------------- 1. preprocess
 
+// ECH = E/8 consecutive lanes share a row (one 16-byte chunk each), so every
+// load instruction of a wave reads whole contiguous rows; the row sums come
+// from a DPP reduction over those lanes.  PRE rows per workgroup.
 template <int E>
-__global__ __launch_bounds__(PRE) void bwd_pre_kernel(BwdParams p) {
-  __shared__ float red[PRE];
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
+  constexpr int ECH = E / 8;
+  constexpr int RPP = 256 / ECH;  // rows per pass of the workgroup
+  __shared__ float red[256];
   const int nh = blockIdx.y;
   const int h = nh % p.Hq;
   const int tid = threadIdx.x;
-  const int i = blockIdx.x * PRE + tid;
+  const int c = tid % ECH;
   float part = 0.f;
-  if (i < p.L) {
-    const size_t row = (size_t)nh * p.L + i;
-    const uint16_t* orow = p.o + row * E;
-    const uint16_t* grow = p.dout + row * E;
-    float d = 0.f, qn2 = 0.f;
+#pragma unroll 1
+  for (int pass = 0; pass < PRE / RPP; ++pass) {
+    const int i = blockIdx.x * PRE + pass * RPP + tid / ECH;
+    const bool ok = i < p.L;
+    const size_t row = (size_t)nh * p.L + (ok ? i : 0);
+    const u32x4 a = load16_or_zero(p.o + row * E + 8 * c, ok);
+    const u32x4 b = load16_or_zero(p.dout + row * E + 8 * c, ok);
+    float d = 0.f;
 #pragma unroll
-    for (int c = 0; c < E / 8; ++c) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(orow + 8 * c);
-      const u32x4 b = *reinterpret_cast<const u32x4*>(grow + 8 * c);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        d = __builtin_fmaf(bf16_lo(a[w]), bf16_lo(b[w]), d);
-        d = __builtin_fmaf(bf16_hi(a[w]), bf16_hi(b[w]), d);
+    for (int w = 0; w < 4; ++w) {
+      d = __builtin_fmaf(bf16_lo(a[w]), bf16_lo(b[w]), d);
+      d = __builtin_fmaf(bf16_hi(a[w]), bf16_hi(b[w]), d);
+    }
+    d = group_sum<ECH>(d);
+    float qn2 = 0.f;
+    if (p.rbf) qn2 = group_sum<ECH>(sumsq8(load16_or_zero(p.q + row * E + 8 * c, ok)));
+    if (ok && c == 0) {
+      const float lse = p.lse[row];
+      float mr = __builtin_huge_valf();
+      if (lse == kNegInf) {
+        d = 0.f;
+      } else {
+        mr = (lse + (p.rbf ? p.gamma * qn2 : 0.f)) * kLog2e;
+        if (p.sink) part += -exp2f((p.sink[h] - lse) * kLog2e) * d;
       }
-      if (p.rbf) qn2 += sumsq8(*reinterpret_cast<const u32x4*>(p.q + row * E + 8 * c));
+      p.delta[row] = d;
+      p.mref[row] = mr;
     }
-    const float lse = p.lse[row];
-    float mr = __builtin_huge_valf();
-    if (lse == kNegInf) {
-      d = 0.f;
-    } else {
-      mr = (lse + (p.rbf ? p.gamma * qn2 : 0.f)) * kLog2e;
-      if (p.sink) part = -exp2f((p.sink[h] - lse) * kLog2e) * d;
-    }
-    p.delta[row] = d;
-    p.mref[row] = mr;
   }
   red[tid] = part;
   __syncthreads();
 #pragma unroll
-  for (int s = PRE / 2; s > 0; s >>= 1) {
+  for (int s = 128; s > 0; s >>= 1) {
     if (tid < s) red[tid] += red[tid + s];
     __syncthreads();
   }
@@ -710,9 +717,9 @@ hipError_t launch_backward_bf16(const BwdArgs& a, hipStream_t stream) {
 
   const dim3 pgrid((unsigned)p.pre_blocks, (unsigned)(f.N * f.Hq));
   if (f.E == 128)
-    hipLaunchKernelGGL((bwd_pre_kernel<128>), pgrid, dim3(PRE), 0, stream, p);
+    hipLaunchKernelGGL((bwd_pre_kernel<128>), pgrid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((bwd_pre_kernel<64>), pgrid, dim3(PRE), 0, stream, p);
+    hipLaunchKernelGGL((bwd_pre_kernel<64>), pgrid, dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.dsink) {  // without a sink the partials are zero and so is the gradient

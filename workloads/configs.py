@@ -163,3 +163,22 @@ def stream_bytes(w: StreamWorkload) -> float:
     kv = 2 * w.N * w.Hkv * w.rows * w.E * esz
     q = w.N * w.Hq * w.E * esz
     return float(2 * new + kv + 2 * q + w.N * w.Hq * 4 + (w.Hq * 4 if w.sink else 0))
+
+
+# Backward steps measured on the prefill shapes C2 and C3 (gradients of O for a
+# seeded upstream gradient).
+BACKWARD = (C2, C3)
+
+
+def backward_flops(w: Workload) -> float:
+    """10*E flops per visible pair: the logits recomputed once (2E) and the four
+    gradient products dP = dO V^T, dV = P^T dO, dK = dS^T Q, dQ = dS K (2E each)."""
+    return 2.5 * algorithmic_flops(w)
+
+
+def backward_bytes(w: Workload) -> float:
+    """Q, K, V, O, dO read once; dQ, dK, dV written once; LSE read."""
+    esz = 2 if w.dtype == "bf16" else 4
+    qo = w.N * w.Hq * w.L * w.E * esz
+    kv = w.N * w.Hkv * w.S * w.E * esz
+    return float(3 * qo + 2 * kv + qo + 2 * kv + w.N * w.Hq * w.L * 4)
