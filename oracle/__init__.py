@@ -62,6 +62,14 @@ def _bind(path: str):
         vp, vp, vp, vp, ctypes.c_int, ctypes.c_double, ctypes.c_double,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, dp,
         ctypes.c_longlong, llp, dp, ctypes.c_longlong, llp, dp, dp, dp, dp, dp, ctypes.c_int]
+    u8p = ctypes.POINTER(ctypes.c_ubyte)
+    fp = ctypes.POINTER(ctypes.c_float)
+    lib.oracle_socket_hash.restype = ctypes.c_int
+    lib.oracle_socket_hash.argtypes = [ctypes.c_int, ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       vp, vp, fp, u8p, dp]
+    lib.oracle_socket_scores.restype = ctypes.c_int
+    lib.oracle_socket_scores.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                         vp, fp, ctypes.c_longlong, u8p, dp, dp]
     lib.oracle_visible.restype = ctypes.c_int
     lib.oracle_visible.argtypes = [ctypes.c_int] * 7
     lib.oracle_num_threads.restype = ctypes.c_int
@@ -275,3 +283,83 @@ def attn_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, *, m
         dv = dv.reshape(N, Hkv, S, E)
     return {"dq": dq, "dk": dk, "dv": dv, "dsink": dsink, "lse": lse.reshape(N, Hq, L),
             "delta": delta.reshape(N, Hq, L)}
+
+
+# ----------------------------------------------------------------------------- SOCKET sparse decode
+
+
+def socket_hash(k: np.ndarray, v: np.ndarray, proj: np.ndarray, tables: int, bits: int, lib=None):
+    """Bucket codes (N,Hkv,S,tables) uint8 and value norms (N,Hkv,S) fp64 of a key/value cache
+    ("기술 요약: SOCKET" page, method step 1: keys hashed by random projections into L tables,
+    value norms cached).  proj: (tables*bits, E) float32 hyperplanes."""
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    pr = np.ascontiguousarray(proj, dtype=np.float32)
+    *lead, E = k.shape
+    nkeys = int(np.prod(lead))
+    buckets = np.zeros(nkeys * tables, dtype=np.uint8)
+    vnorm = np.zeros(nkeys)
+    rc = (lib or _load()).oracle_socket_hash(
+        _dtype_code(k), nkeys, E, tables, bits, k.ctypes.data, v.ctypes.data,
+        pr.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), buckets.ctypes.data_as(ctypes.POINTER(ctypes.c_ubyte)),
+        vnorm.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    if rc != 0:
+        raise ValueError(f"oracle_socket_hash failed with code {rc}")
+    return buckets.reshape(*lead, tables), vnorm.reshape(lead)
+
+
+def socket_scores(q_row: np.ndarray, proj: np.ndarray, buckets: np.ndarray, vnorm: np.ndarray, tables: int,
+                  bits: int, tau: float, lib=None) -> np.ndarray:
+    """Soft-collision scores of every key for one query row (method steps 2-3): the query's
+    temperature softmax over each table's buckets, summed over the tables at each key's
+    bucket, times the key's value norm.  buckets (S, tables), vnorm (S,)."""
+    q_row = np.ascontiguousarray(q_row)
+    pr = np.ascontiguousarray(proj, dtype=np.float32)
+    b = np.ascontiguousarray(buckets, dtype=np.uint8)
+    vn = np.ascontiguousarray(vnorm, dtype=np.float64)
+    S = vn.shape[0]
+    out = np.zeros(S)
+    rc = (lib or _load()).oracle_socket_scores(
+        _dtype_code(q_row), q_row.shape[-1], tables, bits, float(tau), q_row.ctypes.data,
+        pr.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), S, b.ctypes.data_as(ctypes.POINTER(ctypes.c_ubyte)),
+        vn.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    if rc != 0:
+        raise ValueError(f"oracle_socket_scores failed with code {rc}")
+    return out
+
+
+def socket_select(scores: np.ndarray, top_k: int) -> np.ndarray:
+    """The top_k keys by score, ties to the lower index (method step 4: a deterministic
+    top-k), returned in ascending key order."""
+    order = np.lexsort((np.arange(scores.shape[0]), -scores))
+    return np.sort(order[:top_k])
+
+
+def socket_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, proj: np.ndarray, buckets: np.ndarray,
+                  vnorm: np.ndarray, *, tables: int, bits: int, tau: float, top_k: int, mode: str = "dot",
+                  scale: Optional[float] = None, gamma: float = 0.0, sink: Optional[np.ndarray] = None, lib=None):
+    """Sparse decode of q (N,Hq,1,E): per query head, scores -> top_k -> exact attention over
+    the selected keys (the same logits and sink as attn).  Returns (o (N,Hq,1,E), lse (N,Hq,1),
+    selected (N,Hq,top_k) ascending key indices, scores (N,Hq,S))."""
+    N, Hq, L, E = q.shape
+    _, Hkv, S, _ = k.shape
+    G = Hq // Hkv
+    o = np.zeros((N, Hq, 1, E))
+    lse = np.zeros((N, Hq, 1))
+    sel = np.zeros((N, Hq, top_k), dtype=np.int64)
+    sc = np.zeros((N, Hq, S))
+    for n in range(N):
+        for h in range(Hq):
+            kh = h // G
+            s = socket_scores(q[n, h, 0], proj, buckets[n, kh], vnorm[n, kh], tables, bits, tau, lib=lib)
+            idx = socket_select(s, top_k)
+            sc[n, h] = s
+            sel[n, h] = idx
+            kk = np.ascontiguousarray(k[n:n + 1, kh:kh + 1, idx])
+            vv = np.ascontiguousarray(v[n:n + 1, kh:kh + 1, idx])
+            sk = None if sink is None else np.asarray(sink, dtype=np.float64)[h:h + 1]
+            oo, ll = attn(np.ascontiguousarray(q[n:n + 1, h:h + 1]), kk, vv, mode=mode, scale=scale, gamma=gamma,
+                          sink=sk, lib=lib)
+            o[n, h] = oo[0, 0]
+            lse[n, h] = ll[0, 0]
+    return o, lse, sel, sc

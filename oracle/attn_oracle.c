@@ -349,3 +349,71 @@ int oracle_attn_bwd(int dtype, int N, int Hq, int Hkv, int L, int S, int E,
   free(DEL);
   return 0;
 }
+
+/* ------------------------------------------------------------------------ SOCKET soft-LSH scoring */
+
+int oracle_socket_hash(int dtype, long long nkeys, int E, int tables, int bits, const void* k, const void* v,
+                       const float* proj, unsigned char* buckets, double* vnorm) {
+  if (dtype < ORACLE_BF16 || dtype > ORACLE_F64) return -1;
+  if (nkeys < 0 || E <= 0 || tables <= 0 || bits <= 0 || bits > 8) return -2;
+  for (long long j = 0; j < nkeys; ++j) {
+    for (int t = 0; t < tables; ++t) {
+      unsigned code = 0;
+      for (int b = 0; b < bits; ++b) {
+        /* fp32 projection, one fused multiply-add per element in element order */
+        const float* w = proj + ((size_t)t * bits + b) * E;
+        float x = 0.0f;
+        for (int e = 0; e < E; ++e) x = fmaf((float)load_elem(dtype, k, (size_t)j * E + e), w[e], x);
+        if (x > 0.0f) code |= 1u << b;
+      }
+      buckets[(size_t)j * tables + t] = (unsigned char)code;
+    }
+    if (vnorm) {
+      double ss = 0.0;
+      for (int e = 0; e < E; ++e) {
+        const double x = load_elem(dtype, v, (size_t)j * E + e);
+        ss += x * x;
+      }
+      vnorm[j] = sqrt(ss);
+    }
+  }
+  return 0;
+}
+
+int oracle_socket_scores(int dtype, int E, int tables, int bits, double tau, const void* q, const float* proj,
+                         long long nkeys, const unsigned char* buckets, const double* vnorm, double* scores) {
+  if (dtype < ORACLE_BF16 || dtype > ORACLE_F64) return -1;
+  if (E <= 0 || tables <= 0 || bits <= 0 || bits > 8 || !(tau > 0.0)) return -2;
+  const int nb = 1 << bits;
+  double* prob = (double*)malloc(sizeof(double) * (size_t)tables * nb);
+  if (!prob) return -4;
+  for (int t = 0; t < tables; ++t) {
+    /* query projections y_b and the softmax over the 2^bits buckets of
+       sum_b s_b(bucket) y_b / tau, s_b = +1 if bit b of the bucket is set else -1 */
+    double y[8];
+    for (int b = 0; b < bits; ++b) {
+      const float* w = proj + ((size_t)t * bits + b) * E;
+      double acc = 0.0;
+      for (int e = 0; e < E; ++e) acc += load_elem(dtype, q, (size_t)e) * (double)w[e];
+      y[b] = acc;
+    }
+    double mx = -INFINITY;
+    for (int c = 0; c < nb; ++c) {
+      double a = 0.0;
+      for (int b = 0; b < bits; ++b) a += ((c >> b) & 1 ? 1.0 : -1.0) * y[b] / tau;
+      prob[(size_t)t * nb + c] = a;
+      if (a > mx) mx = a;
+    }
+    double den = 0.0;
+    for (int c = 0; c < nb; ++c) den += exp(prob[(size_t)t * nb + c] - mx);
+    for (int c = 0; c < nb; ++c) prob[(size_t)t * nb + c] = exp(prob[(size_t)t * nb + c] - mx) / den;
+  }
+  /* score_j = |v_j| * sum_t prob_t(bucket of key j in table t) */
+  for (long long j = 0; j < nkeys; ++j) {
+    double sum = 0.0;
+    for (int t = 0; t < tables; ++t) sum += prob[(size_t)t * nb + buckets[(size_t)j * tables + t]];
+    scores[j] = vnorm[j] * sum;
+  }
+  free(prob);
+  return 0;
+}

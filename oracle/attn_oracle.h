@@ -121,6 +121,25 @@ int oracle_attn_bwd(int dtype, int N, int Hq, int Hkv, int L, int S, int E,
                     long long nk, const long long* krows, double* dk, double* dv,
                     double* dsink, double* lse_out, double* delta_out, int threads);
 
+/*
+ * SOCKET soft-LSH scoring ("기술 요약: SOCKET" page, method: soft LSH steps 1-4).
+ *   oracle_socket_hash: for nkeys rows of k (E elements each) and table t,
+ *     bit b: x = proj[(t*bits + b)*E + .] . k_j in float32, one fused
+ *     multiply-add per element in element order (so the sign decision is the
+ *     same one a float32 kernel makes); bit set iff x > 0.  buckets[j*tables + t]
+ *     holds the bits of table t; vnorm[j] = |v_j| (fp64, may be NULL).
+ *   oracle_socket_scores: for one query q: y_tb = proj_tb . q (fp64), for each
+ *     table the softmax over its 2^bits buckets of sum_b s_b y_tb / tau
+ *     (s_b = +1 if bit b of the bucket is set, -1 otherwise: the query's soft
+ *     assignment from its hyperplane projections, temperature tau), and
+ *     scores[j] = vnorm[j] * sum_t prob_t(buckets[j*tables + t]).
+ * bits <= 8.  Return 0 or a negative value.
+ */
+int oracle_socket_hash(int dtype, long long nkeys, int E, int tables, int bits, const void* k, const void* v,
+                       const float* proj, unsigned char* buckets, double* vnorm);
+int oracle_socket_scores(int dtype, int E, int tables, int bits, double tau, const void* q, const float* proj,
+                         long long nkeys, const unsigned char* buckets, const double* vnorm, double* scores);
+
 /* Number of OpenMP threads oracle_attn_rows uses for a given `threads`. */
 int oracle_num_threads(int threads);
 

@@ -559,4 +559,97 @@ def pin_bwd_row_subsets_and_delta(lib):
     assert np.max(np.abs(full["lse"] - lse)) < 1e-12
 
 
+# ----------------------------------------------------------------------------- SOCKET
+
+
+def pin_socket_soft_assignment_is_product_of_sigmoids(lib):
+    # softmax over the 2^bits sign patterns of sum_b s_b y_b / tau factorises into
+    # prod_b sigmoid(2 s_b y_b / tau): one key per bucket, unit value norm, one table
+    bits, E, tau = 4, 8, 0.7
+    r = _rng(81)
+    proj = r.standard_normal((bits, E)).astype(np.float32)
+    q = r.standard_normal(E)
+    codes = np.arange(1 << bits, dtype=np.uint8)[:, None]
+    sc = oracle.socket_scores(q, proj, codes, np.ones(1 << bits), 1, bits, tau, lib=lib)
+    y = proj.astype(np.float64) @ q
+    for c in range(1 << bits):
+        s_ = np.array([1.0 if (c >> b) & 1 else -1.0 for b in range(bits)])
+        ref = np.prod(1.0 / (1.0 + np.exp(-2.0 * s_ * y / tau)))
+        assert abs(sc[c] - ref) < 1e-12
+
+
+def pin_socket_low_temperature_is_hard_collision_count(lib):
+    # tau -> 0: all mass on the query's own sign pattern; a key scores |v| * (tables it collides in)
+    tables, bits, E = 5, 3, 8
+    r = _rng(82)
+    proj = r.standard_normal((tables * bits, E)).astype(np.float32)
+    q = r.standard_normal(E)
+    qcode = [sum(1 << b for b in range(bits) if float(proj[t * bits + b].astype(np.float64) @ q) > 0)
+             for t in range(tables)]
+    buckets = r.integers(0, 1 << bits, size=(40, tables)).astype(np.uint8)
+    buckets[0] = qcode
+    vn = r.random(40) + 0.5
+    sc = oracle.socket_scores(q, proj, buckets, vn, tables, bits, 1e-4, lib=lib)
+    hard = vn * np.sum(buckets == np.array(qcode, dtype=np.uint8)[None, :], axis=1)
+    assert np.max(np.abs(sc - hard)) < 1e-9
+
+
+def pin_socket_hash_is_random_hyperplane_signs(lib):
+    # bit b of table t is sign(w_tb . k) (checked where |w.k| is clear of rounding), norms are |v|
+    tables, bits, E = 4, 6, 16
+    r = _rng(83)
+    proj = r.standard_normal((tables * bits, E)).astype(np.float32)
+    k = r.standard_normal((1, 1, 64, E)).astype(np.float32)
+    v = r.standard_normal((1, 1, 64, E)).astype(np.float32)
+    b, vn = oracle.socket_hash(k, v, proj, tables, bits, lib=lib)
+    x = k[0, 0].astype(np.float64) @ proj.astype(np.float64).T  # (64, tables*bits)
+    for j in range(64):
+        for t in range(tables):
+            for bb in range(bits):
+                xv = x[j, t * bits + bb]
+                if abs(xv) > 1e-4:
+                    assert ((int(b[0, 0, j, t]) >> bb) & 1) == (1 if xv > 0 else 0)
+    assert np.max(np.abs(vn[0, 0] - np.linalg.norm(v[0, 0].astype(np.float64), axis=1))) < 1e-12
+
+
+def pin_socket_collision_rate_follows_angle(lib):
+    # random hyperplanes: P(same bit) = 1 - angle/pi (the angular kernel the page's theory builds on)
+    E, nproj = 16, 8192
+    r = _rng(84)
+    proj = r.standard_normal((nproj, E)).astype(np.float32)
+    a = r.standard_normal(E)
+    c = r.standard_normal(E)
+    c = c - (c @ a) / (a @ a) * a
+    b_ = a / np.linalg.norm(a) * np.cos(1.0) + c / np.linalg.norm(c) * np.sin(1.0)  # angle 1 rad to a
+    keys = np.stack([a, b_])[None, None].astype(np.float32)
+    codes, _ = oracle.socket_hash(keys, keys, proj, nproj, 1, lib=lib)
+    same = np.mean(codes[0, 0, 0] == codes[0, 0, 1])
+    expect = 1.0 - 1.0 / np.pi
+    assert abs(same - expect) < 4 * np.sqrt(expect * (1 - expect) / nproj)
+
+
+def pin_socket_full_budget_is_dense_attention(lib):
+    # top_k = S selects every key: the sparse decode is the dense decode
+    q, k, v = _qkv(85, 1, 4, 2, 1, 30, 8)
+    proj = _rng(86).standard_normal((2 * 3, 8)).astype(np.float32)
+    b, vn = oracle.socket_hash(k, v, proj, 2, 3, lib=lib)
+    sink = _rng(87).standard_normal(4)
+    o, lse, sel, _ = oracle.socket_decode(q, k, v, proj, b, vn, tables=2, bits=3, tau=0.5, top_k=30, sink=sink,
+                                          lib=lib)
+    o2, l2 = oracle.attn(q, k, v, sink=sink, lib=lib)
+    assert np.all(sel == np.arange(30)) and np.max(np.abs(o - o2)) < 1e-12 and np.max(np.abs(lse - l2)) < 1e-12
+
+
+def pin_socket_selection_is_top_k_by_score(lib):
+    q, k, v = _qkv(88, 1, 2, 1, 1, 200, 8)
+    proj = _rng(89).standard_normal((4 * 4, 8)).astype(np.float32)
+    b, vn = oracle.socket_hash(k, v, proj, 4, 4, lib=lib)
+    _, _, sel, sc = oracle.socket_decode(q, k, v, proj, b, vn, tables=4, bits=4, tau=0.3, top_k=20, lib=lib)
+    for h in range(2):
+        s = sc[0, h]
+        chosen = np.zeros(200, bool)
+        chosen[sel[0, h]] = True
+        assert chosen.sum() == 20 and s[chosen].min() >= s[~chosen].max()
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -39,8 +39,14 @@ MUTANTS = {
                         "g[e] += w * (2.0 * gamma) * (load_elem(dtype, k, koff + e) - qe);"),
     "bwd_dsink_sign": ("dsink[h] -= exp(sink[h] - LSE[flat]) * DEL[flat];", "dsink[h] += exp(sink[h] - LSE[flat]) * DEL[flat];"),
     "bwd_gqa_one_head": ("for (int h = kh * G; h < (kh + 1) * G; ++h)", "for (int h = kh * G; h < kh * G + 1; ++h)"),
+    "socket_sign_flipped": ("if (x > 0.0f) code |= 1u << b;", "if (x < 0.0f) code |= 1u << b;"),
+    "socket_norm_dropped": ("scores[j] = vnorm[j] * sum;", "scores[j] = sum;"),
+    "socket_tau_inverted": ("a += ((c >> b) & 1 ? 1.0 : -1.0) * y[b] / tau;", "a += ((c >> b) & 1 ? 1.0 : -1.0) * y[b] * tau;"),
+    "socket_bits_reversed": ("a += ((c >> b) & 1 ? 1.0 : -1.0) * y[b] / tau;",
+                             "a += ((c >> (bits - 1 - b)) & 1 ? 1.0 : -1.0) * y[b] / tau;"),
     "bwd_dv_unweighted": ("gv[e] += p * load_elem(dtype, dout, qoff + e);", "gv[e] += load_elem(dtype, dout, qoff + e);"),
-    "head_dim_truncated": ("for (int e = 0; e < E; ++e) acc += load_elem", "for (int e = 0; e < E - 1; ++e) acc += load_elem"),
+    "head_dim_truncated": ("for (int e = 0; e < E; ++e) acc += load_elem(dtype, q, qoff + e)",
+                           "for (int e = 0; e < E - 1; ++e) acc += load_elem(dtype, q, qoff + e)"),
     "lse_without_max": ("lse[r] = M + log(D);", "lse[r] = log(D);"),
     "empty_row_nan": ("if (M == -INFINITY) { /* nothing visible", "if (0) { /* nothing visible"),
     "bf16_shift": ("<< 16;", "<< 15;"),
