@@ -3,7 +3,8 @@
  *
  * One operation, computed by attn_fwd (prefill), attn_fwd_biased (prefill
  * with a general bias), attn_decode (split-K decode) and attn_stream_decode
- * (decode over a rolling cache), with its gradients from attn_bwd:
+ * (decode over a rolling cache) and attn_socket_decode (decode over the keys a
+ * soft-LSH score selects), with its gradients from attn_bwd:
  *
  *   O = softmax(Z) V,  Z_ij = logit(q_i, k_j) + B_ij,  B_ij in {0, -inf}
  *
@@ -231,6 +232,46 @@ int attn_stream_decode(attn_dtype dt, int N, int Hq, int Hkv, int E, int n_sink,
 
 /* Workspace bytes attn_stream_decode needs (0 if the sizes are invalid). */
 size_t attn_stream_decode_workspace_bytes(int N, int Hq, int Hkv, int E, int n_sink, int window, long long pos,
+                                          int num_splits);
+
+/*
+ * SOCKET soft-LSH sparse decode ("기술 요약: SOCKET" page, method: soft LSH
+ * steps 1-4).  proj: (tables*bits, E) float32 random hyperplanes, drawn by the
+ * caller (the method is data-independent: any fixed random draw).
+ *
+ * attn_socket_hash -- prefill step: for every key row of k (N, Hkv, S, E, bf16)
+ * and table t, bit b of buckets[(n,kh,j)*tables + t] is set iff the float32
+ * projection proj[t*bits + b] . k_j (fused multiply-adds in element order) is
+ * > 0; vnorm (N, Hkv, S) float32 receives |v_j| (may be NULL, then v may be NULL).
+ * 1 <= tables <= 64, 1 <= bits <= 8.
+ */
+int attn_socket_hash(attn_dtype dt, int N, int Hkv, int S, int E, int tables, int bits,
+                     const void* k, const void* v, const float* proj,
+                     unsigned char* buckets, float* vnorm, void* stream);
+
+/*
+ * attn_socket_decode -- decode step for q (N, Hq, 1, E): per query head, the
+ * soft assignment of the query to each table's buckets, p_t(c) = softmax over
+ * the 2^bits sign patterns c of sum_b s_b(c) (proj[t*bits+b] . q) / tau
+ * (s_b(c) = +1 if bit b of c is set, else -1); key scores
+ * score_j = vnorm_j * sum_t p_t(bucket of key j in table t); the top_k keys by
+ * score (ties to the lower index) are attended to exactly, with the logits,
+ * sink and LSE conventions of attn_decode (no mask: every key precedes the
+ * query).  o (N, Hq, 1, E), lse (N, Hq, 1).  selected: NULL, or (N, Hq, top_k)
+ * int32 receiving the chosen key rows in ascending order.  1 <= top_k <= S;
+ * tau > 0; Hq/Hkv <= 16 and (Hq/Hkv) * tables * 2^bits * 4 bytes <= 64 KB.
+ * workspace: attn_socket_decode_workspace_bytes(...) bytes, 256-byte aligned.
+ * bf16 only.
+ */
+int attn_socket_decode(attn_dtype dt, int N, int Hq, int Hkv, int S, int E, int tables, int bits, float tau,
+                       int top_k, const void* q, const void* k, const void* v, const float* proj,
+                       const unsigned char* buckets, const float* vnorm,
+                       attn_mode mode, float scale, float gamma, const float* sink,
+                       void* o, float* lse, int* selected,
+                       int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_socket_decode needs (0 for invalid sizes). */
+size_t attn_socket_decode_workspace_bytes(int N, int Hq, int Hkv, int S, int E, int tables, int bits, int top_k,
                                           int num_splits);
 
 /* Static text for a status code. */

@@ -356,6 +356,7 @@ int oracle_socket_hash(int dtype, long long nkeys, int E, int tables, int bits, 
                        const float* proj, unsigned char* buckets, double* vnorm) {
   if (dtype < ORACLE_BF16 || dtype > ORACLE_F64) return -1;
   if (nkeys < 0 || E <= 0 || tables <= 0 || bits <= 0 || bits > 8) return -2;
+#pragma omp parallel for schedule(static)
   for (long long j = 0; j < nkeys; ++j) {
     for (int t = 0; t < tables; ++t) {
       unsigned code = 0;

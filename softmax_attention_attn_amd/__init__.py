@@ -35,6 +35,7 @@ MODES = {"dot": 0, "rbf": 1}
 
 EXPORTS = ("attn_fwd", "attn_fwd_biased", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_num_splits", "attn_decode_workspace_bytes",
            "attn_stream_append", "attn_stream_decode", "attn_stream_decode_workspace_bytes",
+           "attn_socket_hash", "attn_socket_decode", "attn_socket_decode_workspace_bytes",
            "attn_status_string", "attn_last_error")
 
 
@@ -77,6 +78,13 @@ def load() -> ctypes.CDLL:
         lib.attn_stream_decode.argtypes = [I, I, I, I, I, I, I, LL, P, P, P, I, F, F, P, P, P, I, P, Z, P]
         lib.attn_stream_decode_workspace_bytes.restype = Z
         lib.attn_stream_decode_workspace_bytes.argtypes = [I, I, I, I, I, I, LL, I]
+        lib.attn_socket_hash.restype = I
+        lib.attn_socket_hash.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P]
+        lib.attn_socket_decode.restype = I
+        lib.attn_socket_decode.argtypes = [I, I, I, I, I, I, I, I, F, I, P, P, P, P, P, P, I, F, F, P, P, P, P, I, P,
+                                           Z, P]
+        lib.attn_socket_decode_workspace_bytes.restype = Z
+        lib.attn_socket_decode_workspace_bytes.argtypes = [I] * 9
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_status_string.argtypes = [I]
         lib.attn_last_error.restype = ctypes.c_char_p
@@ -315,3 +323,48 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
                       workspace.numel() * workspace.element_size(), _stream(q.device, stream))
     _check(rc)
     return dq, dk, dv, dsink
+
+
+def socket_hash(k: torch.Tensor, v: torch.Tensor, proj: torch.Tensor, *, tables: int, bits: int,
+                stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """SOCKET prefill hashing through attn_socket_hash: bucket codes (N, Hkv, S, tables) uint8 and
+    value norms (N, Hkv, S) float32 of a bf16 key/value cache; proj (tables*bits, E) float32."""
+    if k.dim() != 4 or not k.is_contiguous() or k.shape != v.shape or not v.is_contiguous():
+        raise ValueError("k and v must be contiguous 4-D tensors of one shape")
+    if proj.dtype != torch.float32 or not proj.is_contiguous() or proj.shape != (tables * bits, k.shape[3]):
+        raise ValueError(f"proj must be a contiguous float32 ({tables * bits}, {k.shape[3]}) tensor")
+    N, Hkv, S, E = k.shape
+    buckets = torch.empty((N, Hkv, S, tables), dtype=torch.uint8, device=k.device)
+    vnorm = torch.empty((N, Hkv, S), dtype=torch.float32, device=k.device)
+    rc = load().attn_socket_hash(_dtype_code(k), N, Hkv, S, E, int(tables), int(bits), _ptr(k), _ptr(v),
+                                 _ptr(proj), _ptr(buckets), _ptr(vnorm), _stream(k.device, stream))
+    _check(rc)
+    return buckets, vnorm
+
+
+def socket_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, proj: torch.Tensor, buckets: torch.Tensor,
+                  vnorm: torch.Tensor, *, tables: int, bits: int, tau: float, top_k: int,
+                  scale: Optional[float] = None, mode: str = "dot", gamma: Optional[float] = None,
+                  sink: Optional[torch.Tensor] = None, num_splits: int = 0, want_selected: bool = False,
+                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, stream=None):
+    """SOCKET sparse decode through attn_socket_decode; returns (o, lse, selected or None)."""
+    N, Hq, Hkv, L, S, E, scale, gamma = _common(q, k, v, sink, scale, mode, gamma)
+    if L != 1:
+        raise ValueError(f"socket_decode takes one query per sequence, got q {tuple(q.shape)}")
+    lib = load()
+    need = int(lib.attn_socket_decode_workspace_bytes(N, Hq, Hkv, S, E, tables, bits, top_k, num_splits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((N, Hq, 1), dtype=torch.float32, device=q.device)
+    sel = torch.empty((N, Hq, top_k), dtype=torch.int32, device=q.device) if want_selected else None
+    rc = lib.attn_socket_decode(_dtype_code(q), N, Hq, Hkv, S, E, int(tables), int(bits), float(tau), int(top_k),
+                                _ptr(q), _ptr(k), _ptr(v), _ptr(proj), _ptr(buckets), _ptr(vnorm), MODES[mode],
+                                scale, gamma, _ptr(sink), _ptr(out), _ptr(lse), _ptr(sel), int(num_splits),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(q.device, stream))
+    _check(rc)
+    return out, lse, sel

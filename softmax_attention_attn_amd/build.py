@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["attn_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_bf16.hip", "stream_cache.hip", "backward_bf16.hip"]
+SOURCES = ["attn_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_bf16.hip", "stream_cache.hip", "backward_bf16.hip", "socket_bf16.hip"]
 ARCH = "gfx950"
 
 

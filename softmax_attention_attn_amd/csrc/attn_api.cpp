@@ -8,6 +8,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -230,6 +231,116 @@ int attn_bwd(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, const v
   a.dsink = dsink;
   a.workspace = static_cast<float*>(workspace);
   return hip_status(attn_impl::launch_backward_bf16(a, static_cast<hipStream_t>(stream)), "attn_bwd launch");
+}
+
+// ----------------------------------------------------------------------------- SOCKET
+
+int socket_check(int N, int Hq, int Hkv, int S, int E, int tables, int bits) {
+  if (N < 0 || Hq <= 0 || Hkv <= 0 || S < 0 || Hq % Hkv != 0) return fail(ATTN_ERR_SHAPE, "invalid sizes");
+  if (E != 64 && E != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension E=%d (supported: 64, 128)", E);
+  if (tables < 1 || tables > 64 || bits < 1 || bits > 8)
+    return fail(ATTN_ERR_ARG, "need 1 <= tables <= 64 and 1 <= bits <= 8 (tables=%d bits=%d)", tables, bits);
+  if ((long long)N * Hkv * S * E > kMaxElems) return fail(ATTN_ERR_SHAPE, "tensor too large");
+  return ATTN_OK;
+}
+
+int attn_socket_hash(attn_dtype dt, int N, int Hkv, int S, int E, int tables, int bits, const void* k, const void* v,
+                     const float* proj, unsigned char* buckets, float* vnorm, void* stream) {
+  if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "SOCKET hashing is implemented for bf16 keys only");
+  int rc = socket_check(N, Hkv, Hkv, S, E, tables, bits);
+  if (rc != ATTN_OK) return rc;
+  if ((long long)N * S == 0) return ok();
+  if (!k || !proj || !buckets || (vnorm && !v)) return fail(ATTN_ERR_NULL, "k, proj and buckets (and v with vnorm) must not be NULL");
+  if (!aligned(k, 16) || (v && !aligned(v, 16)) || !aligned(proj, 4) || (vnorm && !aligned(vnorm, 4)))
+    return fail(ATTN_ERR_ALIGN, "k and v must be 16-byte aligned, proj and vnorm 4-byte aligned");
+  if (((long long)N * Hkv * S * tables + 255) / 256 > kMaxGrid) return fail(ATTN_ERR_SHAPE, "grid too large");
+  attn_impl::SocketHashArgs a{k, v, proj, buckets, vnorm, N, Hkv, S, E, tables, bits};
+  return hip_status(attn_impl::launch_socket_hash_bf16(a, static_cast<hipStream_t>(stream)), "attn_socket_hash launch");
+}
+
+// Workspace layout: bucket probabilities, scores, selected rows, decode partials.
+struct SocketLayout {
+  size_t probs, scores, sel, parts, total;
+  int splits;
+};
+
+SocketLayout socket_layout(int N, int Hq, int S, int E, int tables, int bits, int top_k, int num_splits) {
+  SocketLayout l;
+  const size_t heads = (size_t)N * Hq;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  l.splits = num_splits > 0 ? num_splits : (int)std::min<long long>(std::max<long long>(1, (top_k + 255) / 256),
+                                                                     std::max<long long>(1, (2048 + (long long)heads - 1) / std::max<long long>(1, (long long)heads)));
+  l.probs = 0;
+  l.scores = up(l.probs + heads * tables * ((size_t)1 << bits) * sizeof(float));
+  l.sel = up(l.scores + heads * (size_t)S * sizeof(float));
+  l.parts = up(l.sel + heads * (size_t)top_k * sizeof(int));
+  l.total = l.parts + workspace_for(N, Hq, E, l.splits);
+  return l;
+}
+
+size_t attn_socket_decode_workspace_bytes(int N, int Hq, int Hkv, int S, int E, int tables, int bits, int top_k,
+                                          int num_splits) {
+  if (N < 0 || Hq <= 0 || Hkv <= 0 || S < 0 || Hq % Hkv != 0 || (E != 64 && E != 128) || tables < 1 ||
+      tables > 64 || bits < 1 || bits > 8 || top_k < 1 || top_k > S || num_splits < 0)
+    return 0;
+  return socket_layout(N, Hq, S, E, tables, bits, top_k, num_splits).total;
+}
+
+int attn_socket_decode(attn_dtype dt, int N, int Hq, int Hkv, int S, int E, int tables, int bits, float tau, int top_k,
+                       const void* q, const void* k, const void* v, const float* proj, const unsigned char* buckets,
+                       const float* vnorm, attn_mode mode, float scale, float gamma, const float* sink, void* o,
+                       float* lse, int* selected, int num_splits, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  int rc = check_args(dt, N, Hq, Hkv, 1, S, E, q, k, v, mode, scale, gamma, 1, 0, 0, sink, o, lse);
+  if (rc != ATTN_OK) return rc;
+  if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "SOCKET decode is implemented for bf16 only");
+  rc = socket_check(N, Hq, Hkv, S, E, tables, bits);
+  if (rc != ATTN_OK) return rc;
+  if (!(std::isfinite(tau) && tau > 0.f)) return fail(ATTN_ERR_ARG, "tau must be finite and > 0");
+  if (top_k < 1 || top_k > S) return fail(ATTN_ERR_ARG, "top_k=%d outside [1, S=%d]", top_k, S);
+  if (num_splits < 0) return fail(ATTN_ERR_ARG, "num_splits=%d must be >= 0", num_splits);
+  const int G = Hq / Hkv;
+  if (G > 16) return fail(ATTN_ERR_UNSUPPORTED, "SOCKET scoring handles up to 16 query heads per key/value head");
+  if (attn_impl::socket_lds_bytes(G, tables, bits) > 64 * 1024)
+    return fail(ATTN_ERR_UNSUPPORTED, "(Hq/Hkv) * tables * 2^bits probabilities exceed 64 KB of LDS");
+  if (N == 0) return ok();
+  if (!proj || !buckets || !vnorm) return fail(ATTN_ERR_NULL, "proj, buckets and vnorm must not be NULL");
+  if (!aligned(proj, 4) || !aligned(vnorm, 4) || (selected && !aligned(selected, 4)))
+    return fail(ATTN_ERR_ALIGN, "proj, vnorm and selected must be 4-byte aligned");
+  const SocketLayout l = socket_layout(N, Hq, S, E, tables, bits, top_k, num_splits);
+  if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", l.total);
+  if (workspace_bytes < l.total) return fail(ATTN_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, l.total);
+  if (!aligned(workspace, 256)) return fail(ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if ((long long)N * Hq > 65535LL) return fail(ATTN_ERR_SHAPE, "grid too large");
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  attn_impl::SocketSelectArgs s;
+  s.q = q;
+  s.proj = proj;
+  s.buckets = buckets;
+  s.vnorm = vnorm;
+  s.probs = reinterpret_cast<float*>(ws + l.probs);
+  s.scores = reinterpret_cast<float*>(ws + l.scores);
+  s.selected = selected ? selected : reinterpret_cast<int*>(ws + l.sel);
+  s.N = N;
+  s.Hq = Hq;
+  s.Hkv = Hkv;
+  s.S = S;
+  s.E = E;
+  s.tables = tables;
+  s.bits = bits;
+  s.top_k = top_k;
+  s.tau = tau;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = hip_status(attn_impl::launch_socket_select_bf16(s, st), "attn_socket_decode select launch");
+  if (rc != ATTN_OK) return rc;
+  attn_impl::DecodeArgs d;
+  d.f = make_args(N, Hq, Hkv, 1, S, E, q, k, v, mode, scale, gamma, 1, 0, 0, sink, o, lse);
+  d.num_splits = l.splits;
+  d.part_o = reinterpret_cast<float*>(ws + l.parts);
+  d.part_ml = d.part_o + (size_t)N * Hq * l.splits * E;
+  d.key_index = s.selected;
+  d.index_count = top_k;
+  return hip_status(attn_impl::launch_decode_bf16(d, st), "attn_socket_decode launch");
 }
 
 int attn_decode_num_splits(int N, int Hq, int Hkv, int S, int E, int causal, int window, int n_reg) {

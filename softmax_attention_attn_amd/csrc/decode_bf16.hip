@@ -37,15 +37,21 @@ struct DecodeParams {
   float* part_ml;
   int N, Hq, Hkv, kv_rows, n_reg;
   int first_real;  // keys n_reg .. n_reg+first_real-1 are outside the window
-  int nkeys;       // n_reg + visible real keys
+  int nkeys;       // n_reg + visible real keys (indexed: keys per query head)
   int chunk;       // keys per split (multiple of KSTEP)
   int num_splits;
   int qgroups;     // ceil(G / 16)
   float c_logit, c_bias;
+  // Indexed mode (key_index != nullptr): every query head has its own list of
+  // nkeys key rows at key_index[(n*Hq + h)*nkeys ..]; one query head per
+  // workgroup (grid y = Hq), its key/value head h / (Hq/Hkv).
+  const int* key_index;
 };
 
-// Virtual key index (registers first, then the visible real keys) -> key row.
-__device__ __forceinline__ int key_row(int vidx, const DecodeParams& p) {
+// Virtual key index -> key row: registers first, then the visible real keys;
+// in indexed mode the head's list.
+__device__ __forceinline__ int key_row(int vidx, const DecodeParams& p, const int* kidx) {
+  if (kidx) return kidx[vidx];
   return vidx < p.n_reg ? vidx : vidx + p.first_real;
 }
 
@@ -64,12 +70,25 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int l16 = lane & 15, g = lane >> 4;
   const int split = blockIdx.x;
-  const int kvh = blockIdx.y / p.qgroups, qg = blockIdx.y % p.qgroups;
   const int n = blockIdx.z;
   const int G = p.Hq / p.Hkv;
-  const int slot = qg * 16 + l16;
-  const bool qvalid = slot < G;
-  const int h = kvh * G + (qvalid ? slot : 0);
+  const bool indexed = p.key_index != nullptr;
+  int kvh, qg, slot, h;
+  bool qvalid;
+  if (indexed) {  // one query head per workgroup, in MFMA column 0
+    h = blockIdx.y;
+    kvh = h / G;
+    qg = 0;
+    slot = l16;
+    qvalid = l16 == 0;
+  } else {
+    kvh = blockIdx.y / p.qgroups;
+    qg = blockIdx.y % p.qgroups;
+    slot = qg * 16 + l16;
+    qvalid = slot < G;
+    h = kvh * G + (qvalid ? slot : 0);
+  }
+  const int* kidx = indexed ? p.key_index + ((size_t)n * p.Hq + h) * p.nkeys : nullptr;
 
   // Q^T fragments (B operand): lane (l16, g) holds Q[h][32s + 8g .. +8].
   const uint16_t* qrow = p.q + ((size_t)n * p.Hq + h) * E;
@@ -98,7 +117,7 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams p) {
     for (int b = 0; b < 2; ++b) {
       const int vk = vb + 16 * b + l16;
       const bool ok = vk < v1;
-      const uint16_t* row = kbase + (size_t)key_row(ok ? vk : v0, p) * E;
+      const uint16_t* row = kbase + (size_t)key_row(ok ? vk : v0, p, kidx) * E;
 #pragma unroll
       for (int s = 0; s < QS; ++s) kr[b][s] = load16_or_zero(row + 32 * s + 8 * g, ok);
     }
@@ -106,7 +125,7 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams p) {
     for (int i = 0; i < 8; ++i) {
       const int vk = vb + (i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4));
       const bool ok = vk < v1 && l16 < ECH;
-      vr[i] = load16_or_zero(vbase + (size_t)key_row(ok ? vk : v0, p) * E + 8 * l16, ok);
+      vr[i] = load16_or_zero(vbase + (size_t)key_row(ok ? vk : v0, p, kidx) * E + 8 * l16, ok);
     }
   };
 
@@ -206,11 +225,12 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams p) {
     }
   __syncthreads();
 
-  const size_t part_base = ((size_t)n * p.Hq + (size_t)kvh * G) * p.num_splits + split;
+  const size_t part_base = ((size_t)n * p.Hq + (indexed ? (size_t)h : (size_t)kvh * G)) * p.num_splits + split;
+  const int nslots = indexed ? 1 : G;
   for (int idx = tid; idx < 16 * E; idx += NT) {
     const int sl = idx / E, e = idx % E;
     const int gs = qg * 16 + sl;
-    if (gs >= G) continue;
+    if (gs >= nslots) continue;
     float M = kNegInf;
 #pragma unroll
     for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, sM[w][sl]);
@@ -319,7 +339,7 @@ __global__ __launch_bounds__(E) void decode_combine_kernel(CombineParams p) {
 
 template <int E, bool RBF>
 hipError_t launch_t(const DecodeParams& p, const CombineParams& c, int N, hipStream_t stream) {
-  dim3 grid((unsigned)p.num_splits, (unsigned)(p.Hkv * p.qgroups), (unsigned)N);
+  dim3 grid((unsigned)p.num_splits, (unsigned)(p.key_index ? p.Hq : p.Hkv * p.qgroups), (unsigned)N);
   hipLaunchKernelGGL((decode_split_kernel<E, RBF>), grid, dim3(NT), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -356,9 +376,10 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   p.kv_rows = f.kv_rows;
   p.n_reg = f.n_reg;
   p.first_real = dk.first_real;
-  p.nkeys = dk.count;
+  p.nkeys = a.key_index ? a.index_count : dk.count;
+  p.key_index = a.key_index;
   p.num_splits = a.num_splits;
-  const int per = (dk.count + a.num_splits - 1) / a.num_splits;
+  const int per = (p.nkeys + a.num_splits - 1) / a.num_splits;
   p.chunk = ((per + KSTEP - 1) / KSTEP) * KSTEP;
   if (p.chunk == 0) p.chunk = KSTEP;
   const int G = f.Hq / f.Hkv;

@@ -44,6 +44,8 @@ struct DecodeArgs {
   int num_splits;
   float* part_o;      // [N][Hq][num_splits][E]   unnormalised outputs
   float* part_ml;     // [N][Hq][num_splits][2]   running max (log2 units), running sum
+  const int* key_index = nullptr;  // optional: per query head, index_count key rows to attend to
+  int index_count = 0;
 };
 
 hipError_t launch_prefill_bf16(const FwdArgs& a, hipStream_t stream);
@@ -66,6 +68,31 @@ struct BwdArgs {
 };
 hipError_t launch_backward_bf16(const BwdArgs& a, hipStream_t stream);
 size_t backward_workspace_bytes(int N, int Hq, int L);
+
+// SOCKET soft-LSH sparse decode (socket_bf16.hip).
+struct SocketHashArgs {
+  const void* k;
+  const void* v;
+  const float* proj;       // (tables*bits, E)
+  uint8_t* buckets;        // (N, Hkv, S, tables)
+  float* vnorm;            // (N, Hkv, S)
+  int N, Hkv, S, E, tables, bits;
+};
+hipError_t launch_socket_hash_bf16(const SocketHashArgs& a, hipStream_t stream);
+
+struct SocketSelectArgs {
+  const void* q;           // (N, Hq, 1, E)
+  const float* proj;
+  const uint8_t* buckets;
+  const float* vnorm;
+  float* probs;            // workspace [N*Hq][tables][2^bits]
+  float* scores;           // workspace [N*Hq][S]
+  int* selected;           // [N*Hq][top_k] ascending key rows
+  int N, Hq, Hkv, S, E, tables, bits, top_k;
+  float tau;
+};
+hipError_t launch_socket_select_bf16(const SocketSelectArgs& a, hipStream_t stream);
+size_t socket_lds_bytes(int G, int tables, int bits);
 
 // Rolling key/value cache append: tokens at positions pos .. pos+T-1 from
 // k_new / v_new (N, Hkv, T, E) into k_cache / v_cache (N, Hkv, n_sink+window, E);

@@ -231,6 +231,53 @@ def test_stream_decode_workspace_matches_decode_over_kept_rows(lib):
     assert lib.attn_stream_decode_workspace_bytes(2, 8, 2, 128, 4, 0, 5, 0) == 0
 
 
+def shash(lib, dt=0, N=1, Hkv=2, S=16, E=64, tables=4, bits=4, k=A, v=A, proj=A, buckets=A, vnorm=A):
+    return lib.attn_socket_hash(dt, N, Hkv, S, E, tables, bits, k, v, proj, buckets, vnorm, None)
+
+
+def sdecs(lib, dt=0, N=1, Hq=4, Hkv=2, S=64, E=64, tables=4, bits=4, tau=0.5, top_k=8, q=A, k=A, v=A, proj=A,
+          buckets=A, vnorm=A, mode=0, scale=0.125, gamma=0.0, sink=None, o=A, lse=A, sel=None, splits=0, ws=A,
+          wsb=1 << 30):
+    return lib.attn_socket_decode(dt, N, Hq, Hkv, S, E, tables, bits, tau, top_k, q, k, v, proj, buckets, vnorm, mode,
+                                  scale, gamma, sink, o, lse, sel, splits, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=1), -4),
+    (dict(E=96), -4),
+    (dict(bits=9), -8),
+    (dict(bits=0), -8),
+    (dict(tables=65), -8),
+    (dict(k=None), -1),
+    (dict(proj=A + 2), -5),
+])
+def test_socket_hash_rejects(lib, kw, code):
+    assert shash(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=1), -4),
+    (dict(top_k=0), -8),
+    (dict(top_k=65), -8),
+    (dict(tau=0.0), -8),
+    (dict(tau=float("nan")), -8),
+    (dict(Hq=34, Hkv=2), -4),
+    (dict(tables=64, bits=8, Hq=4, Hkv=1), -4),
+    (dict(buckets=None), -1),
+    (dict(ws=None), -6),
+    (dict(wsb=100), -6),
+    (dict(ws=A + 16), -5),
+    (dict(splits=-1), -8),
+])
+def test_socket_decode_rejects(lib, kw, code):
+    assert sdecs(lib, **kw) == code
+
+
+def test_socket_workspace_sizes(lib):
+    assert lib.attn_socket_decode_workspace_bytes(8, 32, 8, 131072, 128, 64, 4, 3972, 0) > 8 * 32 * 131072 * 4
+    assert lib.attn_socket_decode_workspace_bytes(8, 32, 8, 100, 128, 64, 4, 101, 0) == 0
+
+
 def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(attn, "LIB_PATH", "/nonexistent/libattn.so")
     monkeypatch.setattr(attn, "_lib", None)

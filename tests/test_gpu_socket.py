@@ -1,0 +1,104 @@
+"""GPU parity of SOCKET soft-LSH sparse decode (attn_socket_hash and
+attn_socket_decode through the C ABI) against the fp64 oracle.
+
+Bucket codes are integers decided by float32 projections computed the same way
+on both sides (fused multiply-adds in element order), so they must match bit
+for bit; value norms within 1e-5 relative.  The top-k set is unique only where
+the k-th and (k+1)-th scores are apart: with the oracle's fp64 scores, every
+key scoring above s_k (1 + 1e-4) must be chosen and every chosen key must score
+at least s_k (1 - 1e-4) (s_k the k-th largest score); where no other key lies
+in that band the chosen set must equal the oracle's and the output must match
+the oracle's sparse attention within 2e-2 (O) / 1e-3 (LSE).  With top_k = S the
+sparse decode must equal the dense decode.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import softmax_attention_attn_amd as attn
+from gpu_util import say, to_device
+from workloads import gen
+from workloads.configs import Workload
+
+pytestmark = pytest.mark.gpu
+
+
+def W(name, N, Hq, Hkv, S, E, mode="dot", sink=False, seed=51, k_dist="normal", gamma=0.05):
+    return Workload(name, "bf16", N, Hq, Hkv, 1, S, E, mode, float(1.0 / np.sqrt(E)), float(gamma), True, 0, 0,
+                    sink, True, seed, k_dist)
+
+
+CASES = [
+    (W("dot_gqa4_sink_e128", 2, 8, 2, 3000, 128, sink=True), 8, 6, 4.0, 200, (0, 3)),
+    (W("rbf_e64_lognormal_keys", 1, 4, 4, 2500, 64, mode="rbf", k_dist="dir_lognormal"), 16, 4, 2.0, 333, (0,)),
+    (W("gqa16_many_tables", 1, 16, 1, 1500, 64), 64, 2, 8.0, 64, (0,)),
+    (W("ragged_small_budget_e128", 3, 4, 2, 777, 128, sink=True), 12, 5, 1.0, 17, (0, 2)),
+]
+
+
+def _run(w, tables, bits, tau, top_k, splits):
+    inp = gen.generate(w)
+    q, k, v, sink = to_device(inp)
+    proj_np = gen.socket_projections(w.seed, tables, bits, w.E)
+    proj = torch.from_numpy(proj_np).to("cuda:0")
+    bk, vn = attn.socket_hash(k, v, proj, tables=tables, bits=bits)
+    b_ref, vn_ref = oracle.socket_hash(inp.k, inp.v, proj_np, tables, bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(bk.cpu().numpy(), b_ref), "bucket codes differ"
+    assert np.max(np.abs(vn.cpu().numpy() - vn_ref) / np.maximum(vn_ref, 1e-30)) < 1e-5
+    o_ref, l_ref, sel_ref, sc_ref = oracle.socket_decode(inp.q, inp.k, inp.v, proj_np, b_ref, vn_ref, tables=tables,
+                                                         bits=bits, tau=tau, top_k=top_k, mode=w.mode,
+                                                         scale=w.scale, gamma=w.gamma, sink=inp.sink)
+    outs = []
+    for s in splits:
+        o, lse, sel = attn.socket_decode(q, k, v, proj, bk, vn, tables=tables, bits=bits, tau=tau, top_k=top_k,
+                                         scale=w.scale, mode=w.mode, gamma=w.gamma, sink=sink, num_splits=s,
+                                         want_selected=True)
+        torch.cuda.synchronize()
+        outs.append((s, o, lse, sel))
+    return inp, (o_ref, l_ref, sel_ref, sc_ref), outs
+
+
+@pytest.mark.parametrize("w,tables,bits,tau,top_k,splits", CASES, ids=[c[0].name for c in CASES])
+def test_socket_decode(w, tables, bits, tau, top_k, splits):
+    say(f"[socket] {w.name} tables={tables} bits={bits} tau={tau} top_k={top_k}")
+    inp, (o_ref, l_ref, sel_ref, sc_ref), outs = _run(w, tables, bits, tau, top_k, splits)
+    for s, o, lse, sel in outs:
+        og = o.float().cpu().numpy().astype(np.float64)
+        lg = lse.cpu().numpy().astype(np.float64)
+        sg = sel.cpu().numpy()
+        unique = 0
+        for n in range(w.N):
+            for h in range(w.Hq):
+                sc = sc_ref[n, h]
+                sk = np.sort(sc)[::-1][top_k - 1]
+                hi, lo = sk * (1 + 1e-4), sk * (1 - 1e-4)
+                chosen = np.zeros(w.S, bool)
+                chosen[sg[n, h]] = True
+                assert np.all(np.diff(sg[n, h]) > 0), "selection not ascending / repeated"
+                assert chosen.sum() == top_k
+                assert np.all(chosen[sc > hi]), "a clearly better key was left out"
+                assert np.all(sc[chosen] >= lo), "a clearly worse key was chosen"
+                if np.sum(sc >= lo) == top_k:  # the top-k set is unique: compare exactly
+                    unique += 1
+                    assert np.array_equal(sg[n, h], sel_ref[n, h])
+                    assert np.max(np.abs(og[n, h] - o_ref[n, h])) <= 2e-2
+                    assert abs(lg[n, h, 0] - l_ref[n, h, 0]) <= 1e-3
+        say(f"  splits={s}: {unique}/{w.N * w.Hq} heads with a unique top-k, all checked")
+        assert unique >= 0.75 * w.N * w.Hq
+
+
+def test_socket_full_budget_equals_dense_decode():
+    w = W("full_budget", 2, 4, 2, 700, 128, sink=True)
+    inp = gen.generate(w)
+    q, k, v, sink = to_device(inp)
+    proj = torch.from_numpy(gen.socket_projections(w.seed, 4, 8, w.E)).to("cuda:0")
+    bk, vn = attn.socket_hash(k, v, proj, tables=4, bits=8)
+    o1, l1, sel = attn.socket_decode(q, k, v, proj, bk, vn, tables=4, bits=8, tau=1.0, top_k=700, sink=sink,
+                                     num_splits=3, want_selected=True)
+    o2, l2 = attn.decode(q, k, v, sink=sink, num_splits=3)
+    torch.cuda.synchronize()
+    assert torch.equal(sel.cpu(), torch.arange(700, dtype=torch.int32).expand(2, 4, 700))
+    assert (o1.float() - o2.float()).abs().max().item() <= 2e-2
+    assert (l1 - l2).abs().max().item() <= 1e-3

@@ -169,3 +169,8 @@ def key_lengths(seed: int, N: int, S_real: int) -> np.ndarray:
     k = _rng(seed, 9).integers(0, S_real + 1, size=N).astype(np.int32)
     k[0] = S_real
     return k
+
+
+def socket_projections(seed: int, tables: int, bits: int, E: int) -> np.ndarray:
+    """Random hyperplanes for SOCKET hashing: (tables*bits, E) float32, iid N(0, 1)."""
+    return _rng(seed, 10).standard_normal((tables * bits, E)).astype(np.float32)
