@@ -11,7 +11,9 @@ workloads are timed the same way and reported under "extras" (prefill in
 TFLOP/s, decode in HBM GB/s over the K/V bytes read once), as is one step of
 streaming decode over a rolling cache (append the newest token, decode it; HBM
 GB/s over the kept rows read once) and the backward pass on the C2 and C3
-shapes (TFLOP/s at 10*E flops per visible pair).
+shapes (TFLOP/s at 10*E flops per visible pair) and a SOCKET sparse decode step
+on the long-context decode shape (HBM GB/s over the codes, norms and selected
+rows; speedup over the dense decode).
 
 The CPU baseline leg times the fp64 oracle on a bounded sample of rows of the
 headline workload, on this host's cores, and checks the GPU output on those
@@ -203,6 +205,37 @@ def time_backward(w, steps: int, warmup: int, torch, attn):
     return start.elapsed_time(end) / steps
 
 
+def time_socket(sw, steps: int, warmup: int, torch, attn):
+    """Average ms per SOCKET decode step (scores, top-k, sparse attention) on the base decode
+    workload's cache, hashed once before timing."""
+    dev = torch.device("cuda:0")
+    w = sw.base
+    log(f"[bench] {sw.name}: generating inputs")
+    inp = gen.generate(w)
+    q, k, v, sink = to_device(inp, torch, dev)
+    proj = torch.from_numpy(gen.socket_projections(w.seed, sw.tables, sw.bits, w.E)).to(dev)
+    buckets, vnorm = attn.socket_hash(k, v, proj, tables=sw.tables, bits=sw.bits)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.N, w.Hq, 1), dtype=torch.float32, device=dev)
+    need = int(attn.load().attn_socket_decode_workspace_bytes(w.N, w.Hq, w.Hkv, w.S, w.E, sw.tables, sw.bits,
+                                                              sw.top_k, 0))
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    kw = dict(tables=sw.tables, bits=sw.bits, tau=sw.tau, top_k=sw.top_k, scale=w.scale, sink=sink, workspace=ws,
+              out=o, lse=lse)
+    for _ in range(warmup + 1):
+        attn.socket_decode(q, k, v, proj, buckets, vnorm, **kw)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        attn.socket_decode(q, k, v, proj, buckets, vnorm, **kw)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
 def stream_rate(sw, ms: float):
     gbs = configs.stream_bytes(sw) / (ms * 1e-3) / 1e9
     return {"value": gbs, "unit": "GB/s", "bound": "hbm", "peak": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS}
@@ -269,7 +302,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=configs.C2.name,
-                    choices=sorted(configs.BY_NAME) + sorted(configs.STREAM_BY_NAME) +
+                    choices=sorted(configs.BY_NAME) + sorted(configs.STREAM_BY_NAME) + sorted(configs.SOCKET_BY_NAME) +
                     sorted(w.name + "__backward" for w in configs.BACKWARD))
     ap.add_argument("--extras", default="all", choices=["all", "none"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -323,6 +356,19 @@ def main() -> int:
                           "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                        "frac": tf / PEAK_BF16_TFLOPS, "traffic": None,
                                        "kernel": "bwd_pre + bwd_dq + bwd_dkdv"}}), flush=True)
+        return 0
+    if args.workload in configs.SOCKET_BY_NAME:
+        sk = configs.SOCKET_BY_NAME[args.workload]
+        ms = time_socket(sk, args.steps, args.warmup, torch, attn)
+        gbs = configs.socket_bytes(sk) / (ms * 1e-3) / 1e9
+        print(json.dumps({"metric": "SOCKET sparse decode HBM GB/s", "value": gbs, "unit": "GB/s", "n_gpus": 1,
+                          "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+                          "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                          "data": "synthetic (seeded generator, workloads/gen.py)",
+                          "config": {"workload": sk.name},
+                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                       "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                                       "kernel": "socket_score + socket_select + decode"}}), flush=True)
         return 0
     if args.workload in configs.STREAM_BY_NAME:
         # one streaming step (append + decode) on its own, for profiling
@@ -392,6 +438,15 @@ def main() -> int:
                 "frac": tf / PEAK_BF16_TFLOPS, "ms": xms, "kernel": "bwd_pre + bwd_dq + bwd_dkdv",
                 "hbm_GBps": configs.backward_bytes(bw) / (xms * 1e-3) / 1e9,
                 "algorithmic_per_step": configs.backward_flops(bw)}
+        for sk in configs.SOCKET_BY_NAME.values():
+            xms = time_socket(sk, max(5, args.steps // 4), max(2, args.warmup // 4), torch, attn)
+            torch.cuda.empty_cache()
+            gbs = configs.socket_bytes(sk) / (xms * 1e-3) / 1e9
+            dense = extras.get(sk.base.name, {}).get("ms")
+            extras[sk.name] = {"value": gbs, "unit": "GB/s", "bound": "hbm", "peak": PEAK_HBM_GBS,
+                               "frac": gbs / PEAK_HBM_GBS, "ms": xms,
+                               "kernel": "socket_prob + socket_score + socket_select + decode (indexed)",
+                               "speedup_vs_dense_decode": (dense / xms) if dense else None}
         for sw in configs.STREAM_BY_NAME.values():
             xms = time_stream(sw, max(5, args.steps // 2), max(2, args.warmup // 2), 3, torch, attn)
             torch.cuda.empty_cache()

@@ -260,6 +260,8 @@ int attn_socket_hash(attn_dtype dt, int N, int Hkv, int S, int E, int tables, in
  * query).  o (N, Hq, 1, E), lse (N, Hq, 1).  selected: NULL, or (N, Hq, top_k)
  * int32 receiving the chosen key rows in ascending order.  1 <= top_k <= S;
  * tau > 0; Hq/Hkv <= 16 and (Hq/Hkv) * tables * 2^bits * 4 bytes <= 64 KB.
+ * num_splits: 0 = choose; a split takes at most 4096 selected keys, so a count
+ * below ceil(top_k / 4096) is raised to it.
  * workspace: attn_socket_decode_workspace_bytes(...) bytes, 256-byte aligned.
  * bf16 only.
  */

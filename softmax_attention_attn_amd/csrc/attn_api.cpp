@@ -253,7 +253,7 @@ int attn_socket_hash(attn_dtype dt, int N, int Hkv, int S, int E, int tables, in
   if (!k || !proj || !buckets || (vnorm && !v)) return fail(ATTN_ERR_NULL, "k, proj and buckets (and v with vnorm) must not be NULL");
   if (!aligned(k, 16) || (v && !aligned(v, 16)) || !aligned(proj, 4) || (vnorm && !aligned(vnorm, 4)))
     return fail(ATTN_ERR_ALIGN, "k and v must be 16-byte aligned, proj and vnorm 4-byte aligned");
-  if (((long long)N * Hkv * S * tables + 255) / 256 > kMaxGrid) return fail(ATTN_ERR_SHAPE, "grid too large");
+  if (((long long)N * Hkv * S + 255) / 256 > kMaxGrid) return fail(ATTN_ERR_SHAPE, "grid too large");
   attn_impl::SocketHashArgs a{k, v, proj, buckets, vnorm, N, Hkv, S, E, tables, bits};
   return hip_status(attn_impl::launch_socket_hash_bf16(a, static_cast<hipStream_t>(stream)), "attn_socket_hash launch");
 }
@@ -270,6 +270,8 @@ SocketLayout socket_layout(int N, int Hq, int S, int E, int tables, int bits, in
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   l.splits = num_splits > 0 ? num_splits : (int)std::min<long long>(std::max<long long>(1, (top_k + 255) / 256),
                                                                      std::max<long long>(1, (2048 + (long long)heads - 1) / std::max<long long>(1, (long long)heads)));
+  // A split's key list is staged in LDS: at most kDecodeIndexMax keys per split.
+  l.splits = std::max(l.splits, (top_k + attn_impl::kDecodeIndexMax - 1) / attn_impl::kDecodeIndexMax);
   l.probs = 0;
   l.scores = up(l.probs + heads * tables * ((size_t)1 << bits) * sizeof(float));
   l.sel = up(l.scores + heads * (size_t)S * sizeof(float));

@@ -28,6 +28,7 @@ namespace {
 constexpr int NT = 256;   // threads per workgroup
 constexpr int NWAVE = 4;
 constexpr int KSTEP = 32; // keys per wave step
+constexpr int kIdxMax = attn_impl::kDecodeIndexMax;  // indexed mode: longest key list of one split
 
 struct DecodeParams {
   const uint16_t* q;
@@ -49,9 +50,9 @@ struct DecodeParams {
 };
 
 // Virtual key index -> key row: registers first, then the visible real keys;
-// in indexed mode the head's list.
-__device__ __forceinline__ int key_row(int vidx, const DecodeParams& p, const int* kidx) {
-  if (kidx) return kidx[vidx];
+// in indexed mode the split's list, staged in LDS from key v0 on.
+__device__ __forceinline__ int key_row(int vidx, const DecodeParams& p, const int* sidx, int v0) {
+  if (sidx) return sidx[vidx - v0];
   return vidx < p.n_reg ? vidx : vidx + p.first_real;
 }
 
@@ -63,7 +64,11 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams p) {
 
   __shared__ float sM[NWAVE][16];
   __shared__ float sL[NWAVE][64];
-  __shared__ __attribute__((aligned(16))) float sO[NWAVE][16][OSTR];
+  // The per-wave outputs of the epilogue share LDS with the indexed mode's key list.
+  constexpr int SO_FLOATS = NWAVE * 16 * OSTR;
+  static_assert(SO_FLOATS >= kIdxMax, "key list must fit in the output staging area");
+  __shared__ __attribute__((aligned(16))) float sOraw[SO_FLOATS];
+  float(*sO)[16][OSTR] = reinterpret_cast<float(*)[16][OSTR]>(sOraw);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -103,6 +108,12 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams p) {
   const int v0 = split * p.chunk;
   const int v1 = min(v0 + p.chunk, p.nkeys);
   const int steps = v1 > v0 ? (v1 - v0 + KSTEP - 1) / KSTEP : 0;
+  int* sidx = nullptr;
+  if (indexed) {  // the split's key rows, read once (chunk <= kIdxMax)
+    sidx = reinterpret_cast<int*>(sOraw);
+    for (int i = tid; i < v1 - v0; i += NT) sidx[i] = kidx[v0 + i];
+    __syncthreads();
+  }
 
   float m = kNegInf, lsum = 0.f;
   f32x4 acc[8];
@@ -117,7 +128,7 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams p) {
     for (int b = 0; b < 2; ++b) {
       const int vk = vb + 16 * b + l16;
       const bool ok = vk < v1;
-      const uint16_t* row = kbase + (size_t)key_row(ok ? vk : v0, p, kidx) * E;
+      const uint16_t* row = kbase + (size_t)key_row(ok ? vk : v0, p, sidx, v0) * E;
 #pragma unroll
       for (int s = 0; s < QS; ++s) kr[b][s] = load16_or_zero(row + 32 * s + 8 * g, ok);
     }
@@ -125,7 +136,7 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams p) {
     for (int i = 0; i < 8; ++i) {
       const int vk = vb + (i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4));
       const bool ok = vk < v1 && l16 < ECH;
-      vr[i] = load16_or_zero(vbase + (size_t)key_row(ok ? vk : v0, p, kidx) * E + 8 * l16, ok);
+      vr[i] = load16_or_zero(vbase + (size_t)key_row(ok ? vk : v0, p, sidx, v0) * E + 8 * l16, ok);
     }
   };
 
@@ -212,6 +223,8 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams p) {
       }
     }
   }
+
+  if (indexed) __syncthreads();  // every wave is done with the key list before sO overwrites it
 
   // Merge the 4 waves.  Lane (l16, g): acc[j][r] is dim 8(4g + r) + j of slot l16.
   if (g == 0) sM[wave][l16] = m;
@@ -382,6 +395,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   const int per = (p.nkeys + a.num_splits - 1) / a.num_splits;
   p.chunk = ((per + KSTEP - 1) / KSTEP) * KSTEP;
   if (p.chunk == 0) p.chunk = KSTEP;
+  if (p.key_index && p.chunk > kIdxMax) return hipErrorInvalidValue;
   const int G = f.Hq / f.Hkv;
   p.qgroups = (G + 15) / 16;
   if (f.rbf) {

@@ -70,6 +70,9 @@ hipError_t launch_backward_bf16(const BwdArgs& a, hipStream_t stream);
 size_t backward_workspace_bytes(int N, int Hq, int L);
 
 // SOCKET soft-LSH sparse decode (socket_bf16.hip).
+// Longest key list one split of an indexed decode takes (it is staged in LDS).
+constexpr int kDecodeIndexMax = 4096;
+
 struct SocketHashArgs {
   const void* k;
   const void* v;

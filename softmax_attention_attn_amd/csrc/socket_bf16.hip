@@ -10,10 +10,10 @@
 //
 // Kernels (all HBM / latency bound; the scores read tables + 4 bytes per key
 // where dense decode reads 4E bytes of K and V):
-//  - socket_hash_kernel: one thread per (key, table); the `bits` projections
-//    are float32 fused multiply-add chains over the key's elements in element
-//    order (the same float32 decision an fp32 reference makes), bit set iff > 0.
-//    Threads of table 0 also write |v|.
+//  - socket_hash_kernel: one thread per key; the `bits` projections of each
+//    table are float32 fused multiply-add chains over the key's elements in
+//    element order (the same float32 decision an fp32 reference makes), bit
+//    set iff > 0; hyperplanes staged in LDS.  Also writes |v|.
 //  - socket_prob_kernel: per query head, y = W q and, per table, the
 //    probability of every bucket: the softmax over the 2^bits sign patterns of
 //    sum_b s_b y_b / tau factorises into prod_b sigmoid(2 s_b y_b / tau).
@@ -24,6 +24,7 @@
 //    3-pass radix select on the float bits (scores are >= 0, so their bit
 //    patterns order like the values), then an ordered compaction: every key
 //    above the threshold and the lowest-index keys equal to it, ascending.
+//    Reads the head's scores four times in all.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -34,46 +35,80 @@ namespace {
 constexpr int kMaxProj = 512;  // tables * bits
 constexpr int SEL_T = 1024;    // threads of the selection workgroup
 
-template <int E>
+// Hashing: one thread per key, its row in registers.  The hyperplanes of up
+// to HASH_TG tables sit in LDS as [table][element][BP] (BP = bits padded to 4
+// or 8, padding weights zero), so every element's weights of all the table's
+// hyperplanes are one broadcast LDS read.  Each projection is a float32 fused
+// multiply-add chain over the elements in order, starting from zero.
+constexpr int HASH_LDS = 32 * 1024;
+
+template <int E, int BP>
 __global__ __launch_bounds__(256) void socket_hash_kernel(attn_impl::SocketHashArgs a) {
-  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  extern __shared__ float sW[];
+  constexpr int TG = HASH_LDS / (E * BP * 4);  // tables per LDS stage
+  typedef float wvec __attribute__((ext_vector_type(BP)));
   const long long nkeys = (long long)a.N * a.Hkv * a.S;
-  if (gid >= nkeys * a.tables) return;
-  const long long j = gid / a.tables;
-  const int t = (int)(gid % a.tables);
-  const uint16_t* krow = static_cast<const uint16_t*>(a.k) + (size_t)j * E;
+  const long long j = (long long)blockIdx.x * 256 + threadIdx.x;
+  const bool ok = j < nkeys;
   uint32_t kw[E / 2];
+  {
+    const uint16_t* krow = static_cast<const uint16_t*>(a.k) + (size_t)(ok ? j : 0) * E;
 #pragma unroll
-  for (int c = 0; c < E / 8; ++c) {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(krow + 8 * c);
+    for (int c = 0; c < E / 8; ++c) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(krow + 8 * c);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) kw[4 * c + w] = x[w];
-  }
-  float x[8];
-#pragma unroll
-  for (int b = 0; b < 8; ++b) x[b] = 0.f;
-  const float* w0 = a.proj + (size_t)t * a.bits * E;  // this table's hyperplanes (cached)
-  for (int e2 = 0; e2 < E / 2; ++e2) {
-    const float k0 = bf16_lo(kw[e2]), k1 = bf16_hi(kw[e2]);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      if (b < a.bits) {
-        x[b] = __builtin_fmaf(k0, w0[b * E + 2 * e2], x[b]);
-        x[b] = __builtin_fmaf(k1, w0[b * E + 2 * e2 + 1], x[b]);
-      }
+      for (int w = 0; w < 4; ++w) kw[4 * c + w] = x[w];
     }
   }
-  uint32_t code = 0;
-#pragma unroll
-  for (int b = 0; b < 8; ++b)
-    if (b < a.bits && x[b] > 0.f) code |= 1u << b;
-  a.buckets[gid] = (uint8_t)code;
-  if (t == 0 && a.vnorm) {
+  if (ok && a.vnorm) {
     const uint16_t* vrow = static_cast<const uint16_t*>(a.v) + (size_t)j * E;
     float ss = 0.f;
 #pragma unroll
     for (int c = 0; c < E / 8; ++c) ss += sumsq8(*reinterpret_cast<const u32x4*>(vrow + 8 * c));
     a.vnorm[j] = sqrtf(ss);
+  }
+  const bool words = (a.tables & 3) == 0 && (reinterpret_cast<uintptr_t>(a.buckets) & 3) == 0;
+  uint8_t* dst = a.buckets + (size_t)(ok ? j : 0) * a.tables;
+  uint32_t word = 0;
+  for (int t0 = 0; t0 < a.tables; t0 += TG) {
+    const int tn = min(TG, a.tables - t0);
+    __syncthreads();  // the previous stage's weights are no longer read
+    for (int i = threadIdx.x; i < tn * E * BP; i += 256) {
+      const int tt = i / (E * BP), r = i % (E * BP), e = r / BP, b = r % BP;
+      sW[i] = b < a.bits ? a.proj[((size_t)(t0 + tt) * a.bits + b) * E + e] : 0.f;
+    }
+    __syncthreads();
+    for (int tt = 0; tt < tn; ++tt) {
+      const float* w = sW + tt * E * BP;
+      float x[BP];
+#pragma unroll
+      for (int b = 0; b < BP; ++b) x[b] = 0.f;
+#pragma unroll
+      for (int e2 = 0; e2 < E / 2; ++e2) {
+        const float k0 = bf16_lo(kw[e2]), k1 = bf16_hi(kw[e2]);
+        const wvec w0 = *reinterpret_cast<const wvec*>(w + (2 * e2) * BP);
+        const wvec w1 = *reinterpret_cast<const wvec*>(w + (2 * e2 + 1) * BP);
+#pragma unroll
+        for (int b = 0; b < BP; ++b) {
+          x[b] = __builtin_fmaf(k0, w0[b], x[b]);
+          x[b] = __builtin_fmaf(k1, w1[b], x[b]);
+        }
+      }
+      uint32_t code = 0;
+#pragma unroll
+      for (int b = 0; b < BP; ++b)
+        if (b < a.bits && x[b] > 0.f) code |= 1u << b;
+      const int t = t0 + tt;
+      if (words) {
+        word |= code << (8 * (t & 3));
+        if ((t & 3) == 3) {
+          if (ok) *reinterpret_cast<uint32_t*>(dst + (t - 3)) = word;
+          word = 0;
+        }
+      } else if (ok) {
+        dst[t] = (uint8_t)code;
+      }
+    }
   }
 }
 
@@ -109,33 +144,201 @@ __global__ __launch_bounds__(256) void socket_prob_kernel(attn_impl::SocketSelec
   }
 }
 
+// Per (key, table) the bucket probabilities of the P query heads packed
+// together (P = 4, 2 or 1, a divisor of the group size) are one LDS read.
+template <int P>
+__device__ __forceinline__ void score_lookup(const float* __restrict__ sP, int row, int ngrp, int stride,
+                                             float (&acc)[16]) {
+#pragma unroll
+  for (int g = 0; g < 16 / P; ++g) {
+    if (g < ngrp) {
+      const float* e = sP + (size_t)(g * stride + row) * P;
+      if constexpr (P == 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(e);
+        acc[4 * g] += x[0];
+        acc[4 * g + 1] += x[1];
+        acc[4 * g + 2] += x[2];
+        acc[4 * g + 3] += x[3];
+      } else if constexpr (P == 2) {
+        const float2 x = *reinterpret_cast<const float2*>(e);
+        acc[2 * g] += x.x;
+        acc[2 * g + 1] += x.y;
+      } else {
+        acc[g] += e[0];
+      }
+    }
+  }
+}
+
+constexpr int SCORE_KPT = 4;  // keys per thread of the score kernel
+
+// Generic scoring (any group size, table count and alignment): one workgroup
+// scores 256 * SCORE_KPT keys of one (batch, kv head) for all G query heads of
+// its group.  LDS holds the group's bucket probabilities as
+// [G/P][tables][2^bits][P].
+template <int P>
 __global__ __launch_bounds__(256) void socket_score_kernel(attn_impl::SocketSelectArgs a) {
-  extern __shared__ float sP[];  // [G][tables][2^bits]
+  extern __shared__ float sP[];
   const int G = a.Hq / a.Hkv;
-  const int nk = blockIdx.y;     // n * Hkv + kv head
+  const int ngrp = G / P;
+  const int nk = blockIdx.y;  // n * Hkv + kv head
   const int n = nk / a.Hkv, kh = nk % a.Hkv;
   const int nb = 1 << a.bits;
   const int per = a.tables * nb;
   const float* src = a.probs + ((size_t)n * a.Hq + (size_t)kh * G) * per;
-  for (int i = threadIdx.x; i < G * per; i += 256) sP[i] = src[i];
+  for (int i = threadIdx.x; i < G * per; i += 256) {
+    const int g = i / per, r = i % per;  // source head g, row (table, code)
+    sP[((g / P) * per + r) * P + g % P] = src[i];
+  }
   __syncthreads();
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= a.S) return;
-  const size_t key = (size_t)nk * a.S + j;
-  const uint8_t* code = a.buckets + key * a.tables;
-  const float nv = a.vnorm[key];
-  float acc[16];
+  const uintptr_t base = reinterpret_cast<uintptr_t>(a.buckets);
+  const size_t row0 = (size_t)n * a.Hq + (size_t)kh * G;
+  for (int kk = 0; kk < SCORE_KPT; ++kk) {
+    const int j = (blockIdx.x * SCORE_KPT + kk) * 256 + threadIdx.x;
+    if (j >= a.S) break;
+    const size_t key = (size_t)nk * a.S + j;
+    const uint8_t* code = a.buckets + key * a.tables;
+    float acc[16];
 #pragma unroll
-  for (int g = 0; g < 16; ++g) acc[g] = 0.f;
-  for (int t = 0; t < a.tables; ++t) {
-    const int c = code[t];
+    for (int g = 0; g < 16; ++g) acc[g] = 0.f;
+    if ((a.tables & 3) == 0 && (base & 3) == 0) {
+      for (int t0 = 0; t0 < a.tables; t0 += 4) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(code + t0);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) score_lookup<P>(sP, (t0 + b) * nb + ((w >> (8 * b)) & 0xffu), ngrp, per, acc);
+      }
+    } else {
+      for (int t = 0; t < a.tables; ++t) score_lookup<P>(sP, t * nb + code[t], ngrp, per, acc);
+    }
+    const float nv = a.vnorm[key];
 #pragma unroll
     for (int g = 0; g < 16; ++g)
-      if (g < G) acc[g] += sP[(g * a.tables + t) * nb + c];
+      if (g < G) a.scores[(row0 + g) * a.S + j] = nv * acc[g];
   }
+}
+
+template <int P>
+__device__ __forceinline__ void lookup_load(const float* e, float (&x)[P]) {
+  if constexpr (P == 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(e);
+    x[0] = v[0];
+    x[1] = v[1];
+    x[2] = v[2];
+    x[3] = v[3];
+  } else if constexpr (P == 2) {
+    const float2 v = *reinterpret_cast<const float2*>(e);
+    x[0] = v.x;
+    x[1] = v.y;
+  } else {
+    x[0] = e[0];
+  }
+}
+
+// Scoring for the common shapes: group size GT in {1, 2, 4, 8, 16}, tables a
+// multiple of 16 (at most 64), 16-byte aligned codes; NB = 2^bits when fixed
+// at build time (constant LDS offsets), else 0.  Every code and norm of the
+// thread's keys is loaded first; then per 16-table chunk, key and packed head
+// group, 16 independent LDS reads are issued before they are summed.
+template <int GT, int NB>
+__global__ __launch_bounds__(256) void socket_score_fast(attn_impl::SocketSelectArgs a) {
+  constexpr int P = GT % 4 == 0 ? 4 : (GT % 2 == 0 ? 2 : 1);
+  constexpr int NG = GT / P;
+  constexpr int KPT = GT <= 4 ? 4 : 2;
+  extern __shared__ float sP[];
+  const int nk = blockIdx.y;  // n * Hkv + kv head
+  const int n = nk / a.Hkv, kh = nk % a.Hkv;
+  const int nb = NB ? NB : (1 << a.bits);
+  const int per = a.tables * nb;
+  const float* src = a.probs + ((size_t)n * a.Hq + (size_t)kh * GT) * per;
+  for (int i = threadIdx.x; i < GT * per; i += 256) {
+    const int g = i / per, r = i % per;
+    sP[((g / P) * per + r) * P + g % P] = src[i];
+  }
+  __syncthreads();
+  const int nch = a.tables / 16;
+  u32x4 w[KPT][4];
+  float nv[KPT];
 #pragma unroll
-  for (int g = 0; g < 16; ++g)
-    if (g < G) a.scores[((size_t)n * a.Hq + (size_t)kh * G + g) * a.S + j] = nv * acc[g];
+  for (int kk = 0; kk < KPT; ++kk) {
+    const int j = (blockIdx.x * KPT + kk) * 256 + threadIdx.x;
+    const bool ok = j < a.S;
+    const size_t key = (size_t)nk * a.S + (ok ? j : 0);
+    const u32x4* c16 = reinterpret_cast<const u32x4*>(a.buckets + key * a.tables);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w[kk][c] = (ok && c < nch) ? c16[c] : u32x4{0u, 0u, 0u, 0u};
+    nv[kk] = ok ? a.vnorm[key] : 0.f;
+  }
+  float acc[KPT][GT];
+#pragma unroll
+  for (int kk = 0; kk < KPT; ++kk)
+#pragma unroll
+    for (int g = 0; g < GT; ++g) acc[kk][g] = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (c < nch) {
+#pragma unroll
+      for (int kk = 0; kk < KPT; ++kk) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          float x[16][P];
+#pragma unroll
+          for (int b = 0; b < 16; ++b) {
+            const int code = (int)((w[kk][c][b / 4] >> (8 * (b % 4))) & 0xffu);
+            lookup_load<P>(sP + ((size_t)g * per + (16 * c + b) * nb + code) * P, x[b]);
+          }
+#pragma unroll
+          for (int b = 0; b < 16; ++b)
+#pragma unroll
+            for (int q = 0; q < P; ++q) acc[kk][g * P + q] += x[b][q];
+        }
+      }
+    }
+  }
+  const size_t row0 = (size_t)n * a.Hq + (size_t)kh * GT;
+#pragma unroll
+  for (int kk = 0; kk < KPT; ++kk) {
+    const int j = (blockIdx.x * KPT + kk) * 256 + threadIdx.x;
+    if (j < a.S) {
+#pragma unroll
+      for (int g = 0; g < GT; ++g) a.scores[(row0 + g) * a.S + j] = nv[kk] * acc[kk][g];
+    }
+  }
+}
+
+template <int GT>
+hipError_t launch_score_fast(const attn_impl::SocketSelectArgs& a, size_t lds, hipStream_t stream) {
+  constexpr int KPT = GT <= 4 ? 4 : 2;
+  const dim3 grid((unsigned)((a.S + 256 * KPT - 1) / (256 * KPT)), (unsigned)(a.N * a.Hkv));
+  if (a.bits == 4)
+    hipLaunchKernelGGL((socket_score_fast<GT, 16>), grid, dim3(256), lds, stream, a);
+  else
+    hipLaunchKernelGGL((socket_score_fast<GT, 0>), grid, dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+// ---- exact top-k selection -------------------------------------------------
+//
+// One workgroup of SEL_T threads per query head.  Wave w owns the contiguous
+// key segment [w * seg, (w + 1) * seg) and walks it in steps of 64 keys, so
+// (wave, step, lane) is ascending key order.  Three radix passes over the
+// score bit patterns (12 + 12 + 8 bits; scores are >= 0, so bit patterns order
+// like values) find the k-th largest pattern `thr` and how many keys equal to
+// it are taken; the last pass keeps one histogram per wave, which gives every
+// wave its count of keys above `thr` and equal to it without another read.
+// The write pass then places keys in ascending order using ballots.
+
+constexpr int SEL_WAVES = SEL_T / 64;
+static_assert(SEL_WAVES * 256 >= 4096, "pass-3 histograms must cover the pass-1 bins' storage");
+constexpr int SEL_U = 8;  // loads in flight per lane
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
 }
 
 // Exclusive prefix sum over the workgroup of one int per thread (LDS
@@ -155,69 +358,171 @@ __device__ __forceinline__ int block_exclusive_scan(int* buf, int v) {
   return excl;
 }
 
-__global__ __launch_bounds__(SEL_T) void socket_select_kernel(attn_impl::SocketSelectArgs a) {
-  __shared__ int hist[2048];
-  __shared__ int scan[SEL_T];
-  __shared__ uint32_t sPrefix, sMask;
-  __shared__ int sRemain;
-  const int nh = blockIdx.x;
+// Finds, among `nbins` bins whose counts are in hist, the bin holding the
+// `remain`-th largest key counting down from the top bin; sets *bin_out and
+// *remain_out (the rank inside that bin).  All threads call it.
+__device__ __forceinline__ void find_bin(const int* hist, int nbins, int remain, int* scan, int* bin_out,
+                                         int* remain_out) {
   const int tid = threadIdx.x;
-  const uint32_t* sc = reinterpret_cast<const uint32_t*>(a.scores) + (size_t)nh * a.S;
-  int* out = a.selected + (size_t)nh * a.top_k;
-
-  // Radix select of the top_k-th largest bit pattern: 11 + 11 + 10 bits.
-  if (tid == 0) {
-    sPrefix = 0;
-    sMask = 0;
-    sRemain = a.top_k;
+  const int bpt = (nbins + SEL_T - 1) / SEL_T;  // bins per thread, highest bins to thread 0
+  const int hi = nbins - 1 - tid * bpt;
+  int local = 0;
+  for (int i = 0; i < bpt; ++i)
+    if (hi - i >= 0) local += hist[hi - i];
+  const int above = block_exclusive_scan(scan, local);
+  if (above < remain && above + local >= remain) {
+    int r = remain - above, b = hi;
+    for (int i = 0; i < bpt; ++i, --b) {
+      if (hist[b] >= r) break;
+      r -= hist[b];
+    }
+    *bin_out = b;
+    *remain_out = r;
   }
+  __syncthreads();
+}
+
+// Four consecutive scores from key j on (zero past s1); 16-byte loads where
+// the row allows them.
+__device__ __forceinline__ u32x4 load_scores4(const uint32_t* sc, int j, int s1, bool vec) {
+  if (vec && j + 3 < s1) return *reinterpret_cast<const u32x4*>(sc + j);
+  u32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = j + e < s1 ? sc[j + e] : 0u;
+  return r;
+}
+
+// Exclusive prefix over the wave's lanes of x in [0, 7], and the wave total.
+__device__ __forceinline__ int wave_prefix3(int x, int* total) {
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int b = 0; b < 3; ++b) {
+    const uint64_t m = __ballot((x >> b) & 1);
+    pre += lanes_below(m) << b;
+    tot += __popcll(m) << b;
+  }
+  *total = tot;
+  return pre;
+}
+
+__global__ __launch_bounds__(SEL_T) void socket_select_kernel(attn_impl::SocketSelectArgs a) {
+  __shared__ int hist[SEL_WAVES * 256 + 256];  // passes 1-2: 4096 bins; pass 3: [SEL_WAVES][256] + their sum
+  __shared__ int scan[SEL_T];
+  __shared__ int sBin, sRemain;
+  __shared__ int sGt[SEL_WAVES], sEq[SEL_WAVES], sPos[SEL_WAVES], sTake[SEL_WAVES];
+  const int nh = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const uint32_t* sc = reinterpret_cast<const uint32_t*>(a.scores) + (size_t)nh * a.S;
+  const bool vec = (a.S & 3) == 0;  // rows start 16-byte aligned
+  int* out = a.selected + (size_t)nh * a.top_k;
+  // Wave segments are whole steps of 256 keys (64 lanes x 4 consecutive keys).
+  const int seg = (a.S + SEL_WAVES * 256 - 1) / (SEL_WAVES * 256) * 256;
+  const int s0 = min(a.S, wave * seg), s1 = min(a.S, s0 + seg);
+
+  uint32_t prefix = 0, mask = 0;
+  int remain = a.top_k;
+  int above = 0;  // this lane's keys whose top 24 bits exceed the pass-3 prefix
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
-    const int sh = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int nbins = pass == 2 ? 1024 : 2048;
-    for (int i = tid; i < nbins; i += SEL_T) hist[i] = 0;
+    const int sh = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
+    const int nbins = pass == 2 ? 256 : 4096;
+    const int hsize = pass == 2 ? SEL_WAVES * 256 : 4096;
+    int* h = pass == 2 ? hist + wave * 256 : hist;
+    for (int i = tid; i < hsize; i += SEL_T) hist[i] = 0;
     __syncthreads();
-    const uint32_t prefix = sPrefix, mask = sMask;
-    for (int j = tid; j < a.S; j += SEL_T) {
-      const uint32_t v = sc[j];
-      if ((v & mask) == prefix) atomicAdd(&hist[(v >> sh) & (nbins - 1)], 1);
-    }
-    __syncthreads();
-    if (tid == 0) {  // walk the bins from the top until `remain` keys are covered
-      int remain = sRemain, bin = nbins - 1;
-      for (; bin > 0; --bin) {
-        if (hist[bin] >= remain) break;
-        remain -= hist[bin];
+    for (int j0 = s0; j0 < s1; j0 += 256 * SEL_U) {
+      u32x4 v[SEL_U];
+#pragma unroll
+      for (int u = 0; u < SEL_U; ++u) v[u] = load_scores4(sc, j0 + u * 256 + lane * 4, s1, vec);
+#pragma unroll
+      for (int u = 0; u < SEL_U; ++u) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (j0 + u * 256 + lane * 4 + e < s1) {
+            const uint32_t x = v[u][e];
+            if ((x & mask) == prefix) atomicAdd(&h[(x >> sh) & (nbins - 1)], 1);
+            if (pass == 2) above += (x >> 8) > (prefix >> 8);
+          }
+        }
       }
-      sPrefix = prefix | ((uint32_t)bin << sh);
-      sMask = mask | ((uint32_t)(nbins - 1) << sh);
-      sRemain = remain;
     }
     __syncthreads();
+    if (pass == 2) {  // fold the per-wave histograms into hist[SEL_WAVES * 256 ...]
+      if (tid < 256) {
+        int t = 0;
+        for (int w = 0; w < SEL_WAVES; ++w) t += hist[w * 256 + tid];
+        hist[SEL_WAVES * 256 + tid] = t;
+      }
+      __syncthreads();
+    }
+    find_bin(pass == 2 ? hist + SEL_WAVES * 256 : hist, nbins, remain, scan, &sBin, &sRemain);
+    prefix |= (uint32_t)sBin << sh;
+    mask |= (uint32_t)(nbins - 1) << sh;
+    remain = sRemain;
   }
-  const uint32_t thr = sPrefix;  // the top_k-th largest value
-  const int need_eq = sRemain;   // keys equal to it that are taken (lowest indices)
+  const uint32_t thr = prefix;  // the top_k-th largest bit pattern
+  const int need_eq = remain;   // keys equal to it that are taken, lowest indices first
 
-  // Ordered compaction over contiguous chunks of keys.
-  const int chunk = (a.S + SEL_T - 1) / SEL_T;
-  const int j0 = min(a.S, tid * chunk), j1 = min(a.S, j0 + chunk);
-  int gt = 0, eq = 0;
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t v = sc[j];
-    gt += v > thr;
-    eq += v == thr;
+  // Per-wave counts: above the 24-bit prefix, plus the wave's own last-pass bins.
+  {
+    const int bin = (int)(thr & 0xffu);
+    int gt = above;
+    for (int b = lane; b < 256; b += 64) gt += b > bin ? hist[wave * 256 + b] : 0;
+    gt = wave_sum_int(gt);
+    if (lane == 0) {
+      sGt[wave] = gt;
+      sEq[wave] = hist[wave * 256 + bin];
+    }
   }
-  const int eq_before = block_exclusive_scan(scan, eq);
-  const int take_eq = max(0, min(eq, need_eq - eq_before));
-  int pos = block_exclusive_scan(scan, gt + take_eq);
-  int eq_seen = 0;
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t v = sc[j];
-    if (v > thr) {
-      out[pos++] = j;
-    } else if (v == thr) {
-      if (eq_seen < take_eq) out[pos++] = j;
-      ++eq_seen;
+  __syncthreads();
+  if (tid == 0) {
+    int eq_before = 0, pos = 0;
+    for (int w = 0; w < SEL_WAVES; ++w) {
+      const int take = max(0, min(sEq[w], need_eq - eq_before));
+      eq_before += sEq[w];
+      sPos[w] = pos;
+      sTake[w] = take;
+      pos += sGt[w] + take;
+    }
+  }
+  __syncthreads();
+
+  // Ordered write: ascending key index = (wave, step, lane, element).
+  const int take_eq = sTake[wave];
+  const int quota = sGt[wave] + take_eq;
+  int pos = sPos[wave], written = 0, eq_seen = 0;
+  for (int j0 = s0; j0 < s1 && written < quota; j0 += 256 * SEL_U) {
+    u32x4 v[SEL_U];
+#pragma unroll
+    for (int u = 0; u < SEL_U; ++u) v[u] = load_scores4(sc, j0 + u * 256 + lane * 4, s1, vec);
+#pragma unroll
+    for (int u = 0; u < SEL_U; ++u) {
+      const int jb = j0 + u * 256 + lane * 4;
+      int eqm = 0, neq = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool is_eq = jb + e < s1 && v[u][e] == thr;
+        eqm |= (int)is_eq << e;
+        neq += is_eq;
+      }
+      int eq_tot;
+      const int eq_pre = eq_seen + wave_prefix3(neq, &eq_tot);
+      int tkm = 0, ntk = 0, r = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool is_eq = (eqm >> e) & 1;
+        const bool take = (jb + e < s1 && v[u][e] > thr) || (is_eq && eq_pre + r < take_eq);
+        r += is_eq;
+        tkm |= (int)take << e;
+        ntk += take;
+      }
+      int tk_tot;
+      int p = pos + written + wave_prefix3(ntk, &tk_tot);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((tkm >> e) & 1) out[p++] = jb + e;
+      written += tk_tot;
+      eq_seen += eq_tot;
     }
   }
 }
@@ -227,13 +532,20 @@ __global__ __launch_bounds__(SEL_T) void socket_select_kernel(attn_impl::SocketS
 namespace attn_impl {
 
 hipError_t launch_socket_hash_bf16(const SocketHashArgs& a, hipStream_t stream) {
-  const long long total = (long long)a.N * a.Hkv * a.S * a.tables;
-  if (total == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((total + 255) / 256);
-  if (a.E == 128)
-    hipLaunchKernelGGL((socket_hash_kernel<128>), dim3(blocks), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((socket_hash_kernel<64>), dim3(blocks), dim3(256), 0, stream, a);
+  const long long keys = (long long)a.N * a.Hkv * a.S;
+  if (keys == 0) return hipSuccess;
+  const dim3 grid((unsigned)((keys + 255) / 256));
+  if (a.E == 128) {
+    if (a.bits <= 4)
+      hipLaunchKernelGGL((socket_hash_kernel<128, 4>), grid, dim3(256), HASH_LDS, stream, a);
+    else
+      hipLaunchKernelGGL((socket_hash_kernel<128, 8>), grid, dim3(256), HASH_LDS, stream, a);
+  } else {
+    if (a.bits <= 4)
+      hipLaunchKernelGGL((socket_hash_kernel<64, 4>), grid, dim3(256), HASH_LDS, stream, a);
+    else
+      hipLaunchKernelGGL((socket_hash_kernel<64, 8>), grid, dim3(256), HASH_LDS, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -245,9 +557,25 @@ hipError_t launch_socket_select_bf16(const SocketSelectArgs& a, hipStream_t stre
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int G = a.Hq / a.Hkv;
-  const size_t lds = (size_t)G * a.tables * (1u << a.bits) * sizeof(float);
-  hipLaunchKernelGGL(socket_score_kernel, dim3((unsigned)((a.S + 255) / 256), (unsigned)(a.N * a.Hkv)), dim3(256),
-                     lds, stream, a);
+  const size_t lds = socket_lds_bytes(G, a.tables, a.bits);
+  const bool fast = (a.tables & 15) == 0 && (reinterpret_cast<uintptr_t>(a.buckets) & 15) == 0;
+  if (fast && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16)) {
+    e = G == 1 ? launch_score_fast<1>(a, lds, stream)
+      : G == 2 ? launch_score_fast<2>(a, lds, stream)
+      : G == 4 ? launch_score_fast<4>(a, lds, stream)
+      : G == 8 ? launch_score_fast<8>(a, lds, stream)
+               : launch_score_fast<16>(a, lds, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(socket_select_kernel, dim3((unsigned)(a.N * a.Hq)), dim3(SEL_T), 0, stream, a);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)((a.S + 256 * SCORE_KPT - 1) / (256 * SCORE_KPT)), (unsigned)(a.N * a.Hkv));
+  if (G % 4 == 0)
+    hipLaunchKernelGGL(socket_score_kernel<4>, grid, dim3(256), lds, stream, a);
+  else if (G % 2 == 0)
+    hipLaunchKernelGGL(socket_score_kernel<2>, grid, dim3(256), lds, stream, a);
+  else
+    hipLaunchKernelGGL(socket_score_kernel<1>, grid, dim3(256), lds, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(socket_select_kernel, dim3((unsigned)(a.N * a.Hq)), dim3(SEL_T), 0, stream, a);

@@ -182,3 +182,32 @@ def backward_bytes(w: Workload) -> float:
     qo = w.N * w.Hq * w.L * w.E * esz
     kv = w.N * w.Hkv * w.S * w.E * esz
     return float(3 * qo + 2 * kv + qo + 2 * kv + w.N * w.Hq * w.L * 4)
+
+
+@dataclass(frozen=True)
+class SocketWorkload:
+    """One SOCKET sparse decode step ("기술 요약: SOCKET" page, method): score every key of the
+    cache by soft collisions, select top_k per query head, attend to them exactly.  The
+    cache and queries are those of `base` (a decode workload); hashing is prefill work and
+    is not part of the step."""
+    name: str
+    base: Workload
+    tables: int
+    bits: int
+    tau: float
+    top_k: int
+
+
+# The long-context decode shape at about 33x sparsity (the page's setting), 64 tables of
+# 4-bit codes (64 bytes of codes + a 4-byte norm per key: ~13% of the K and V bytes).
+SOCKET1 = SocketWorkload("socket_decode_sink_bf16_8x32to8x131072x128_k3972", C5, 64, 4, 4.0, 3972)
+SOCKET_BY_NAME = {SOCKET1.name: SOCKET1}
+
+
+def socket_bytes(sw: SocketWorkload) -> float:
+    """Per step: every key's codes and value norm read once per kv head, the selected K and V
+    rows read once per query head, q read and o / lse written."""
+    w = sw.base
+    keys = w.N * w.Hkv * w.S
+    return float(keys * (sw.tables + 4) + 2 * w.N * w.Hq * sw.top_k * w.E * 2 + 2 * w.N * w.Hq * w.E * 2 +
+                 w.N * w.Hq * 4)
