@@ -20,11 +20,12 @@
 //  - socket_score_kernel: one thread per key of a (batch, kv head); the bucket
 //    probabilities of the group's query heads sit in LDS, so the key's codes
 //    are read once for all of them.
-//  - socket_select_kernel: one workgroup per query head; exact top_k by a
-//    3-pass radix select on the float bits (scores are >= 0, so their bit
-//    patterns order like the values), then an ordered compaction: every key
-//    above the threshold and the lowest-index keys equal to it, ascending.
-//    Reads the head's scores four times in all.
+//  - socket_select_kernel: one workgroup per query head; exact top_k on the
+//    float bits (scores are >= 0, so their bit patterns order like the
+//    values): a sampled bracket narrows the threshold to a few thousand
+//    candidates in one read of the scores (else a 3-pass radix select), then
+//    an ordered compaction writes every key above the threshold and the
+//    lowest-index keys equal to it, ascending.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -217,6 +218,10 @@ __global__ __launch_bounds__(256) void socket_score_kernel(attn_impl::SocketSele
   }
 }
 
+// Ordering key of a score: its bit pattern without the sign bit (scores are
+// >= 0, so this orders like the values; a NaN orders above every number).
+__device__ __forceinline__ uint32_t score_key(uint32_t bits) { return bits & 0x7fffffffu; }
+
 template <int P>
 __device__ __forceinline__ void lookup_load(const float* e, float (&x)[P]) {
   if constexpr (P == 4) {
@@ -236,14 +241,19 @@ __device__ __forceinline__ void lookup_load(const float* e, float (&x)[P]) {
 
 // Scoring for the common shapes: group size GT in {1, 2, 4, 8, 16}, tables a
 // multiple of 16 (at most 64), 16-byte aligned codes; NB = 2^bits when fixed
-// at build time (constant LDS offsets), else 0.  Every code and norm of the
-// thread's keys is loaded first; then per 16-table chunk, key and packed head
-// group, 16 independent LDS reads are issued before they are summed.
+// at build time (constant LDS offsets), else 0.  A workgroup stages the
+// group's probabilities once and scores FAST_ROUNDS * 256 * FAST_KPT keys; in
+// each round every code and norm of the thread's keys is loaded first, then per
+// 16-table chunk, key and packed head group 16 independent LDS reads are
+// issued before they are summed.
+constexpr int FAST_KPT = 2;   // keys per thread per round
+constexpr int FAST_ROUNDS = 4;  // rounds per workgroup (amortise the LDS staging)
+
 template <int GT, int NB>
 __global__ __launch_bounds__(256) void socket_score_fast(attn_impl::SocketSelectArgs a) {
   constexpr int P = GT % 4 == 0 ? 4 : (GT % 2 == 0 ? 2 : 1);
   constexpr int NG = GT / P;
-  constexpr int KPT = GT <= 4 ? 4 : 2;
+  constexpr int KPT = FAST_KPT;
   extern __shared__ float sP[];
   const int nk = blockIdx.y;  // n * Hkv + kv head
   const int n = nk / a.Hkv, kh = nk % a.Hkv;
@@ -256,58 +266,62 @@ __global__ __launch_bounds__(256) void socket_score_fast(attn_impl::SocketSelect
   }
   __syncthreads();
   const int nch = a.tables / 16;
-  u32x4 w[KPT][4];
-  float nv[KPT];
+  const size_t row0 = (size_t)n * a.Hq + (size_t)kh * GT;  // first query head of the group
+  for (int it = 0; it < FAST_ROUNDS; ++it) {
+    const int blk = blockIdx.x * FAST_ROUNDS + it;
+    if (blk * KPT * 256 >= a.S) break;
+    u32x4 w[KPT][4];
+    float nv[KPT];
 #pragma unroll
-  for (int kk = 0; kk < KPT; ++kk) {
-    const int j = (blockIdx.x * KPT + kk) * 256 + threadIdx.x;
-    const bool ok = j < a.S;
-    const size_t key = (size_t)nk * a.S + (ok ? j : 0);
-    const u32x4* c16 = reinterpret_cast<const u32x4*>(a.buckets + key * a.tables);
+    for (int kk = 0; kk < KPT; ++kk) {
+      const int j = (blk * KPT + kk) * 256 + threadIdx.x;
+      const bool ok = j < a.S;
+      const size_t key = (size_t)nk * a.S + (ok ? j : 0);
+      const u32x4* c16 = reinterpret_cast<const u32x4*>(a.buckets + key * a.tables);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) w[kk][c] = (ok && c < nch) ? c16[c] : u32x4{0u, 0u, 0u, 0u};
-    nv[kk] = ok ? a.vnorm[key] : 0.f;
-  }
-  float acc[KPT][GT];
+      for (int c = 0; c < 4; ++c) w[kk][c] = (ok && c < nch) ? c16[c] : u32x4{0u, 0u, 0u, 0u};
+      nv[kk] = ok ? a.vnorm[key] : 0.f;
+    }
+    float acc[KPT][GT];
 #pragma unroll
-  for (int kk = 0; kk < KPT; ++kk)
+    for (int kk = 0; kk < KPT; ++kk)
 #pragma unroll
-    for (int g = 0; g < GT; ++g) acc[kk][g] = 0.f;
+      for (int g = 0; g < GT; ++g) acc[kk][g] = 0.f;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    if (c < nch) {
+    for (int c = 0; c < 4; ++c) {
+      if (c < nch) {
 #pragma unroll
-      for (int kk = 0; kk < KPT; ++kk) {
+        for (int kk = 0; kk < KPT; ++kk) {
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          float x[16][P];
+          for (int g = 0; g < NG; ++g) {
+            float x[16][P];
 #pragma unroll
-          for (int b = 0; b < 16; ++b) {
-            const int code = (int)((w[kk][c][b / 4] >> (8 * (b % 4))) & 0xffu);
-            lookup_load<P>(sP + ((size_t)g * per + (16 * c + b) * nb + code) * P, x[b]);
+            for (int b = 0; b < 16; ++b) {
+              const int code = (int)((w[kk][c][b / 4] >> (8 * (b % 4))) & 0xffu);
+              lookup_load<P>(sP + ((size_t)g * per + (16 * c + b) * nb + code) * P, x[b]);
+            }
+#pragma unroll
+            for (int b = 0; b < 16; ++b)
+#pragma unroll
+              for (int q = 0; q < P; ++q) acc[kk][g * P + q] += x[b][q];
           }
-#pragma unroll
-          for (int b = 0; b < 16; ++b)
-#pragma unroll
-            for (int q = 0; q < P; ++q) acc[kk][g * P + q] += x[b][q];
         }
       }
     }
-  }
-  const size_t row0 = (size_t)n * a.Hq + (size_t)kh * GT;
 #pragma unroll
-  for (int kk = 0; kk < KPT; ++kk) {
-    const int j = (blockIdx.x * KPT + kk) * 256 + threadIdx.x;
-    if (j < a.S) {
+    for (int kk = 0; kk < KPT; ++kk) {
+      const int j = (blk * KPT + kk) * 256 + threadIdx.x;
+      if (j < a.S) {
 #pragma unroll
-      for (int g = 0; g < GT; ++g) a.scores[(row0 + g) * a.S + j] = nv[kk] * acc[kk][g];
+        for (int g = 0; g < GT; ++g) a.scores[(row0 + g) * a.S + j] = nv[kk] * acc[kk][g];
+      }
     }
   }
 }
 
 template <int GT>
 hipError_t launch_score_fast(const attn_impl::SocketSelectArgs& a, size_t lds, hipStream_t stream) {
-  constexpr int KPT = GT <= 4 ? 4 : 2;
+  constexpr int KPT = FAST_KPT * FAST_ROUNDS;
   const dim3 grid((unsigned)((a.S + 256 * KPT - 1) / (256 * KPT)), (unsigned)(a.N * a.Hkv));
   if (a.bits == 4)
     hipLaunchKernelGGL((socket_score_fast<GT, 16>), grid, dim3(256), lds, stream, a);
@@ -318,14 +332,10 @@ hipError_t launch_score_fast(const attn_impl::SocketSelectArgs& a, size_t lds, h
 
 // ---- exact top-k selection -------------------------------------------------
 //
-// One workgroup of SEL_T threads per query head.  Wave w owns the contiguous
-// key segment [w * seg, (w + 1) * seg) and walks it in steps of 64 keys, so
-// (wave, step, lane) is ascending key order.  Three radix passes over the
-// score bit patterns (12 + 12 + 8 bits; scores are >= 0, so bit patterns order
-// like values) find the k-th largest pattern `thr` and how many keys equal to
-// it are taken; the last pass keeps one histogram per wave, which gives every
-// wave its count of keys above `thr` and equal to it without another read.
-// The write pass then places keys in ascending order using ballots.
+// Score bit patterns without the sign bit order like the scores (they are
+// >= 0), so the selection works on those integer keys: the bracket path or
+// the radix path finds the top_k-th largest key, the write pass emits the
+// chosen keys in ascending order (socket_select_kernel below).
 
 constexpr int SEL_WAVES = SEL_T / 64;
 static_assert(SEL_WAVES * 256 >= 4096, "pass-3 histograms must cover the pass-1 bins' storage");
@@ -385,10 +395,15 @@ __device__ __forceinline__ void find_bin(const int* hist, int nbins, int remain,
 // Four consecutive scores from key j on (zero past s1); 16-byte loads where
 // the row allows them.
 __device__ __forceinline__ u32x4 load_scores4(const uint32_t* sc, int j, int s1, bool vec) {
-  if (vec && j + 3 < s1) return *reinterpret_cast<const u32x4*>(sc + j);
   u32x4 r;
+  if (vec && j + 3 < s1) {
+    r = *reinterpret_cast<const u32x4*>(sc + j);
+  } else {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) r[e] = j + e < s1 ? sc[j + e] : 0u;
+    for (int e = 0; e < 4; ++e) r[e] = j + e < s1 ? sc[j + e] : 0u;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = score_key(r[e]);
   return r;
 }
 
@@ -405,66 +420,332 @@ __device__ __forceinline__ int wave_prefix3(int x, int* total) {
   return pre;
 }
 
+// Appends the lane's flagged keys (bit e of m: key jb + e) to list at the
+// LDS counter *cnt, at most cap entries in all.  Every lane of the wave calls it.
+__device__ __forceinline__ void wave_append4(int* list, int* cnt, int cap, int m, int jb) {
+  int tot;
+  const int pre = wave_prefix3(__builtin_popcount(m), &tot);
+  if (tot == 0) return;  // wave-uniform
+  int base = 0;
+  if ((threadIdx.x & 63) == 0) base = atomicAdd(cnt, tot);
+  int p = __shfl(base, 0, 64) + pre;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if ((m >> e) & 1) {
+      if (p < cap) list[p] = jb + e;
+      ++p;
+    }
+}
+
+constexpr int CAP = 512;          // per-wave capacity of the one-read path's two key lists
+constexpr int SAMPLE_MAX = 8192;  // sample size of the one-read path
+constexpr int SEL_SMEM = 4096 + 3 * SEL_WAVES * CAP;
+static_assert(SEL_WAVES * CAP >= SAMPLE_MAX, "the sample lives in the first list area");
+static_assert(SEL_SMEM >= SEL_WAVES * 256 + 256, "the radix path's histograms share the same LDS");
+
+// Radix select over `n` keys (read through key(i)) whose bits under `mask`
+// equal `prefix`: the `remain`-th largest, 11 bits per pass down to bit 0,
+// starting below the bits already fixed (bit `top` is the highest unfixed
+// bit).  Returns the key; *remain_out = its rank among the keys equal to it.
+template <typename KeyAt>
+__device__ __forceinline__ uint32_t select_small(KeyAt key, int n, uint32_t prefix, uint32_t mask, int top,
+                                                 int remain, int* hist, int* scan, int* sv, int* remain_out) {
+  const int tid = threadIdx.x;
+  for (int hi = top; hi >= 0; hi -= 11) {
+    const int width = hi + 1 < 11 ? hi + 1 : 11;
+    const int sh = hi + 1 - width;
+    const int nbins = 1 << width;
+    for (int i = tid; i < nbins; i += SEL_T) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += SEL_T) {
+      const uint32_t u = key(i);
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> sh) & (nbins - 1)], 1);
+    }
+    __syncthreads();
+    find_bin(hist, nbins, remain, scan, &sv[0], &sv[1]);
+    prefix |= (uint32_t)sv[0] << sh;
+    mask |= (uint32_t)(nbins - 1) << sh;
+    remain = sv[1];
+  }
+  *remain_out = remain;
+  return prefix;
+}
+
+// Number of entries of the ascending list d[0, n) below x.
+__device__ __forceinline__ int count_below(const int* d, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (d[mid] < x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// One-read path.  A sample of the scores (runs of 64 keys every Z keys, at
+// most SAMPLE_MAX of them; every key when S is small) gives, by two radix
+// passes over its top 22 key bits, scores L <= U around ranks top_k*f -/+ a
+// 4-sigma margin (f the sample fraction; the exact rank when the sample is
+// every key), so that the threshold lies in [L, U].  One pass over the scores
+// by wave segments appends, in key order, each wave's keys above U (all
+// chosen) and its candidates in [L, U] (index and score) to per-wave LDS
+// lists.  A radix select over the candidates alone gives the exact threshold;
+// each wave keeps the candidates above it and the first equal ones within the
+// tie budget (lowest indices first, over the waves in order) and merges them
+// with its keys above U into the output, ascending.  The bracket only decides
+// speed: when it misses (more than top_k keys above U, fewer than top_k at or
+// above L, or a wave list over CAP) this returns false having written
+// nothing, and the radix path runs.
+__device__ bool select_one_read(const attn_impl::SocketSelectArgs& a, const uint32_t* sc, bool vec, int seg,
+                                int* out, int* smem, int* scan, int* sv, int* sA, int* sC, int* sPos,
+                                int* sTake) {
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int S = a.S, K = a.top_k;
+  int* hist = smem;                          // 2 x 2048 bins
+  int* A = smem + 4096;                      // [SEL_WAVES][CAP] keys above U
+  int* Ci = A + SEL_WAVES * CAP;             // [SEL_WAVES][CAP] candidate keys
+  uint32_t* Cv = reinterpret_cast<uint32_t*>(Ci + SEL_WAVES * CAP);  // their score keys
+  int* samp = A;
+
+  // Sample: key j with (j % Z) < 64.
+  int Z = 64;
+  while ((long long)((S + Z - 1) / Z) * 64 > SAMPLE_MAX) Z <<= 1;
+  const int nfull = S / Z, tail = S - nfull * Z;
+  const int ns = nfull * 64 + (tail < 64 ? tail : 64);
+  int rhi = K, rlo = K;
+  if (ns < S) {
+    const double f = (double)ns / S, mean = K * f;
+    const int m = (int)ceil(4.0 * sqrt(mean * (1.0 - f))) + 8;
+    rhi = (int)floor(mean) - m;
+    rlo = (int)ceil(mean) + m;
+  }
+  const bool do_hi = rhi >= 1, do_lo = rlo <= ns;
+  for (int i = tid; i < 2048; i += SEL_T) hist[i] = 0;
+  for (int i = tid; i < ns; i += SEL_T) samp[i] = (int)score_key(sc[(i / 64) * Z + (i % 64)]);
+  __syncthreads();
+  for (int i = tid; i < ns; i += SEL_T) atomicAdd(&hist[samp[i] >> 20], 1);
+  __syncthreads();
+  uint32_t phi = 0, plo = 0;
+  if (do_hi) {
+    find_bin(hist, 2048, rhi, scan, &sv[0], &sv[1]);
+    phi = (uint32_t)sv[0] << 20;
+    rhi = sv[1];
+  }
+  if (do_lo) {
+    find_bin(hist, 2048, rlo, scan, &sv[0], &sv[1]);
+    plo = (uint32_t)sv[0] << 20;
+    rlo = sv[1];
+  }
+  for (int i = tid; i < 4096; i += SEL_T) hist[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < ns; i += SEL_T) {
+    const uint32_t v = (uint32_t)samp[i];
+    if (do_hi && (v & 0x7ff00000u) == phi) atomicAdd(&hist[(v >> 9) & 2047], 1);
+    if (do_lo && (v & 0x7ff00000u) == plo) atomicAdd(&hist[2048 + ((v >> 9) & 2047)], 1);
+  }
+  __syncthreads();
+  if (do_hi) {
+    find_bin(hist, 2048, rhi, scan, &sv[0], &sv[1]);
+    phi |= (uint32_t)sv[0] << 9;
+  }
+  if (do_lo) {
+    find_bin(hist + 2048, 2048, rlo, scan, &sv[0], &sv[1]);
+    plo |= (uint32_t)sv[0] << 9;
+  }
+  const uint32_t U = do_hi ? (phi | 0x1ffu) : 0xffffffffu;  // top of the sample's 22-bit bin
+  const uint32_t L = do_lo ? plo : 0u;                       // bottom of its 22-bit bin
+  __syncthreads();  // the sample (in A) is dead from here
+
+  // Gather by wave segments, in key order.
+  const int s0 = min(S, wave * seg), s1 = min(S, s0 + seg);
+  int* myA = A + wave * CAP;
+  int* myCi = Ci + wave * CAP;
+  uint32_t* myCv = Cv + wave * CAP;
+  int na = 0, nc = 0;  // wave-uniform
+  for (int j0 = s0; j0 < s1; j0 += 256 * SEL_U) {
+    u32x4 v[SEL_U];
+#pragma unroll
+    for (int u = 0; u < SEL_U; ++u) v[u] = load_scores4(sc, j0 + u * 256 + lane * 4, s1, vec);
+#pragma unroll
+    for (int u = 0; u < SEL_U; ++u) {
+      const int jb = j0 + u * 256 + lane * 4;
+      int ma = 0, mc = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool in = jb + e < s1;
+        ma |= (int)(in && v[u][e] > U) << e;
+        mc |= (int)(in && v[u][e] >= L && v[u][e] <= U) << e;
+      }
+      int ta, tc;
+      int pa = na + wave_prefix3(__builtin_popcount(ma), &ta);
+      int pc = nc + wave_prefix3(__builtin_popcount(mc), &tc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if ((ma >> e) & 1) {
+          if (pa < CAP) myA[pa] = jb + e;
+          ++pa;
+        }
+        if ((mc >> e) & 1) {
+          if (pc < CAP) {
+            myCi[pc] = jb + e;
+            myCv[pc] = v[u][e];
+          }
+          ++pc;
+        }
+      }
+      na += ta;
+      nc += tc;
+    }
+  }
+  if (lane == 0) {
+    sA[wave] = na;
+    sC[wave] = nc;
+  }
+  __syncthreads();
+  int nA = 0, nC = 0;
+  bool fits = true;
+  for (int w = 0; w < SEL_WAVES; ++w) {
+    nA += sA[w];
+    nC += sC[w];
+    fits = fits && sA[w] <= CAP && sC[w] <= CAP;
+  }
+  if (!fits || nA > K || nA + nC < K) {  // same decision in every thread
+    __syncthreads();  // everyone has read the counts before LDS is reused
+    return false;
+  }
+
+  // Exact threshold among the candidates (nA == K: exactly the keys above U).
+  uint32_t thr = U;
+  int need_eq = 0;
+  if (nA < K)
+    thr = select_small(
+        [&](int i) { return (i % CAP) < sC[i / CAP] ? Cv[i] : 0xffffffffu; }, SEL_WAVES * CAP, 0u, 0x80000000u, 30,
+        K - nA, hist, scan, sv, &need_eq);
+
+  // Per wave: candidates above thr and equal to it.
+  int gt = 0, eq = 0;
+  if (nA < K)
+    for (int r = lane; r < sC[wave]; r += 64) {
+      gt += myCv[r] > thr;
+      eq += myCv[r] == thr;
+    }
+  gt = wave_sum_int(gt);
+  eq = wave_sum_int(eq);
+  if (lane == 0) {
+    sTake[wave] = eq;  // equal-key counts for now
+    sPos[wave] = gt;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int eq_before = 0, pos = 0;
+    for (int w = 0; w < SEL_WAVES; ++w) {
+      const int e = sTake[w], g = sPos[w];
+      const int take = max(0, min(e, need_eq - eq_before));
+      eq_before += e;
+      sTake[w] = take;
+      sPos[w] = pos;
+      pos += sA[w] + g + take;
+    }
+  }
+  __syncthreads();
+
+  // Keep the chosen candidates, in order, at the front of the wave's list.
+  const int take_eq = sTake[wave];
+  int kept = 0, eq_seen = 0;
+  if (nA < K)
+    for (int r0 = 0; r0 < sC[wave]; r0 += 64) {
+      const int r = r0 + lane;
+      const bool in = r < sC[wave];
+      const uint32_t x = in ? myCv[r] : 0u;
+      const int idx = in ? myCi[r] : 0;
+      const bool is_eq = in && x == thr;
+      const uint64_t em = __ballot(is_eq);
+      const bool take = in && (x > thr || (is_eq && eq_seen + lanes_below(em) < take_eq));
+      const uint64_t tm = __ballot(take);
+      if (take) myCi[kept + lanes_below(tm)] = idx;
+      kept += __popcll(tm);
+      eq_seen += __popcll(em);
+    }
+
+  // Merge the wave's keys above U with its kept candidates (both ascending).
+  const int na_w = sA[wave];
+  int* o = out + sPos[wave];
+  for (int i = lane; i < na_w; i += 64) o[i + count_below(myCi, kept, myA[i])] = myA[i];
+  for (int i = lane; i < kept; i += 64) o[i + count_below(myA, na_w, myCi[i])] = myCi[i];
+  return true;
+}
+
+// One workgroup of SEL_T threads per query head.  Wave w owns the contiguous
+// key segment [w * seg, (w + 1) * seg) and walks it in steps of 256 keys (64
+// lanes x 4 consecutive keys), so (wave, step, lane, element) is ascending key
+// order.  The threshold and the per-wave counts come from the bracket path
+// (one read of the scores) or, when its bracket misses, from three radix
+// passes (12 + 12 + 8 bits; the last keeps one histogram per wave, which gives
+// every wave its counts without another read).  The write pass then places
+// the keys above the threshold and the lowest-index keys equal to it in
+// ascending order using ballots.
 __global__ __launch_bounds__(SEL_T) void socket_select_kernel(attn_impl::SocketSelectArgs a) {
-  __shared__ int hist[SEL_WAVES * 256 + 256];  // passes 1-2: 4096 bins; pass 3: [SEL_WAVES][256] + their sum
+  __shared__ int smem[SEL_SMEM];
   __shared__ int scan[SEL_T];
-  __shared__ int sBin, sRemain;
+  __shared__ int sv[8];
   __shared__ int sGt[SEL_WAVES], sEq[SEL_WAVES], sPos[SEL_WAVES], sTake[SEL_WAVES];
   const int nh = blockIdx.x;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const uint32_t* sc = reinterpret_cast<const uint32_t*>(a.scores) + (size_t)nh * a.S;
   const bool vec = (a.S & 3) == 0;  // rows start 16-byte aligned
   int* out = a.selected + (size_t)nh * a.top_k;
-  // Wave segments are whole steps of 256 keys (64 lanes x 4 consecutive keys).
   const int seg = (a.S + SEL_WAVES * 256 - 1) / (SEL_WAVES * 256) * 256;
   const int s0 = min(a.S, wave * seg), s1 = min(a.S, s0 + seg);
+  if (select_one_read(a, sc, vec, seg, out, smem, scan, sv, sGt, sEq, sPos, sTake)) return;
 
-  uint32_t prefix = 0, mask = 0;
-  int remain = a.top_k;
-  int above = 0;  // this lane's keys whose top 24 bits exceed the pass-3 prefix
+  uint32_t thr;
+  int need_eq;
+  {
+    int* hist = smem;  // passes 1-2: 4096 bins; pass 3: [SEL_WAVES][256] + their sum
+    uint32_t prefix = 0, mask = 0;
+    int remain = a.top_k;
+    int above = 0;  // this lane's keys whose top 24 bits exceed the pass-3 prefix
 #pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int sh = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
-    const int nbins = pass == 2 ? 256 : 4096;
-    const int hsize = pass == 2 ? SEL_WAVES * 256 : 4096;
-    int* h = pass == 2 ? hist + wave * 256 : hist;
-    for (int i = tid; i < hsize; i += SEL_T) hist[i] = 0;
-    __syncthreads();
-    for (int j0 = s0; j0 < s1; j0 += 256 * SEL_U) {
-      u32x4 v[SEL_U];
+    for (int pass = 0; pass < 3; ++pass) {
+      const int sh = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
+      const int nbins = pass == 2 ? 256 : 4096;
+      const int hsize = pass == 2 ? SEL_WAVES * 256 : 4096;
+      int* h = pass == 2 ? hist + wave * 256 : hist;
+      for (int i = tid; i < hsize; i += SEL_T) hist[i] = 0;
+      __syncthreads();
+      for (int j0 = s0; j0 < s1; j0 += 256 * SEL_U) {
+        u32x4 v[SEL_U];
 #pragma unroll
-      for (int u = 0; u < SEL_U; ++u) v[u] = load_scores4(sc, j0 + u * 256 + lane * 4, s1, vec);
+        for (int u = 0; u < SEL_U; ++u) v[u] = load_scores4(sc, j0 + u * 256 + lane * 4, s1, vec);
 #pragma unroll
-      for (int u = 0; u < SEL_U; ++u) {
+        for (int u = 0; u < SEL_U; ++u) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (j0 + u * 256 + lane * 4 + e < s1) {
-            const uint32_t x = v[u][e];
-            if ((x & mask) == prefix) atomicAdd(&h[(x >> sh) & (nbins - 1)], 1);
-            if (pass == 2) above += (x >> 8) > (prefix >> 8);
+          for (int e = 0; e < 4; ++e) {
+            if (j0 + u * 256 + lane * 4 + e < s1) {
+              const uint32_t x = v[u][e];
+              if ((x & mask) == prefix) atomicAdd(&h[(x >> sh) & (nbins - 1)], 1);
+              if (pass == 2) above += (x >> 8) > (prefix >> 8);
+            }
           }
         }
       }
-    }
-    __syncthreads();
-    if (pass == 2) {  // fold the per-wave histograms into hist[SEL_WAVES * 256 ...]
-      if (tid < 256) {
-        int t = 0;
-        for (int w = 0; w < SEL_WAVES; ++w) t += hist[w * 256 + tid];
-        hist[SEL_WAVES * 256 + tid] = t;
-      }
       __syncthreads();
+      if (pass == 2) {  // fold the per-wave histograms into hist[SEL_WAVES * 256 ...]
+        if (tid < 256) {
+          int t = 0;
+          for (int w = 0; w < SEL_WAVES; ++w) t += hist[w * 256 + tid];
+          hist[SEL_WAVES * 256 + tid] = t;
+        }
+        __syncthreads();
+      }
+      find_bin(pass == 2 ? hist + SEL_WAVES * 256 : hist, nbins, remain, scan, &sv[0], &sv[1]);
+      prefix |= (uint32_t)sv[0] << sh;
+      mask |= (uint32_t)(nbins - 1) << sh;
+      remain = sv[1];
     }
-    find_bin(pass == 2 ? hist + SEL_WAVES * 256 : hist, nbins, remain, scan, &sBin, &sRemain);
-    prefix |= (uint32_t)sBin << sh;
-    mask |= (uint32_t)(nbins - 1) << sh;
-    remain = sRemain;
-  }
-  const uint32_t thr = prefix;  // the top_k-th largest bit pattern
-  const int need_eq = remain;   // keys equal to it that are taken, lowest indices first
-
-  // Per-wave counts: above the 24-bit prefix, plus the wave's own last-pass bins.
-  {
+    thr = prefix;
+    need_eq = remain;
+    // Per-wave counts: above the 24-bit prefix, plus the wave's own last-pass bins.
     const int bin = (int)(thr & 0xffu);
     int gt = above;
     for (int b = lane; b < 256; b += 64) gt += b > bin ? hist[wave * 256 + b] : 0;
@@ -473,8 +754,9 @@ __global__ __launch_bounds__(SEL_T) void socket_select_kernel(attn_impl::SocketS
       sGt[wave] = gt;
       sEq[wave] = hist[wave * 256 + bin];
     }
+    __syncthreads();
   }
-  __syncthreads();
+
   if (tid == 0) {
     int eq_before = 0, pos = 0;
     for (int w = 0; w < SEL_WAVES; ++w) {

@@ -10,6 +10,13 @@ at least s_k (1 - 1e-4) (s_k the k-th largest score); where no other key lies
 in that band the chosen set must equal the oracle's and the output must match
 the oracle's sparse attention within 2e-2 (O) / 1e-3 (LSE).  With top_k = S the
 sparse decode must equal the dense decode.
+
+Exact ties: keys that are copies of one key (same K and V rows) get bit-equal
+scores on both sides, so a selection whose only near-threshold keys are such a
+group is fixed by the tie rule (lower index first) and compared exactly; the
+cases reach every selection path (one read of the scores with and without the
+scorer's histogram, ties straddling the cut, top_k above 4096, and more than
+8192 keys in the threshold's first-level bin).
 """
 import numpy as np
 import pytest
@@ -37,8 +44,8 @@ CASES = [
 ]
 
 
-def _run(w, tables, bits, tau, top_k, splits):
-    inp = gen.generate(w)
+def _run(w, tables, bits, tau, top_k, splits, inp=None):
+    inp = gen.generate(w) if inp is None else inp
     q, k, v, sink = to_device(inp)
     proj_np = gen.socket_projections(w.seed, tables, bits, w.E)
     proj = torch.from_numpy(proj_np).to("cuda:0")
@@ -102,3 +109,62 @@ def test_socket_full_budget_equals_dense_decode():
     assert torch.equal(sel.cpu(), torch.arange(700, dtype=torch.int32).expand(2, 4, 700))
     assert (o1.float() - o2.float()).abs().max().item() <= 2e-2
     assert (l1 - l2).abs().max().item() <= 1e-3
+
+
+def _tie_case(S, E, rank, group, extra_keep, seed, Hq=1, tables=16, bits=4, tau=2.0, identical=False):
+    """A single-head cache where `group` other keys are copies of the key at `rank` (by the
+    oracle's score) -- or, with identical=True, every key is a copy of key 0 -- and top_k cuts
+    the copies after `extra_keep` of them."""
+    w = W(f"ties_S{S}", 1, Hq, 1, S, E, seed=seed)
+    inp = gen.generate(w)
+    proj = gen.socket_projections(w.seed, tables, bits, E)
+    k, v = inp.k.copy(), inp.v.copy()
+    if identical:
+        k[:, :, :] = k[:, :, :1]
+        v[:, :, :] = v[:, :, :1]
+        members = np.arange(S)
+    else:
+        b0, vn0 = oracle.socket_hash(k, v, proj, tables, bits)
+        sc0 = oracle.socket_scores(inp.q[0, 0, 0], proj, b0[0, 0], vn0[0, 0], tables, bits, tau)
+        src = int(np.lexsort((np.arange(S), -sc0))[rank])
+        rest = np.setdiff1d(np.arange(S), [src])
+        dup = np.random.default_rng(seed).choice(rest, size=group, replace=False)
+        k[:, :, dup] = k[:, :, src:src + 1]
+        v[:, :, dup] = v[:, :, src:src + 1]
+        members = np.sort(np.concatenate([dup, [src]]))
+    inp = gen.Inputs(w, inp.q, k, v, inp.sink)
+    b, vn = oracle.socket_hash(k, v, proj, tables, bits)
+    sc = oracle.socket_scores(inp.q[0, 0, 0], proj, b[0, 0], vn[0, 0], tables, bits, tau)
+    tie = sc[members[0]]
+    assert np.all(sc[members] == tie)
+    top_k = int(np.sum(sc > tie)) + extra_keep
+    near = np.abs(sc - tie) <= 1e-4 * tie
+    assert np.array_equal(np.flatnonzero(near), members), "another key scores within the band of the copies"
+    return w, inp, tables, bits, tau, top_k
+
+
+TIE_CASES = [
+    # name, S, E, rank of the copied key, copies, copies kept, seed, extra
+    ("one_read_ties_straddle", 3000, 64, 120, 499, 250, 61, {}),
+    ("one_read_ties_straddle_gqa2", 3000, 128, 90, 300, 77, 62, {"Hq": 2}),
+    ("radix_top_k_above_4096", 12000, 64, 4000, 1999, 1000, 63, {}),
+    ("radix_after_bin_overflow", 16000, 64, 150, 9000, 1000, 64, {}),
+    ("all_keys_identical", 9000, 64, 0, 0, 100, 65, {"identical": True}),
+]
+
+
+@pytest.mark.parametrize("name,S,E,rank,group,keep,seed,extra", TIE_CASES, ids=[c[0] for c in TIE_CASES])
+def test_socket_exact_ties(name, S, E, rank, group, keep, seed, extra):
+    w, inp, tables, bits, tau, top_k = _tie_case(S, E, rank, group, keep, seed, **extra)
+    say(f"[socket ties] {name}: S={S} top_k={top_k} Hq={w.Hq}")
+    inp, (o_ref, l_ref, sel_ref, sc_ref), outs = _run(w, tables, bits, tau, top_k, (0,), inp=inp)
+    for s, o, lse, sel in outs:
+        sg = sel.cpu().numpy()
+        og = o.float().cpu().numpy().astype(np.float64)
+        lg = lse.cpu().numpy().astype(np.float64)
+        for h in range(w.Hq):
+            if h == 0:  # the copies were placed by head 0's ranking
+                assert np.array_equal(sg[0, h], sel_ref[0, h]), "tie-broken selection differs"
+                assert np.max(np.abs(og[0, h] - o_ref[0, h])) <= 2e-2
+                assert abs(lg[0, h, 0] - l_ref[0, h, 0]) <= 1e-3
+            assert np.all(np.diff(sg[0, h]) > 0)
