@@ -41,6 +41,7 @@ from workloads import configs, gen  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+RIDGE_BF16 = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop per byte where the two bounds meet
 METRIC = "prefill TFLOP/s + decode HBM GB/s, as % of MI355X roofline, oracle-exact"
 
 KERNEL_FILES = {
@@ -246,10 +247,14 @@ def rate(w, ms: float):
         gbs = configs.algorithmic_bytes(w) / (ms * 1e-3) / 1e9
         return {"value": gbs, "unit": "GB/s", "bound": "hbm", "peak": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS}
     tf = configs.algorithmic_flops(w) / (ms * 1e-3) / 1e12
+    gbs = configs.algorithmic_bytes(w) / (ms * 1e-3) / 1e9
+    if w.dtype == "bf16" and configs.algorithmic_flops(w) / configs.algorithmic_bytes(w) < RIDGE_BF16:
+        # Below the ridge point the kernel is bound by HBM, not by the matrix cores.
+        return {"value": gbs, "unit": "GB/s", "bound": "hbm", "peak": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS,
+                "tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS}
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     out = {"value": tf, "unit": "TFLOP/s", "bound": "mfma" if w.dtype == "bf16" else "alu", "peak": peak,
            "frac": tf / peak}
-    gbs = configs.algorithmic_bytes(w) / (ms * 1e-3) / 1e9
     out["hbm_GBps"] = gbs
     out["hbm_frac"] = gbs / PEAK_HBM_GBS
     return out
