@@ -249,8 +249,12 @@ void bwd_dq_kernel(BwdParams p, int num_q_tiles) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const int qt = blockIdx.x % num_q_tiles;
-  const int nh = blockIdx.x / num_q_tiles;
+  // Query tiles in descending order when causal (the last tiles see the most
+  // keys: heaviest first); consecutive blocks are different heads, so every
+  // tile of a head lands on the same XCD (its K/V stays in that L2).
+  const int nhs = gridDim.x / num_q_tiles;
+  const int qt = p.causal ? num_q_tiles - 1 - (int)blockIdx.x / nhs : (int)blockIdx.x / nhs;
+  const int nh = blockIdx.x % nhs;
   const int h = nh % p.Hq, n = nh / p.Hq;
   const int kh = h / (p.Hq / p.Hkv);
   const int i0 = qt * BR;
@@ -481,8 +485,12 @@ void bwd_dkdv_kernel(BwdParams p, int num_k_tiles) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const int kt = blockIdx.x % num_k_tiles;
-  const int nk = blockIdx.x / num_k_tiles;
+  // Key tiles in ascending order (with a causal mask the first tiles are seen
+  // by the most queries: heaviest first); consecutive blocks are different kv
+  // heads, so every tile of a kv head lands on the same XCD.
+  const int nks = gridDim.x / num_k_tiles;
+  const int kt = blockIdx.x / nks;
+  const int nk = blockIdx.x % nks;
   const int kh = nk % p.Hkv, n = nk / p.Hkv;
   const int G = p.Hq / p.Hkv;
   const int j0 = kt * BR;                 // first key (flat, registers included) of the workgroup
