@@ -15,19 +15,21 @@
 //          denominator, "Attention Sink" section 4.2)
 // dK and dV of a key/value head sum over the query heads of its GQA group.
 //
-// Three launches, no atomics (results are deterministic):
-//  1. bwd_pre_kernel: per row D_i, and the reference the weights are taken
-//     against in the kernels' log2 frame, mref_i = (LSE_i [+ gamma |q_i|^2]) log2 e
-//     (+inf for a row with nothing visible, whose weights are all 0); per-block
-//     partial sums of the sink gradient, reduced by bwd_sink_kernel.
-//  2. bwd_dq_kernel: the forward's layout (128 query rows per workgroup, each
+// Up to three launches, no atomics (results are deterministic):
+//  1. bwd_dq_kernel: the forward's layout (128 query rows per workgroup, each
 //     wave 32 rows, keys streamed through LDS in tiles of 64): S^T = K Q^T and
 //     dP^T = V dO^T on v_mfma_f32_32x32x16_bf16, dS^T in registers, then
-//     dQ^T += K^T dS^T with K^T read by the transposing LDS read.
-//  3. bwd_dkdv_kernel: the transposed layout (128 keys per workgroup, each wave
+//     dQ^T += K^T dS^T with K^T read by the transposing LDS read.  Before its
+//     key loop it forms, per row, D_i and the reference the weights are taken
+//     against in the kernels' log2 frame, mref_i = (LSE_i [+ gamma |q_i|^2])
+//     log2 e (+inf for a row with nothing visible, whose weights are all 0),
+//     stores both for the dK/dV kernel, and writes one partial sum of the sink
+//     gradient per wave.
+//  2. bwd_dkdv_kernel: the transposed layout (128 keys per workgroup, each wave
 //     32 keys held in VGPRs as K^T and V^T operands), streaming the query tiles
 //     of every head of the group through LDS: S = Q K^T, dP = dO V^T, then
 //     dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read transposed.
+//  3. bwd_sink_kernel (with a sink): the partials summed in a fixed order.
 // P and dS are rounded to bf16 as MFMA operands (fp32 accumulation), like P in
 // the forward; outputs are bf16.
 #include "device_common.h"
@@ -41,7 +43,6 @@ namespace {
 constexpr int NT = 256;   // threads per workgroup (4 waves)
 constexpr int BT = 64;    // rows per staged LDS tile (keys in dQ, queries in dK/dV)
 constexpr int BR = 128;   // rows owned per workgroup (queries in dQ, keys in dK/dV)
-constexpr int PRE = 256;  // rows per preprocess workgroup
 
 struct BwdParams {
   const uint16_t* q;
@@ -57,65 +58,11 @@ struct BwdParams {
   float* dsink;
   float* delta;      // [N*Hq*L] D_i
   float* mref;       // [N*Hq*L] reference (log2 units); +inf for empty rows
-  float* sink_part;  // [N*Hq*pre_blocks] partial sink gradients
+  float* sink_part;  // [N*Hq*pre_blocks] partial sink gradients (one per dQ wave)
   int N, Hq, Hkv, L, S, n_reg, S_real, off, causal, window, rbf;
   float c_logit, c_bias, gamma, scale;
   int pre_blocks;
 };
-
-// ---------------------------------------------------------------------------- 1. preprocess
-
-// ECH = E/8 consecutive lanes share a row (one 16-byte chunk each), so every
-// load instruction of a wave reads whole contiguous rows; the row sums come
-// from a DPP reduction over those lanes.  PRE rows per workgroup.
-template <int E>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
-  constexpr int ECH = E / 8;
-  constexpr int RPP = 256 / ECH;  // rows per pass of the workgroup
-  __shared__ float red[256];
-  const int nh = blockIdx.y;
-  const int h = nh % p.Hq;
-  const int tid = threadIdx.x;
-  const int c = tid % ECH;
-  float part = 0.f;
-#pragma unroll 1
-  for (int pass = 0; pass < PRE / RPP; ++pass) {
-    const int i = blockIdx.x * PRE + pass * RPP + tid / ECH;
-    const bool ok = i < p.L;
-    const size_t row = (size_t)nh * p.L + (ok ? i : 0);
-    const u32x4 a = load16_or_zero(p.o + row * E + 8 * c, ok);
-    const u32x4 b = load16_or_zero(p.dout + row * E + 8 * c, ok);
-    float d = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      d = __builtin_fmaf(bf16_lo(a[w]), bf16_lo(b[w]), d);
-      d = __builtin_fmaf(bf16_hi(a[w]), bf16_hi(b[w]), d);
-    }
-    d = group_sum<ECH>(d);
-    float qn2 = 0.f;
-    if (p.rbf) qn2 = group_sum<ECH>(sumsq8(load16_or_zero(p.q + row * E + 8 * c, ok)));
-    if (ok && c == 0) {
-      const float lse = p.lse[row];
-      float mr = __builtin_huge_valf();
-      if (lse == kNegInf) {
-        d = 0.f;
-      } else {
-        mr = (lse + (p.rbf ? p.gamma * qn2 : 0.f)) * kLog2e;
-        if (p.sink) part += -exp2f((p.sink[h] - lse) * kLog2e) * d;
-      }
-      p.delta[row] = d;
-      p.mref[row] = mr;
-    }
-  }
-  red[tid] = part;
-  __syncthreads();
-#pragma unroll
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) red[tid] += red[tid + s];
-    __syncthreads();
-  }
-  if (tid == 0) p.sink_part[(size_t)nh * p.pre_blocks + blockIdx.x] = red[0];
-}
 
 // One workgroup per query head: the partial sums in a fixed order.
 __global__ __launch_bounds__(64) void bwd_sink_kernel(BwdParams p) {
@@ -263,14 +210,45 @@ void bwd_dq_kernel(BwdParams p, int num_q_tiles) {
   const int qb = min(qa + 31, p.L - 1);
   const size_t row = (size_t)nh * p.L + min(qi, p.L - 1);
 
+  // Q^T and dO^T fragments, and this workgroup's share of the row
+  // preliminaries: D_i = dO_i . O_i, the reference the weights are taken
+  // against in the log2 frame, mref_i = (LSE_i [+ gamma |q_i|^2]) log2 e (+inf
+  // for a row with nothing visible, whose weights are all 0), both stored for
+  // the dK/dV kernel, and one partial sum of the sink gradient per wave.
   bf16x8 qf[QS], gf[QS];
+  float dd = 0.f, qn2 = 0.f;
 #pragma unroll
   for (int s = 0; s < QS; ++s) {
-    qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(p.q + row * E + 16 * s + 8 * g));
-    gf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(p.dout + row * E + 16 * s + 8 * g));
+    const u32x4 qc = *reinterpret_cast<const u32x4*>(p.q + row * E + 16 * s + 8 * g);
+    const u32x4 gc = *reinterpret_cast<const u32x4*>(p.dout + row * E + 16 * s + 8 * g);
+    const u32x4 oc = *reinterpret_cast<const u32x4*>(p.o + row * E + 16 * s + 8 * g);
+    qf[s] = as_bf16x8(qc);
+    gf[s] = as_bf16x8(gc);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      dd = __builtin_fmaf(bf16_lo(oc[w]), bf16_lo(gc[w]), dd);
+      dd = __builtin_fmaf(bf16_hi(oc[w]), bf16_hi(gc[w]), dd);
+    }
+    if (RBF) qn2 += sumsq8(qc);
   }
-  const float mr = qi < p.L ? p.mref[row] : __builtin_huge_valf();
-  const float dl = qi < p.L ? p.delta[row] : 0.f;
+  dd = pair32_sum(dd);
+  if (RBF) qn2 = pair32_sum(qn2);
+  const float lse = qi < p.L ? p.lse[row] : kNegInf;
+  float mr = __builtin_huge_valf(), dl = 0.f;
+  if (lse != kNegInf) {
+    mr = (lse + (RBF ? p.gamma * qn2 : 0.f)) * kLog2e;
+    dl = dd;
+  }
+  if (g == 0 && qi < p.L) {
+    p.delta[row] = dl;
+    p.mref[row] = mr;
+  }
+  if (p.dsink) {
+    float part = (g == 0 && lse != kNegInf && p.sink) ? -exp2f((p.sink[h] - lse) * kLog2e) * dl : 0.f;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) part += xor_lane(part, o);
+    if (lane == 0) p.sink_part[(size_t)nh * p.pre_blocks + qt * 4 + wave] = part;
+  }
   // Dot mode: acc = K^T dS^T.  RBF mode: dQ_i/2gamma = sum_j dS_ij (k_j - q_i)
   // would difference two large terms (|q| >> |k - q| is common), and D_i from
   // the bf16 O would be amplified by |q_i|; instead acc = K^T (P o dP)^T and
@@ -718,31 +696,25 @@ hipError_t launch_backward_bf16(const BwdArgs& a, hipStream_t stream) {
     p.c_logit = f.scale * kLog2e;
     p.c_bias = 0.f;
   }
-  p.pre_blocks = (f.L + PRE - 1) / PRE;
+  p.pre_blocks = 4 * ((f.L + BR - 1) / BR);  // one sink-gradient partial per wave of the dQ kernel
   p.delta = a.workspace;
   p.mref = p.delta + (size_t)f.N * f.Hq * f.L;
   p.sink_part = p.mref + (size_t)f.N * f.Hq * f.L;
 
-  const dim3 pgrid((unsigned)p.pre_blocks, (unsigned)(f.N * f.Hq));
+  hipError_t e;
   if (f.E == 128)
-    hipLaunchKernelGGL((bwd_pre_kernel<128>), pgrid, dim3(256), 0, stream, p);
+    e = f.rbf ? launch_main<128, kRbf>(p, stream) : launch_main<128, kDot>(p, stream);
   else
-    hipLaunchKernelGGL((bwd_pre_kernel<64>), pgrid, dim3(256), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (p.dsink) {  // without a sink the partials are zero and so is the gradient
-    hipLaunchKernelGGL(bwd_sink_kernel, dim3((unsigned)f.Hq), dim3(64), 0, stream, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (f.E == 128) return f.rbf ? launch_main<128, kRbf>(p, stream) : launch_main<128, kDot>(p, stream);
-  return f.rbf ? launch_main<64, kRbf>(p, stream) : launch_main<64, kDot>(p, stream);
+    e = f.rbf ? launch_main<64, kRbf>(p, stream) : launch_main<64, kDot>(p, stream);
+  if (e != hipSuccess || !p.dsink) return e;
+  hipLaunchKernelGGL(bwd_sink_kernel, dim3((unsigned)f.Hq), dim3(64), 0, stream, p);
+  return hipGetLastError();
 }
 
 size_t backward_workspace_bytes(int N, int Hq, int L) {
   const size_t rows = (size_t)N * Hq * L;
-  const size_t pre_blocks = (size_t)(L + PRE - 1) / PRE;
-  return (2 * rows + (size_t)N * Hq * pre_blocks) * sizeof(float);
+  const size_t partials = 4 * (size_t)((L + BR - 1) / BR);
+  return (2 * rows + (size_t)N * Hq * partials) * sizeof(float);
 }
 
 }  // namespace attn_impl

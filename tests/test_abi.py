@@ -169,8 +169,8 @@ def test_bwd_rejects(lib, kw, code):
 
 
 def test_bwd_workspace_size(lib):
-    # D and the reference per row, plus one partial sink sum per (batch, head, 256 rows)
-    assert lib.attn_bwd_workspace_bytes(2, 4, 300) == (2 * 2 * 4 * 300 + 2 * 4 * 2) * 4
+    # D and the reference per row, then one sink partial per 32-row wave of each 128-row query tile
+    assert lib.attn_bwd_workspace_bytes(2, 4, 300) == (2 * 2 * 4 * 300 + 2 * 4 * 4 * 3) * 4
     assert bwd(lib, N=0, L=0, S=0) == 0
 
 
