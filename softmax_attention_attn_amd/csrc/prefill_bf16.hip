@@ -112,11 +112,11 @@ enum { kBiasNone = 0, kBiasF32 = 1, kBiasBool = 2 };
 
 // Waves per SIMD the register budget allows: E = 128 needs ~230 VGPRs (2 waves);
 // E = 64 fits in 128 VGPRs in dot mode (4 waves = 4 workgroups per CU, 128 KB of
-// LDS) and under 168 in RBF mode or with a user bias (3 waves), where 128 would
-// spill.
+// LDS) and under 168 in RBF mode (3 waves), where 128 would spill; with a user
+// bias it needs up to ~210 (2 waves).
 template <int E, int MODE, int UB>
 struct Occupancy {
-  static constexpr int kWaves = E == 64 ? ((MODE == kRbf || UB != 0) ? 3 : 4) : 2;
+  static constexpr int kWaves = (E == 128 || UB != 0) ? 2 : (MODE == kRbf ? 3 : 4);
 };
 
 template <int E, int MODE, int UB>
