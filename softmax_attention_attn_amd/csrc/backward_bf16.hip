@@ -87,16 +87,16 @@ __global__ __launch_bounds__(64) void bwd_sink_kernel(BwdParams p) {
 // x = c_logit*s + c_bias*|k|^2 (the -gamma|q|^2 part is folded into mref).
 enum { kDot = 0, kRbf = 1 };
 
-template <int E>
+template <int E, int R = BT>
 struct TileGeom {
-  static constexpr int QS = E / 16;          // MFMA steps over the head dimension
-  static constexpr int EB = E / 32;          // 32-row blocks of a transposed E x 32 accumulator
-  static constexpr int ECH = E / 8;          // 16-byte chunks per row
-  static constexpr int ROWB = E * 2;         // bytes per row
-  static constexpr int TILEB = BT * ROWB;    // bytes per staged tile
-  static constexpr int RPI = 1024 / ROWB;    // rows per 1 KB wave-wide LDS-direct load
-  static constexpr int IPW = BT / RPI / 4;   // such loads per wave per tile
-  static constexpr int KCH = BT * ECH / NT;  // 16-byte chunks per thread (register staging)
+  static constexpr int QS = E / 16;         // MFMA steps over the head dimension
+  static constexpr int EB = E / 32;         // 32-row blocks of a transposed E x 32 accumulator
+  static constexpr int ECH = E / 8;         // 16-byte chunks per row
+  static constexpr int ROWB = E * 2;        // bytes per row
+  static constexpr int TILEB = R * ROWB;    // bytes per staged tile of R rows
+  static constexpr int RPI = 1024 / ROWB;   // rows per 1 KB wave-wide LDS-direct load
+  static constexpr int IPW = R / RPI / 4;   // such loads per wave per tile
+  static constexpr int KCH = R * ECH / NT;  // 16-byte chunks per thread (register staging)
 };
 
 // Row-operand read offsets (A operand: row l32 of a 32-row block, chunk 2s+g)
@@ -167,13 +167,14 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[EB], float mul, c
 }
 
 // Waves per SIMD: the dQ kernel holds Q^T and dO^T fragments, S^T and dP^T,
-// and the dQ^T accumulator (E = 128: ~230 VGPRs); the dK/dV kernel holds K^T,
-// V^T and two E x 32 accumulators (E = 128: over 256 registers, one wave).
-// In RBF mode the dQ kernel keeps a second E x 32 accumulator (see there).
+// and the dQ^T accumulator (E = 128: ~230 VGPRs); the dK/dV kernel holds K^T
+// and two E x 32 accumulators, plus V^T at E = 64 (at E = 128 V^T is read
+// from LDS, which keeps it within 256 registers: 2 waves).  In RBF mode the dQ
+// kernel keeps a second E x 32 accumulator (see there).
 template <int E, int MODE>
 struct BwdOcc {
   static constexpr int kDq = E == 64 ? (MODE == 1 ? 2 : 3) : (MODE == 1 ? 1 : 2);
-  static constexpr int kDkdv = E == 64 ? 2 : 1;
+  static constexpr int kDkdv = 2;
 };
 
 // ---------------------------------------------------------------------------- 2. dQ
@@ -447,17 +448,27 @@ void bwd_dq_kernel(BwdParams p, int num_q_tiles) {
 template <int E, int MODE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(BwdOcc<E, MODE>::kDkdv, BwdOcc<E, MODE>::kDkdv)))
 void bwd_dkdv_kernel(BwdParams p, int num_k_tiles) {
-  using T = TileGeom<E>;
+  // E = 128: the V^T operands live in LDS (the workgroup's 128 value rows)
+  // instead of registers, and query tiles are 32 rows, so that the kernel fits
+  // 256 registers and runs 2 waves per SIMD; E = 64 keeps them in registers.
+  constexpr bool VL = E == 128;
+  constexpr int QT = VL ? 32 : BT;  // query rows per staged tile
+  using T = TileGeom<E, QT>;
   constexpr bool RBF = MODE == kRbf;
   constexpr int QS = T::QS, EB = T::EB, ECH = T::ECH, ROWB = T::ROWB, TILEB = T::TILEB;
-  static_assert(BR * (E + 8) * 2 <= 2 * 2 * TILEB, "epilogue staging must fit the tile buffers");
+  constexpr int VB = VL ? BR * ROWB : 0;  // bytes of the staged value rows
+  constexpr int RING = 2 * 2 * TILEB;
+  constexpr int EPB = BR * (E + 8) * 2;   // epilogue staging
+  constexpr int SQG = (RING + VB) > EPB ? (RING + VB) : EPB;
 
-  // [buf][Q tile | dO tile]; per buf the 64 rows' reference and D values.
-  __shared__ __attribute__((aligned(16))) uint8_t sQG[2 * 2 * TILEB];
-  __shared__ __attribute__((aligned(16))) float sMR[2][BT];
-  __shared__ __attribute__((aligned(16))) float sDL[2][BT];
+  // [buf][Q tile | dO tile] then (VL) the value rows; per buf the tile rows'
+  // reference and D values.  The epilogue reuses the same bytes.
+  __shared__ __attribute__((aligned(16))) uint8_t sQG[SQG];
+  __shared__ __attribute__((aligned(16))) float sMR[2][QT];
+  __shared__ __attribute__((aligned(16))) float sDL[2][QT];
   auto q_tile = [&](int buf) { return sQG + buf * 2 * TILEB; };
   auto g_tile = [&](int buf) { return sQG + buf * 2 * TILEB + TILEB; };
+  uint8_t* sV = sQG + RING;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -477,15 +488,28 @@ void bwd_dkdv_kernel(BwdParams p, int num_k_tiles) {
   const size_t kvbase = ((size_t)n * p.Hkv + kh) * (size_t)p.S;
 
   // K^T and V^T fragments: lane holds row kj, dims 16s + 8g .. +8 (zeros past S).
-  bf16x8 kf[QS], vf[QS];
+  // VL: the workgroup's value rows go to LDS instead (row r, 16-byte chunk c at
+  // chunk slot c ^ swz(r): the fragment reads of a 32-row block are then
+  // conflict-free, as for the forward's K tile); a barrier precedes their use.
+  bf16x8 kf[QS], vf[VL ? 1 : QS];
   float nk2 = 0.f;
 #pragma unroll
   for (int s = 0; s < QS; ++s) {
     const bool ok = kj < p.S;
     const u32x4 kc = load16_or_zero(p.k + (kvbase + min(kj, p.S - 1)) * E + 16 * s + 8 * g, ok);
     kf[s] = as_bf16x8(kc);
-    vf[s] = as_bf16x8(load16_or_zero(p.v + (kvbase + min(kj, p.S - 1)) * E + 16 * s + 8 * g, ok));
+    if (!VL) vf[s] = as_bf16x8(load16_or_zero(p.v + (kvbase + min(kj, p.S - 1)) * E + 16 * s + 8 * g, ok));
     if (RBF) nk2 += sumsq8(kc);
+  }
+  if (VL) {
+#pragma unroll
+    for (int i = 0; i < BR * ECH / NT; ++i) {
+      const int id = tid + NT * i;
+      const int r = id / ECH, c = id % ECH;
+      const int row = j0 + r;
+      const u32x4 x = load16_or_zero(p.v + (kvbase + min(row, p.S - 1)) * E + 8 * c, row < p.S);
+      *reinterpret_cast<u32x4*>(sV + r * ROWB + ((c ^ tile_swz<E>(r)) * 16)) = x;
+    }
   }
   const float kbias = RBF ? p.c_bias * pair32_sum(nk2) : 0.f;
   float csum = 0.f;  // RBF: this lane's share of sum_i dS_ij
@@ -521,8 +545,8 @@ void bwd_dkdv_kernel(BwdParams p, int num_k_tiles) {
       if (p.window > 0) i_hi = min(p.L - 1, rb - p.off + p.window - 1);
     }
   }
-  const int t_lo = i_lo / BT;
-  const int ntq = i_hi >= i_lo ? i_hi / BT - t_lo + 1 : 0;
+  const int t_lo = i_lo / QT;
+  const int ntq = i_hi >= i_lo ? i_hi / QT - t_lo + 1 : 0;
   const int steps = G * ntq;
 
   uint32_t ld_off[T::IPW];
@@ -533,11 +557,11 @@ void bwd_dkdv_kernel(BwdParams p, int num_k_tiles) {
   }
   uint32_t rd[QS], trd[EB][2];
   tile_offsets<E>(lane, rd, trd);
-  float mrv = 0.f, dlv = 0.f;  // staged per-row values (threads < BT)
+  float mrv = 0.f, dlv = 0.f;  // staged per-row values (threads < QT)
 
   auto step_rows = [&](int st_i, int& h, int& i0) {
     h = kh * G + st_i / ntq;
-    i0 = (t_lo + st_i % ntq) * BT;
+    i0 = (t_lo + st_i % ntq) * QT;
   };
   auto issue_step = [&](int st_i, int buf) {
     int h, i0;
@@ -552,14 +576,14 @@ void bwd_dkdv_kernel(BwdParams p, int num_k_tiles) {
       buffer_load16_to_lds(qrs, q_tile(buf) + blk * 1024, tb + ld_off[b]);
       buffer_load16_to_lds(grs, g_tile(buf) + blk * 1024, tb + ld_off[b]);
     }
-    if (tid < BT) {
+    if (tid < QT) {
       const int i = i0 + tid;
       mrv = i < p.L ? p.mref[qoff + i] : __builtin_huge_valf();
       dlv = i < p.L ? p.delta[qoff + i] : 0.f;
     }
   };
   auto finish_step = [&](int buf) {
-    if (tid < BT) {
+    if (tid < QT) {
       sMR[buf][tid] = mrv;
       sDL[buf][tid] = dlv;
     }
@@ -573,7 +597,7 @@ void bwd_dkdv_kernel(BwdParams p, int num_k_tiles) {
     const uint8_t* q_s = q_tile(buf);
     const uint8_t* g_s = g_tile(buf);
 #pragma unroll
-    for (int b = 0; b < BT / 32; ++b) {
+    for (int b = 0; b < QT / 32; ++b) {
       const int ib = i0 + 32 * b;  // first query row of this block
       f32x16 s_acc, d_acc;
 #pragma unroll
@@ -585,8 +609,10 @@ void bwd_dkdv_kernel(BwdParams p, int num_k_tiles) {
       for (int s = 0; s < QS; ++s) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(q_s + rd[s] + 32 * b * ROWB);
         const bf16x8 ga = *reinterpret_cast<const bf16x8*>(g_s + rd[s] + 32 * b * ROWB);
+        // V^T fragment of this wave's 32 value rows (same offsets as the tile reads).
+        const bf16x8 vs = VL ? *reinterpret_cast<const bf16x8*>(sV + wave * 32 * ROWB + rd[s]) : vf[VL ? 0 : s];
         s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[s], s_acc, 0, 0, 0);
-        d_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[s], d_acc, 0, 0, 0);
+        d_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vs, d_acc, 0, 0, 0);
       }
       // Register r holds query row ib + 8(r/4) + 4g + r%4 for this lane's key.
       const int lo = qlo - ib - 4 * g, hi = qhi - ib - 4 * g;
