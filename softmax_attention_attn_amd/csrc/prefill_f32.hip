@@ -1,12 +1,16 @@
 // prefill_f32.hip -- fused tiled attention forward for float32 inputs on gfx950.
 //
-// Full fp32 arithmetic (no bf16 rounding of P).  One wave = 64 query rows, one
-// row per lane; keys stream through LDS in tiles of 32 with the online softmax
-// (running max and running sum, "SDPA란 무엇인가?" section 2).  Same logit frame, visibility rule, sink and
-// LSE conventions as the bf16 kernel: x = c_logit*(q.k) + c_bias*|k|^2 in log2
-// units, with |k|^2 computed once per staged tile from LDS.  Keys are taken
-// one at a time: the running max only moves (and the accumulator is only
-// rescaled) when a larger logit arrives.
+// Full fp32 arithmetic (no bf16 rounding of P).  A workgroup owns 64 query
+// rows, one per lane, and runs W waves over them (4 at E = 128, 8 at E = 64): keys stream through LDS
+// in tiles of 32 (staged by all W waves), and wave w takes the keys w, w + W,
+// ... of every tile, keeping its own online-softmax state (running max,
+// running sum, accumulator: "SDPA란 무엇인가?" section 2).  At the end the W
+// partial states of each row are merged through LDS with log-sum-exp weights,
+// the split-K combine of the decode path.  Same logit frame, visibility rule,
+// sink and LSE conventions as the bf16 kernel: x = c_logit*(q.k) +
+// c_bias*|k|^2 in log2 units, with |k|^2 computed once per staged tile from
+// LDS.  Within a wave keys are taken one at a time: the running max only moves
+// (and the accumulator is only rescaled) when a larger logit arrives.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -14,8 +18,14 @@ using namespace attn_dev;
 
 namespace {
 
-constexpr int BQ = 64;  // query rows per workgroup (one wave)
+constexpr int BQ = 64;  // query rows per workgroup (one per lane)
 constexpr int BK = 32;  // keys per staged tile
+// Waves per workgroup, each taking every W-th key: E = 128 needs ~400 VGPRs
+// (one wave per SIMD, 4 waves); E = 64 fits in 256 (two per SIMD, 8 waves).
+template <int E>
+struct F32Waves {
+  static constexpr int W = E == 128 ? 4 : 8;
+};
 
 struct PrefillF32Params {
   const float* q;
@@ -34,18 +44,26 @@ struct PrefillF32Params {
 };
 
 template <int E, bool RBF>
-__global__ __launch_bounds__(BQ) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_f32_kernel(PrefillF32Params p) {
+__global__ __launch_bounds__(BQ * F32Waves<E>::W) __attribute__((amdgpu_waves_per_eu(F32Waves<E>::W / 4,
+                                                                                    F32Waves<E>::W / 4)))
+void prefill_f32_kernel(PrefillF32Params p) {
+  constexpr int W = F32Waves<E>::W;
   __shared__ __attribute__((aligned(16))) float sK[BK * E];
   __shared__ __attribute__((aligned(16))) float sV[BK * E];
   __shared__ float sBias[BK];
+  // Partial states of waves 1 .. W-1: per row max, sum and E accumulator values.
+  __shared__ float sM[W - 1][BQ], sL[W - 1][BQ];
+  __shared__ __attribute__((aligned(16))) float sAcc[W - 1][E][BQ];
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qt = blockIdx.x % p.num_q_tiles;
   const int nh = blockIdx.x / p.num_q_tiles;
   const int h = nh % p.Hq, n = nh / p.Hq;
   const int kh = h / (p.Hq / p.Hkv);
   const int i0 = qt * BQ;
-  const int qi = i0 + tid;
+  const int qi = i0 + lane;
   const bool qvalid = qi < p.L;
 
   float q[E], acc[E];
@@ -57,8 +75,9 @@ __global__ __launch_bounds__(BQ) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     qn2 = __builtin_fmaf(q[e], q[e], qn2);
     acc[e] = 0.f;
   }
+  // The sink seeds wave 0's state only (it enters the denominator once).
   float m = kNegInf, lsum = 0.f;
-  if (p.sink) {
+  if (p.sink && wave == 0) {
     float s0 = p.sink[h];
     if (RBF) s0 += p.gamma * qn2;
     m = s0 * kLog2e;
@@ -87,7 +106,7 @@ __global__ __launch_bounds__(BQ) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       kc = min(BK, p.S - j0);
     }
     __syncthreads();
-    for (int idx = tid; idx < BK * E / 4; idx += BQ) {
+    for (int idx = tid; idx < BK * E / 4; idx += BQ * W) {
       const int row = (idx * 4) / E, col = (idx * 4) % E;
       f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
       if (row < kc) {
@@ -103,10 +122,10 @@ __global__ __launch_bounds__(BQ) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       for (int e = 0; e < E; ++e) ss = __builtin_fmaf(sK[tid * E + e], sK[tid * E + e], ss);
       sBias[tid] = p.c_bias * ss;
     }
-    __syncthreads();
+    if (RBF) __syncthreads();
 
 #pragma unroll 1
-    for (int kt = 0; kt < BK; ++kt) {
+    for (int kt = wave; kt < BK; kt += W) {
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) d = __builtin_fmaf(q[e], sK[kt * E + e], d);
@@ -144,6 +163,32 @@ __global__ __launch_bounds__(BQ) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     }
   }
 
+  // Merge: waves 1 .. W-1 publish their states, wave 0 combines them.
+  if (wave > 0) {
+    sM[wave - 1][lane] = m;
+    sL[wave - 1][lane] = lsum;
+#pragma unroll
+    for (int e = 0; e < E; ++e) sAcc[wave - 1][e][lane] = acc[e];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float mt = m;
+#pragma unroll
+  for (int w = 0; w < W - 1; ++w) mt = fmaxf(mt, sM[w][lane]);
+  const float mu = mt == kNegInf ? 0.f : mt;
+  const float a0 = exp2f(m - mu);
+  lsum *= a0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] *= a0;
+#pragma unroll
+  for (int w = 0; w < W - 1; ++w) {
+    const float aw = exp2f(sM[w][lane] - mu);
+    lsum = __builtin_fmaf(sL[w][lane], aw, lsum);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(sAcc[w][e][lane], aw, acc[e]);
+  }
+  m = mt;
+
   if (qvalid) {
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     float* orow = p.o + (((size_t)n * p.Hq + h) * p.L + qi) * E;
@@ -164,7 +209,7 @@ __global__ __launch_bounds__(BQ) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 template <int E, bool RBF>
 hipError_t launch_t(const PrefillF32Params& p, hipStream_t stream) {
   const long long blocks = (long long)p.num_q_tiles * p.N * p.Hq;
-  hipLaunchKernelGGL((prefill_f32_kernel<E, RBF>), dim3((unsigned)blocks), dim3(BQ), 0, stream, p);
+  hipLaunchKernelGGL((prefill_f32_kernel<E, RBF>), dim3((unsigned)blocks), dim3(BQ * F32Waves<E>::W), 0, stream, p);
   return hipGetLastError();
 }
 
