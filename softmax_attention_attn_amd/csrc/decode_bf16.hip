@@ -18,6 +18,12 @@
 // row per load).  V is loaded as whole 256-byte rows -- lane (m, g) takes dims
 // 8m..8m+7 of 8 keys -- and transposed in registers, so the 8 PV products of a
 // step each produce the 16 dims {8m + j}.
+//
+// Indexed mode (SOCKET sparse decode): every query head attends to its own
+// list of key rows, so a workgroup serves one query head (MFMA column 0) and
+// first copies its split's part of the list (at most kDecodeIndexMax rows)
+// into LDS, where the row addresses of every step are then read without a
+// global-memory round trip.
 #include "device_common.h"
 #include "kernels.h"
 

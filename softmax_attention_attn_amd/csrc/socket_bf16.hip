@@ -17,9 +17,11 @@
 //  - socket_prob_kernel: per query head, y = W q and, per table, the
 //    probability of every bucket: the softmax over the 2^bits sign patterns of
 //    sum_b s_b y_b / tau factorises into prod_b sigmoid(2 s_b y_b / tau).
-//  - socket_score_kernel: one thread per key of a (batch, kv head); the bucket
-//    probabilities of the group's query heads sit in LDS, so the key's codes
-//    are read once for all of them.
+//  - socket_score_fast / socket_score_kernel: threads own keys of a (batch,
+//    kv head); the bucket probabilities of the group's query heads sit in LDS,
+//    packed per (table, code), so the key's codes are read once for all of
+//    them (the fast kernel for group sizes 1/2/4/8/16 and tables a multiple of
+//    16, the other for any shape).
 //  - socket_select_kernel: one workgroup per query head; exact top_k on the
 //    float bits (scores are >= 0, so their bit patterns order like the
 //    values): a sampled bracket narrows the threshold to a few thousand
@@ -36,9 +38,9 @@ namespace {
 constexpr int kMaxProj = 512;  // tables * bits
 constexpr int SEL_T = 1024;    // threads of the selection workgroup
 
-// Hashing: one thread per key, its row in registers.  The hyperplanes of up
-// to HASH_TG tables sit in LDS as [table][element][BP] (BP = bits padded to 4
-// or 8, padding weights zero), so every element's weights of all the table's
+// Hashing: one thread per key, its row in registers.  The hyperplanes of the
+// TG tables that fit in HASH_LDS bytes sit in LDS as [table][element][BP]
+// (BP = bits padded to 4 or 8, padding weights zero), so every element's weights of all the table's
 // hyperplanes are one broadcast LDS read.  Each projection is a float32 fused
 // multiply-add chain over the elements in order, starting from zero.
 constexpr int HASH_LDS = 32 * 1024;
