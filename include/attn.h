@@ -240,14 +240,21 @@ size_t attn_stream_decode_workspace_bytes(int N, int Hq, int Hkv, int E, int n_s
  * caller (the method is data-independent: any fixed random draw).
  *
  * attn_socket_hash -- prefill step: for every key row of k (N, Hkv, S, E, bf16)
- * and table t, bit b of buckets[(n,kh,j)*tables + t] is set iff the float32
+ * and table t, bit b of the code of (key j, table t) is set iff the float32
  * projection proj[t*bits + b] . k_j (fused multiply-adds in element order) is
- * > 0; vnorm (N, Hkv, S) float32 receives |v_j| (may be NULL, then v may be NULL).
- * 1 <= tables <= 64, 1 <= bits <= 8.
+ * > 0.  buckets: (N, Hkv, S, C) bytes with C = attn_socket_code_bytes(tables,
+ * bits): with bits <= 4 two codes share a byte (table t in the low nibble of
+ * byte t/2 when t is even, in the high nibble when t is odd, an unused high
+ * nibble 0), else byte t holds table t.  vnorm (N, Hkv, S) float32 receives
+ * |v_j| (may be NULL, then v may be NULL).  1 <= tables <= 64, 1 <= bits <= 8.
  */
 int attn_socket_hash(attn_dtype dt, int N, int Hkv, int S, int E, int tables, int bits,
                      const void* k, const void* v, const float* proj,
                      unsigned char* buckets, float* vnorm, void* stream);
+
+/* Bytes of bucket codes per key for these sizes (ATTN_ERR_ARG if tables or
+ * bits is out of range). */
+int attn_socket_code_bytes(int tables, int bits);
 
 /*
  * attn_socket_decode -- decode step for q (N, Hq, 1, E): per query head, the

@@ -35,7 +35,7 @@ MODES = {"dot": 0, "rbf": 1}
 
 EXPORTS = ("attn_fwd", "attn_fwd_biased", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_num_splits", "attn_decode_workspace_bytes",
            "attn_stream_append", "attn_stream_decode", "attn_stream_decode_workspace_bytes",
-           "attn_socket_hash", "attn_socket_decode", "attn_socket_decode_workspace_bytes",
+           "attn_socket_hash", "attn_socket_code_bytes", "attn_socket_decode", "attn_socket_decode_workspace_bytes",
            "attn_status_string", "attn_last_error")
 
 
@@ -78,6 +78,8 @@ def load() -> ctypes.CDLL:
         lib.attn_stream_decode.argtypes = [I, I, I, I, I, I, I, LL, P, P, P, I, F, F, P, P, P, I, P, Z, P]
         lib.attn_stream_decode_workspace_bytes.restype = Z
         lib.attn_stream_decode_workspace_bytes.argtypes = [I, I, I, I, I, I, LL, I]
+        lib.attn_socket_code_bytes.restype = I
+        lib.attn_socket_code_bytes.argtypes = [I, I]
         lib.attn_socket_hash.restype = I
         lib.attn_socket_hash.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P]
         lib.attn_socket_decode.restype = I
@@ -325,16 +327,33 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
     return dq, dk, dv, dsink
 
 
+def socket_code_bytes(tables: int, bits: int) -> int:
+    """Bytes of bucket codes per key (attn_socket_code_bytes)."""
+    r = load().attn_socket_code_bytes(int(tables), int(bits))
+    _check(min(r, 0))
+    return r
+
+
+def unpack_codes(buckets: torch.Tensor, tables: int, bits: int) -> torch.Tensor:
+    """Bucket codes (..., C) as stored by socket_hash -> one code per table (..., tables) uint8."""
+    if bits > 4:
+        return buckets[..., :tables]
+    lo, hi = buckets & 15, buckets >> 4
+    return torch.stack((lo, hi), dim=-1).flatten(-2)[..., :tables]
+
+
 def socket_hash(k: torch.Tensor, v: torch.Tensor, proj: torch.Tensor, *, tables: int, bits: int,
                 stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """SOCKET prefill hashing through attn_socket_hash: bucket codes (N, Hkv, S, tables) uint8 and
-    value norms (N, Hkv, S) float32 of a bf16 key/value cache; proj (tables*bits, E) float32."""
+    """SOCKET prefill hashing through attn_socket_hash: bucket codes (N, Hkv, S, C) uint8 with
+    C = socket_code_bytes(tables, bits) (codes of at most 4 bits packed two per byte, see
+    unpack_codes) and value norms (N, Hkv, S) float32 of a bf16 key/value cache; proj
+    (tables*bits, E) float32."""
     if k.dim() != 4 or not k.is_contiguous() or k.shape != v.shape or not v.is_contiguous():
         raise ValueError("k and v must be contiguous 4-D tensors of one shape")
     if proj.dtype != torch.float32 or not proj.is_contiguous() or proj.shape != (tables * bits, k.shape[3]):
         raise ValueError(f"proj must be a contiguous float32 ({tables * bits}, {k.shape[3]}) tensor")
     N, Hkv, S, E = k.shape
-    buckets = torch.empty((N, Hkv, S, tables), dtype=torch.uint8, device=k.device)
+    buckets = torch.empty((N, Hkv, S, socket_code_bytes(tables, bits)), dtype=torch.uint8, device=k.device)
     vnorm = torch.empty((N, Hkv, S), dtype=torch.float32, device=k.device)
     rc = load().attn_socket_hash(_dtype_code(k), N, Hkv, S, E, int(tables), int(bits), _ptr(k), _ptr(v),
                                  _ptr(proj), _ptr(buckets), _ptr(vnorm), _stream(k.device, stream))

@@ -244,6 +244,12 @@ int socket_check(int N, int Hq, int Hkv, int S, int E, int tables, int bits) {
   return ATTN_OK;
 }
 
+int attn_socket_code_bytes(int tables, int bits) {
+  if (tables < 1 || tables > 64 || bits < 1 || bits > 8)
+    return fail(ATTN_ERR_ARG, "tables=%d (1..64) or bits=%d (1..8) out of range", tables, bits);
+  return attn_impl::socket_code_bytes(tables, bits);
+}
+
 int attn_socket_hash(attn_dtype dt, int N, int Hkv, int S, int E, int tables, int bits, const void* k, const void* v,
                      const float* proj, unsigned char* buckets, float* vnorm, void* stream) {
   if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "SOCKET hashing is implemented for bf16 keys only");

@@ -73,11 +73,16 @@ size_t backward_workspace_bytes(int N, int Hq, int L);
 // Longest key list one split of an indexed decode takes (it is staged in LDS).
 constexpr int kDecodeIndexMax = 4096;
 
+// Bytes of bucket codes per key: codes of at most 4 bits are packed two per
+// byte (table t in the low nibble of byte t/2 when t is even, else the high
+// nibble); wider codes take one byte per table.
+__host__ __device__ inline int socket_code_bytes(int tables, int bits) { return bits <= 4 ? (tables + 1) / 2 : tables; }
+
 struct SocketHashArgs {
   const void* k;
   const void* v;
   const float* proj;       // (tables*bits, E)
-  uint8_t* buckets;        // (N, Hkv, S, tables)
+  uint8_t* buckets;        // (N, Hkv, S, socket_code_bytes(tables, bits))
   float* vnorm;            // (N, Hkv, S)
   int N, Hkv, S, E, tables, bits;
 };

@@ -70,8 +70,13 @@ __global__ __launch_bounds__(256) void socket_hash_kernel(attn_impl::SocketHashA
     for (int c = 0; c < E / 8; ++c) ss += sumsq8(*reinterpret_cast<const u32x4*>(vrow + 8 * c));
     a.vnorm[j] = sqrtf(ss);
   }
-  const bool words = (a.tables & 3) == 0 && (reinterpret_cast<uintptr_t>(a.buckets) & 3) == 0;
-  uint8_t* dst = a.buckets + (size_t)(ok ? j : 0) * a.tables;
+  // Codes are gathered into 32-bit words (8 four-bit or 4 eight-bit codes),
+  // stored whole when every key's code bytes are whole aligned words.
+  const int cw = a.bits <= 4 ? 4 : 8;  // bits per stored code
+  const int per = 32 / cw;              // codes per word
+  const int cbytes = attn_impl::socket_code_bytes(a.tables, a.bits);
+  const bool words = (cbytes & 3) == 0 && (reinterpret_cast<uintptr_t>(a.buckets) & 3) == 0;
+  uint8_t* dst = a.buckets + (size_t)(ok ? j : 0) * cbytes;
   uint32_t word = 0;
   for (int t0 = 0; t0 < a.tables; t0 += TG) {
     const int tn = min(TG, a.tables - t0);
@@ -102,14 +107,18 @@ __global__ __launch_bounds__(256) void socket_hash_kernel(attn_impl::SocketHashA
       for (int b = 0; b < BP; ++b)
         if (b < a.bits && x[b] > 0.f) code |= 1u << b;
       const int t = t0 + tt;
-      if (words) {
-        word |= code << (8 * (t & 3));
-        if ((t & 3) == 3) {
-          if (ok) *reinterpret_cast<uint32_t*>(dst + (t - 3)) = word;
-          word = 0;
+      word |= code << (cw * (t % per));
+      if (t % per == per - 1 || t == a.tables - 1) {  // a word is complete
+        const int wi = t / per;
+        if (ok) {
+          if (words) {
+            *reinterpret_cast<uint32_t*>(dst + 4 * wi) = word;
+          } else {
+            const int nb = min(4, cbytes - 4 * wi);
+            for (int b = 0; b < nb; ++b) dst[4 * wi + b] = (uint8_t)(word >> (8 * b));
+          }
         }
-      } else if (ok) {
-        dst[t] = (uint8_t)code;
+        word = 0;
       }
     }
   }
@@ -175,10 +184,10 @@ __device__ __forceinline__ void score_lookup(const float* __restrict__ sP, int r
 
 constexpr int SCORE_KPT = 4;  // keys per thread of the score kernel
 
-// Generic scoring (any group size, table count and alignment): one workgroup
-// scores 256 * SCORE_KPT keys of one (batch, kv head) for all G query heads of
-// its group.  LDS holds the group's bucket probabilities as
-// [G/P][tables][2^bits][P].
+// Generic scoring (any group size, table count and alignment; codes read a
+// byte at a time): one workgroup scores 256 * SCORE_KPT keys of one (batch, kv
+// head) for all G query heads of its group.  LDS holds the group's bucket
+// probabilities as [G/P][tables][2^bits][P].
 template <int P>
 __global__ __launch_bounds__(256) void socket_score_kernel(attn_impl::SocketSelectArgs a) {
   extern __shared__ float sP[];
@@ -194,24 +203,20 @@ __global__ __launch_bounds__(256) void socket_score_kernel(attn_impl::SocketSele
     sP[((g / P) * per + r) * P + g % P] = src[i];
   }
   __syncthreads();
-  const uintptr_t base = reinterpret_cast<uintptr_t>(a.buckets);
+  const int cbytes = attn_impl::socket_code_bytes(a.tables, a.bits);
+  const bool packed = a.bits <= 4;
   const size_t row0 = (size_t)n * a.Hq + (size_t)kh * G;
   for (int kk = 0; kk < SCORE_KPT; ++kk) {
     const int j = (blockIdx.x * SCORE_KPT + kk) * 256 + threadIdx.x;
     if (j >= a.S) break;
     const size_t key = (size_t)nk * a.S + j;
-    const uint8_t* code = a.buckets + key * a.tables;
+    const uint8_t* code = a.buckets + key * cbytes;
     float acc[16];
 #pragma unroll
     for (int g = 0; g < 16; ++g) acc[g] = 0.f;
-    if ((a.tables & 3) == 0 && (base & 3) == 0) {
-      for (int t0 = 0; t0 < a.tables; t0 += 4) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(code + t0);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) score_lookup<P>(sP, (t0 + b) * nb + ((w >> (8 * b)) & 0xffu), ngrp, per, acc);
-      }
-    } else {
-      for (int t = 0; t < a.tables; ++t) score_lookup<P>(sP, t * nb + code[t], ngrp, per, acc);
+    for (int t = 0; t < a.tables; ++t) {
+      const int c = packed ? (code[t >> 1] >> (4 * (t & 1))) & 15 : code[t];
+      score_lookup<P>(sP, t * nb + c, ngrp, per, acc);
     }
     const float nv = a.vnorm[key];
 #pragma unroll
@@ -241,9 +246,10 @@ __device__ __forceinline__ void lookup_load(const float* e, float (&x)[P]) {
   }
 }
 
-// Scoring for the common shapes: group size GT in {1, 2, 4, 8, 16}, tables a
-// multiple of 16 (at most 64), 16-byte aligned codes; NB = 2^bits when fixed
-// at build time (constant LDS offsets), else 0.  A workgroup stages the
+// Scoring for the common shapes: group size GT in {1, 2, 4, 8, 16}, code
+// bytes per key a multiple of 16 (at most 64 tables: 16-byte chunks of 16 byte
+// codes, or of 32 packed 4-bit codes when PK), 16-byte aligned codes; NB =
+// 2^bits when fixed at build time (constant LDS offsets), else 0.  A workgroup stages the
 // group's probabilities once and scores FAST_ROUNDS * 256 * FAST_KPT keys; in
 // each round every code and norm of the thread's keys is loaded first, then per
 // 16-table chunk, key and packed head group 16 independent LDS reads are
@@ -251,7 +257,7 @@ __device__ __forceinline__ void lookup_load(const float* e, float (&x)[P]) {
 constexpr int FAST_KPT = 2;   // keys per thread per round
 constexpr int FAST_ROUNDS = 4;  // rounds per workgroup (amortise the LDS staging)
 
-template <int GT, int NB>
+template <int GT, int NB, bool PK>
 __global__ __launch_bounds__(256) void socket_score_fast(attn_impl::SocketSelectArgs a) {
   constexpr int P = GT % 4 == 0 ? 4 : (GT % 2 == 0 ? 2 : 1);
   constexpr int NG = GT / P;
@@ -267,21 +273,23 @@ __global__ __launch_bounds__(256) void socket_score_fast(attn_impl::SocketSelect
     sP[((g / P) * per + r) * P + g % P] = src[i];
   }
   __syncthreads();
-  const int nch = a.tables / 16;
+  constexpr int CPC = PK ? 32 : 16;  // codes per 16-byte chunk
+  constexpr int MAXCH = 64 / CPC;    // chunks for 64 tables
+  const int nch = a.tables / CPC;
   const size_t row0 = (size_t)n * a.Hq + (size_t)kh * GT;  // first query head of the group
   for (int it = 0; it < FAST_ROUNDS; ++it) {
     const int blk = blockIdx.x * FAST_ROUNDS + it;
     if (blk * KPT * 256 >= a.S) break;
-    u32x4 w[KPT][4];
+    u32x4 w[KPT][MAXCH];
     float nv[KPT];
 #pragma unroll
     for (int kk = 0; kk < KPT; ++kk) {
       const int j = (blk * KPT + kk) * 256 + threadIdx.x;
       const bool ok = j < a.S;
       const size_t key = (size_t)nk * a.S + (ok ? j : 0);
-      const u32x4* c16 = reinterpret_cast<const u32x4*>(a.buckets + key * a.tables);
+      const u32x4* c16 = reinterpret_cast<const u32x4*>(a.buckets + key * (a.tables * 16 / CPC));
 #pragma unroll
-      for (int c = 0; c < 4; ++c) w[kk][c] = (ok && c < nch) ? c16[c] : u32x4{0u, 0u, 0u, 0u};
+      for (int c = 0; c < MAXCH; ++c) w[kk][c] = (ok && c < nch) ? c16[c] : u32x4{0u, 0u, 0u, 0u};
       nv[kk] = ok ? a.vnorm[key] : 0.f;
     }
     float acc[KPT][GT];
@@ -290,22 +298,28 @@ __global__ __launch_bounds__(256) void socket_score_fast(attn_impl::SocketSelect
 #pragma unroll
       for (int g = 0; g < GT; ++g) acc[kk][g] = 0.f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < MAXCH; ++c) {
       if (c < nch) {
 #pragma unroll
         for (int kk = 0; kk < KPT; ++kk) {
 #pragma unroll
           for (int g = 0; g < NG; ++g) {
-            float x[16][P];
 #pragma unroll
-            for (int b = 0; b < 16; ++b) {
-              const int code = (int)((w[kk][c][b / 4] >> (8 * (b % 4))) & 0xffu);
-              lookup_load<P>(sP + ((size_t)g * per + (16 * c + b) * nb + code) * P, x[b]);
+            for (int h16 = 0; h16 < CPC / 16; ++h16) {
+              // 16 tables of this chunk: codes are bytes, or nibbles of 2 words.
+              float x[16][P];
+#pragma unroll
+              for (int b = 0; b < 16; ++b) {
+                const int tb = 16 * h16 + b;  // table within the chunk
+                const int code = PK ? (int)((w[kk][c][tb / 8] >> (4 * (tb % 8))) & 0xfu)
+                                    : (int)((w[kk][c][tb / 4] >> (8 * (tb % 4))) & 0xffu);
+                lookup_load<P>(sP + ((size_t)g * per + (CPC * c + tb) * nb + code) * P, x[b]);
+              }
+#pragma unroll
+              for (int b = 0; b < 16; ++b)
+#pragma unroll
+                for (int q = 0; q < P; ++q) acc[kk][g * P + q] += x[b][q];
             }
-#pragma unroll
-            for (int b = 0; b < 16; ++b)
-#pragma unroll
-              for (int q = 0; q < P; ++q) acc[kk][g * P + q] += x[b][q];
           }
         }
       }
@@ -326,9 +340,11 @@ hipError_t launch_score_fast(const attn_impl::SocketSelectArgs& a, size_t lds, h
   constexpr int KPT = FAST_KPT * FAST_ROUNDS;
   const dim3 grid((unsigned)((a.S + 256 * KPT - 1) / (256 * KPT)), (unsigned)(a.N * a.Hkv));
   if (a.bits == 4)
-    hipLaunchKernelGGL((socket_score_fast<GT, 16>), grid, dim3(256), lds, stream, a);
+    hipLaunchKernelGGL((socket_score_fast<GT, 16, true>), grid, dim3(256), lds, stream, a);
+  else if (a.bits < 4)
+    hipLaunchKernelGGL((socket_score_fast<GT, 0, true>), grid, dim3(256), lds, stream, a);
   else
-    hipLaunchKernelGGL((socket_score_fast<GT, 0>), grid, dim3(256), lds, stream, a);
+    hipLaunchKernelGGL((socket_score_fast<GT, 0, false>), grid, dim3(256), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -842,7 +858,8 @@ hipError_t launch_socket_select_bf16(const SocketSelectArgs& a, hipStream_t stre
   if (e != hipSuccess) return e;
   const int G = a.Hq / a.Hkv;
   const size_t lds = socket_lds_bytes(G, a.tables, a.bits);
-  const bool fast = (a.tables & 15) == 0 && (reinterpret_cast<uintptr_t>(a.buckets) & 15) == 0;
+  const bool fast = (a.tables % (a.bits <= 4 ? 32 : 16)) == 0 && a.tables <= 64 &&
+                    (reinterpret_cast<uintptr_t>(a.buckets) & 15) == 0;
   if (fast && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16)) {
     e = G == 1 ? launch_score_fast<1>(a, lds, stream)
       : G == 2 ? launch_score_fast<2>(a, lds, stream)

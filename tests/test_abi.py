@@ -231,6 +231,15 @@ def test_stream_decode_workspace_matches_decode_over_kept_rows(lib):
     assert lib.attn_stream_decode_workspace_bytes(2, 8, 2, 128, 4, 0, 5, 0) == 0
 
 
+def test_socket_code_bytes(lib):
+    assert lib.attn_socket_code_bytes(64, 4) == 32  # 4-bit codes: two per byte
+    assert lib.attn_socket_code_bytes(7, 3) == 4
+    assert lib.attn_socket_code_bytes(8, 5) == 8    # wider codes: a byte per table
+    assert lib.attn_socket_code_bytes(1, 8) == 1
+    for t, b in ((0, 4), (65, 4), (4, 0), (4, 9)):
+        assert lib.attn_socket_code_bytes(t, b) == -8
+
+
 def shash(lib, dt=0, N=1, Hkv=2, S=16, E=64, tables=4, bits=4, k=A, v=A, proj=A, buckets=A, vnorm=A):
     return lib.attn_socket_hash(dt, N, Hkv, S, E, tables, bits, k, v, proj, buckets, vnorm, None)
 

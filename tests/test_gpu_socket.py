@@ -41,6 +41,12 @@ CASES = [
     (W("rbf_e64_lognormal_keys", 1, 4, 4, 2500, 64, mode="rbf", k_dist="dir_lognormal"), 16, 4, 2.0, 333, (0,)),
     (W("gqa16_many_tables", 1, 16, 1, 1500, 64), 64, 2, 8.0, 64, (0,)),
     (W("ragged_small_budget_e128", 3, 4, 2, 777, 128, sink=True), 12, 5, 1.0, 17, (0, 2)),
+    # packed 4-bit codes through the fast scorer (32 tables = one 16-byte chunk per key)
+    (W("packed_fast_gqa4_e128", 2, 8, 2, 2048, 128, sink=True), 32, 4, 4.0, 150, (0,)),
+    # packed 3-bit codes, odd table count (the last byte holds one code)
+    (W("packed_odd_tables_e64", 1, 2, 1, 1000, 64), 7, 3, 2.0, 50, (0,)),
+    # byte codes through the fast scorer
+    (W("bytes_fast_gqa2_e64", 1, 4, 2, 1200, 64), 16, 5, 4.0, 100, (0,)),
 ]
 
 
@@ -52,7 +58,10 @@ def _run(w, tables, bits, tau, top_k, splits, inp=None):
     bk, vn = attn.socket_hash(k, v, proj, tables=tables, bits=bits)
     b_ref, vn_ref = oracle.socket_hash(inp.k, inp.v, proj_np, tables, bits)
     torch.cuda.synchronize()
-    assert np.array_equal(bk.cpu().numpy(), b_ref), "bucket codes differ"
+    assert bk.shape[-1] == (tables + 1) // 2 if bits <= 4 else tables
+    if bits <= 4 and tables % 2:  # the unused high nibble of the last byte is zero
+        assert not (bk[..., -1] >> 4).any()
+    assert np.array_equal(attn.unpack_codes(bk, tables, bits).cpu().numpy(), b_ref), "bucket codes differ"
     assert np.max(np.abs(vn.cpu().numpy() - vn_ref) / np.maximum(vn_ref, 1e-30)) < 1e-5
     o_ref, l_ref, sel_ref, sc_ref = oracle.socket_decode(inp.q, inp.k, inp.v, proj_np, b_ref, vn_ref, tables=tables,
                                                          bits=bits, tau=tau, top_k=top_k, mode=w.mode,

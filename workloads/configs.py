@@ -199,9 +199,14 @@ class SocketWorkload:
 
 
 # The long-context decode shape at about 33x sparsity (the page's setting), 64 tables of
-# 4-bit codes (64 bytes of codes + a 4-byte norm per key: ~13% of the K and V bytes).
+# 4-bit codes (32 bytes of packed codes + a 4-byte norm per key: 7% of the K and V bytes).
 SOCKET1 = SocketWorkload("socket_decode_sink_bf16_8x32to8x131072x128_k3972", C5, 64, 4, 4.0, 3972)
 SOCKET_BY_NAME = {SOCKET1.name: SOCKET1}
+
+
+def socket_code_bytes(tables: int, bits: int) -> int:
+    """Bytes of bucket codes per key: codes of at most 4 bits are stored two per byte."""
+    return (tables + 1) // 2 if bits <= 4 else tables
 
 
 def socket_bytes(sw: SocketWorkload) -> float:
@@ -209,5 +214,5 @@ def socket_bytes(sw: SocketWorkload) -> float:
     rows read once per query head, q read and o / lse written."""
     w = sw.base
     keys = w.N * w.Hkv * w.S
-    return float(keys * (sw.tables + 4) + 2 * w.N * w.Hq * sw.top_k * w.E * 2 + 2 * w.N * w.Hq * w.E * 2 +
-                 w.N * w.Hq * 4)
+    return float(keys * (socket_code_bytes(sw.tables, sw.bits) + 4) + 2 * w.N * w.Hq * sw.top_k * w.E * 2 +
+                 2 * w.N * w.Hq * w.E * 2 + w.N * w.Hq * 4)
