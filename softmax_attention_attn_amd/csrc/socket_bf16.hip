@@ -369,21 +369,23 @@ __device__ __forceinline__ int wave_sum_int(int v) {
   return v;
 }
 
-// Exclusive prefix sum over the workgroup of one int per thread (LDS
-// Hillis-Steele scan); every thread must call it.
+// Exclusive prefix sum over the workgroup of one int per thread: a shuffle
+// scan inside each wave, then the wave totals through LDS (two barriers);
+// every thread must call it.  buf holds at least SEL_WAVES ints.
 __device__ __forceinline__ int block_exclusive_scan(int* buf, int v) {
-  const int tid = threadIdx.x;
-  buf[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < SEL_T; off <<= 1) {
-    const int add = tid >= off ? buf[tid - off] : 0;
-    __syncthreads();
-    buf[tid] += add;
-    __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
   }
-  const int excl = buf[tid] - v;
+  if (lane == 63) buf[wave] = x;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += buf[w];
   __syncthreads();  // buf is reused by the next call
-  return excl;
+  return base + x - v;
 }
 
 // Finds, among `nbins` bins whose counts are in hist, the bin holding the
