@@ -5,7 +5,9 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
+import torch
 
 import softmax_attention_attn_amd as attn
 
@@ -238,6 +240,22 @@ def test_socket_code_bytes(lib):
     assert lib.attn_socket_code_bytes(1, 8) == 1
     for t, b in ((0, 4), (65, 4), (4, 0), (4, 9)):
         assert lib.attn_socket_code_bytes(t, b) == -8
+
+
+def test_unpack_codes_reads_the_nibble_layout():
+    """Codes of at most 4 bits: table t in the low nibble of byte t/2 for even t, the high
+    nibble for odd t (include/attn.h, attn_socket_hash); wider codes: byte t."""
+    rng = np.random.default_rng(3)
+    for tables, bits in ((7, 3), (64, 4), (12, 5)):
+        codes = rng.integers(0, 1 << bits, size=(2, 5, tables)).astype(np.uint8)
+        if bits <= 4:
+            packed = np.zeros((2, 5, (tables + 1) // 2), np.uint8)
+            for t in range(tables):
+                packed[..., t // 2] |= codes[..., t] << (4 * (t % 2))
+        else:
+            packed = codes
+        got = attn.unpack_codes(torch.from_numpy(packed), tables, bits).numpy()
+        assert np.array_equal(got, codes)
 
 
 def shash(lib, dt=0, N=1, Hkv=2, S=16, E=64, tables=4, bits=4, k=A, v=A, proj=A, buckets=A, vnorm=A):
