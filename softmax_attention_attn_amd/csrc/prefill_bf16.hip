@@ -137,13 +137,18 @@ void prefill_bf16_kernel(PrefillParams p) {
   constexpr int KCH = BN * ECH / NT;       // K chunks per thread (RBF register staging)
   static_assert(IPW * RPI * 4 == BN, "tile must split into whole 1 KB loads per wave");
   static_assert(KCH * NT == BN * ECH, "K staging must tile evenly");
-  static_assert(BM * OSTR * 2 <= 2 * 2 * TILEB, "epilogue staging must fit the tile buffers");
+  static_assert(2 * 32 * OSTR * 2 <= 2 * TILEB, "epilogue staging of two waves must fit one tile buffer");
 
   // [buf][K tile | V tile], each tile row-major with swizzled 16-byte chunks.
-  __shared__ __attribute__((aligned(16))) uint8_t sKV[2 * 2 * TILEB];
+  // The two buffers are separate LDS objects: where the buffer index is a
+  // compile-time constant, the compiler can then tell a read of one buffer from
+  // the LDS-direct loads in flight into the other and does not make the
+  // transposing V reads wait for them.
+  __shared__ __attribute__((aligned(16))) uint8_t sKV0[2 * TILEB];
+  __shared__ __attribute__((aligned(16))) uint8_t sKV1[2 * TILEB];
   __shared__ __attribute__((aligned(16))) float sBias[2][BN];
-  auto k_tile = [&](int buf) { return sKV + buf * 2 * TILEB; };
-  auto v_tile = [&](int buf) { return sKV + buf * 2 * TILEB + TILEB; };
+  auto k_tile = [&](int buf) { return buf ? sKV1 : sKV0; };
+  auto v_tile = [&](int buf) { return (buf ? sKV1 : sKV0) + TILEB; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -235,7 +240,7 @@ void prefill_bf16_kernel(PrefillParams p) {
 
   u32x4 kreg[KCH];  // RBF only: K chunks on their way to LDS
 
-  auto tile_keys = [&](int t, int& j0, int& kc) {
+  auto tile_keys = [&](int t, int& j0, int& kc) __attribute__((always_inline)) {
     if (t < n_reg_tiles) {
       j0 = t * BN;
       kc = min(BN, p.n_reg - j0);
@@ -247,7 +252,7 @@ void prefill_bf16_kernel(PrefillParams p) {
 
   // Request tile t into buffer `buf`.  Rows past the tile's last key are loaded
   // anyway (real keys of the slice, or zeros past its end) and masked later.
-  auto issue_tile = [&](int t, int buf) {
+  auto issue_tile = [&](int t, int buf) __attribute__((always_inline)) {
     int j0, kc;
     tile_keys(t, j0, kc);
     const uint32_t tb = (uint32_t)j0 * ROWB;
@@ -269,7 +274,7 @@ void prefill_bf16_kernel(PrefillParams p) {
   // Complete the requested tile in `buf`: in RBF mode write the K registers
   // (swizzled) and the per-key bias c_bias * |k|^2; then wait until this wave's
   // LDS-direct requests have landed.
-  auto finish_tile = [&](int buf) {
+  auto finish_tile = [&](int buf) __attribute__((always_inline)) {
     if (RBF) {
 #pragma unroll
       for (int i = 0; i < KCH; ++i) {
@@ -284,7 +289,7 @@ void prefill_bf16_kernel(PrefillParams p) {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   };
 
-  auto compute_tile = [&](int t, int buf, auto masked_tag) {
+  auto compute_tile = [&](int t, int buf, auto masked_tag) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     int j0, kc;
     tile_keys(t, j0, kc);
@@ -415,7 +420,7 @@ void prefill_bf16_kernel(PrefillParams p) {
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(st[b][r], st[b][r + 1]));
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, st[b][r]), st[b][r + 1]);  // v_max3 chain
     mx = pair32_max(mx);
     if (FAST) mx = (mx == kNegInf) ? kNegInf : mx * p.c_logit;
 
@@ -489,28 +494,53 @@ void prefill_bf16_kernel(PrefillParams p) {
   // Tile t lives in buffer t % 2: right after the barrier that frees the other
   // buffer, tile t+1 is requested into it; tile t is consumed; the wave waits
   // for its own requests; one barrier publishes tile t+1 to every wave.
-  auto step = [&](int t, auto masked_tag) {
-    if (t + 1 < T) issue_tile(t + 1, (t + 1) & 1);
-    compute_tile(t, t & 1, masked_tag);
-    if (t + 1 < T) finish_tile((t + 1) & 1);
+  // The buffer index is a compile-time constant at each call (the loops below
+  // take tiles in pairs), so LDS addresses become base registers plus
+  // immediate offsets instead of per-tile address arithmetic.
+  // Both buffers are free at the start, so in dot mode (K straight to LDS)
+  // tile 1 is requested together with tile 0 and its latency overlaps tile 0's.
+  const bool pre1 = !RBF && T > 1;
+  auto step = [&](int t, int buf, auto masked_tag) __attribute__((always_inline)) {
+    if (t + 1 < T && !(pre1 && t == 0)) issue_tile(t + 1, buf ^ 1);
+    compute_tile(t, buf, masked_tag);
+    if (t + 1 < T) finish_tile(buf ^ 1);
     __syncthreads();
+  };
+  auto run = [&](int ta, int tb, auto masked_tag) __attribute__((always_inline)) {
+    int t = ta;
+    if constexpr (UB != kBiasNone) {  // no registers to spare for the doubled loop body
+      for (; t < tb; ++t) step(t, t & 1, masked_tag);
+      return;
+    }
+    if (t < tb && (t & 1)) step(t++, 1, masked_tag);
+    for (; t + 1 < tb; t += 2) {
+      step(t, 0, masked_tag);
+      step(t + 1, 1, masked_tag);
+    }
+    if (t < tb) step(t, 0, masked_tag);
   };
 
   if (T > 0) {
     issue_tile(0, 0);
-    finish_tile(0);  // also waits for the Q loads issued above
+    if (pre1) {
+      issue_tile(1, 1);
+      static_assert(2 * IPW < 16, "vmcnt field");
+      __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * IPW));  // Q and tile 0 landed; tile 1 in flight
+    } else {
+      finish_tile(0);  // also waits for the Q loads issued above
+    }
   }
   __syncthreads();
   const int head_end = (t_full1 > t_full0) ? t_full0 : T;
-  for (int t = 0; t < head_end; ++t) step(t, std::true_type{});
-  for (int t = head_end; t < t_full1; ++t) step(t, std::false_type{});
-  for (int t = max(head_end, t_full1); t < T; ++t) step(t, std::true_type{});
+  run(0, head_end, std::true_type{});
+  run(head_end, t_full1, std::false_type{});
+  run(max(head_end, t_full1), T, std::true_type{});
 
   // Epilogue: O = acc / l (0 for an empty row) staged through LDS (free after
   // the last barrier) so that global stores are whole rows; LSE in natural log.
   const float ltot = pair32_sum(lsum);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  uint16_t* sO = reinterpret_cast<uint16_t*>(sKV) + wave * 32 * OSTR;
+  uint16_t* sO = reinterpret_cast<uint16_t*>(wave < 2 ? sKV0 : sKV1) + (wave & 1) * 32 * OSTR;
 #pragma unroll
   for (int c = 0; c < EB; ++c)
 #pragma unroll
