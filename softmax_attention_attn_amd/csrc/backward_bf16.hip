@@ -186,12 +186,16 @@ void bwd_dq_kernel(BwdParams p, int num_q_tiles) {
   constexpr bool RBF = MODE == kRbf;
   constexpr int NB = BT / 32;
   constexpr int QS = T::QS, EB = T::EB, ECH = T::ECH, ROWB = T::ROWB, TILEB = T::TILEB;
-  static_assert(BR * (E + 8) * 2 <= 2 * 2 * TILEB, "epilogue staging must fit the tile buffers");
+  static_assert(2 * 32 * (E + 8) * 2 <= 2 * TILEB, "epilogue staging of two waves must fit one tile buffer");
 
-  __shared__ __attribute__((aligned(16))) uint8_t sKV[2 * 2 * TILEB];
+  // Two separate LDS objects for the two [K | V] buffers: with the buffer index
+  // a compile-time constant (tiles are taken in pairs) the compiler can tell
+  // the reads of one buffer from the LDS-direct loads in flight into the other.
+  __shared__ __attribute__((aligned(16))) uint8_t sKV0[2 * TILEB];
+  __shared__ __attribute__((aligned(16))) uint8_t sKV1[2 * TILEB];
   __shared__ __attribute__((aligned(16))) float sBias[2][BT];
-  auto k_tile = [&](int buf) { return sKV + buf * 2 * TILEB; };
-  auto v_tile = [&](int buf) { return sKV + buf * 2 * TILEB + TILEB; };
+  auto k_tile = [&](int buf) { return buf ? sKV1 : sKV0; };
+  auto v_tile = [&](int buf) { return (buf ? sKV1 : sKV0) + TILEB; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -285,7 +289,7 @@ void bwd_dq_kernel(BwdParams p, int num_q_tiles) {
   tile_offsets<E>(lane, rd, trd);
   u32x4 kreg[T::KCH];
 
-  auto tile_keys = [&](int t, int& j0, int& kc) {
+  auto tile_keys = [&](int t, int& j0, int& kc) __attribute__((always_inline)) {
     if (t < n_reg_tiles) {
       j0 = t * BT;
       kc = min(BT, p.n_reg - j0);
@@ -294,7 +298,7 @@ void bwd_dq_kernel(BwdParams p, int num_q_tiles) {
       kc = min(BT, p.S - j0);
     }
   };
-  auto issue_tile = [&](int t, int buf) {
+  auto issue_tile = [&](int t, int buf) __attribute__((always_inline)) {
     int j0, kc;
     tile_keys(t, j0, kc);
     const uint32_t tb = (uint32_t)j0 * ROWB;
@@ -312,7 +316,7 @@ void bwd_dq_kernel(BwdParams p, int num_q_tiles) {
       }
     }
   };
-  auto finish_tile = [&](int buf) {
+  auto finish_tile = [&](int buf) __attribute__((always_inline)) {
     if (RBF) {
 #pragma unroll
       for (int i = 0; i < T::KCH; ++i) {
@@ -326,7 +330,7 @@ void bwd_dq_kernel(BwdParams p, int num_q_tiles) {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   };
 
-  auto compute_tile = [&](int t, int buf) {
+  auto compute_tile = [&](int t, int buf) __attribute__((always_inline)) {
     int j0, kc;
     tile_keys(t, j0, kc);
     const bool is_reg = t < n_reg_tiles;
@@ -418,11 +422,15 @@ void bwd_dq_kernel(BwdParams p, int num_q_tiles) {
     finish_tile(0);
   }
   __syncthreads();
-  for (int t = 0; t < TT; ++t) {
-    if (t + 1 < TT) issue_tile(t + 1, (t + 1) & 1);
-    compute_tile(t, t & 1);
-    if (t + 1 < TT) finish_tile((t + 1) & 1);
+  auto step = [&](int t, int buf) __attribute__((always_inline)) {
+    if (t + 1 < TT) issue_tile(t + 1, buf ^ 1);
+    compute_tile(t, buf);
+    if (t + 1 < TT) finish_tile(buf ^ 1);
     __syncthreads();
+  };
+  for (int t = 0; t < TT; t += 2) {
+    step(t, 0);
+    if (t + 1 < TT) step(t + 1, 1);
   }
 
   // dQ = scale K^T dS^T (dot) or 2 gamma (acc - D acc2 - q_i D (1 - sum_j P_ij)) (rbf).
@@ -438,7 +446,7 @@ void bwd_dq_kernel(BwdParams p, int num_q_tiles) {
     if (g == 0 && qi < p.L) p.delta[obase + qi] = d;  // the dK/dV kernel uses the same D
   }
   const float mul = RBF ? 2.f * p.gamma : p.scale;
-  uint16_t* sO = reinterpret_cast<uint16_t*>(sKV) + wave * 32 * (E + 8);
+  uint16_t* sO = reinterpret_cast<uint16_t*>(wave < 2 ? sKV0 : sKV1) + (wave & 1) * 32 * (E + 8);
   store_rows<E, EB>(acc, mul, RBF ? p.q + (obase + qa) * E : nullptr, ext, sO, lane, qa, p.L,
                     p.dq + (obase + qa) * E);
 }
@@ -457,18 +465,22 @@ void bwd_dkdv_kernel(BwdParams p, int num_k_tiles) {
   constexpr bool RBF = MODE == kRbf;
   constexpr int QS = T::QS, EB = T::EB, ECH = T::ECH, ROWB = T::ROWB, TILEB = T::TILEB;
   constexpr int VB = VL ? BR * ROWB : 0;  // bytes of the staged value rows
-  constexpr int RING = 2 * 2 * TILEB;
-  constexpr int EPB = BR * (E + 8) * 2;   // epilogue staging
-  constexpr int SQG = (RING + VB) > EPB ? (RING + VB) : EPB;
 
   // [buf][Q tile | dO tile] then (VL) the value rows; per buf the tile rows'
   // reference and D values.  The epilogue reuses the same bytes.
-  __shared__ __attribute__((aligned(16))) uint8_t sQG[SQG];
+  // The two [Q | dO] buffers and the value rows are separate LDS objects (see
+  // the dQ kernel); the epilogue stages each wave's rows in one of them.
+  constexpr int EPW = 32 * (E + 8) * 2;   // epilogue staging per wave
+  constexpr int SQB = (2 * TILEB) > EPW ? (2 * TILEB) : EPW;
+  constexpr int SVB = VB > 2 * EPW ? VB : 2 * EPW;
+  __shared__ __attribute__((aligned(16))) uint8_t sQG0[SQB];
+  __shared__ __attribute__((aligned(16))) uint8_t sQG1[SQB];
+  __shared__ __attribute__((aligned(16))) uint8_t sVR[SVB];
   __shared__ __attribute__((aligned(16))) float sMR[2][QT];
   __shared__ __attribute__((aligned(16))) float sDL[2][QT];
-  auto q_tile = [&](int buf) { return sQG + buf * 2 * TILEB; };
-  auto g_tile = [&](int buf) { return sQG + buf * 2 * TILEB + TILEB; };
-  uint8_t* sV = sQG + RING;
+  auto q_tile = [&](int buf) { return buf ? sQG1 : sQG0; };
+  auto g_tile = [&](int buf) { return (buf ? sQG1 : sQG0) + TILEB; };
+  uint8_t* sV = sVR;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -559,11 +571,11 @@ void bwd_dkdv_kernel(BwdParams p, int num_k_tiles) {
   tile_offsets<E>(lane, rd, trd);
   float mrv = 0.f, dlv = 0.f;  // staged per-row values (threads < QT)
 
-  auto step_rows = [&](int st_i, int& h, int& i0) {
+  auto step_rows = [&](int st_i, int& h, int& i0) __attribute__((always_inline)) {
     h = kh * G + st_i / ntq;
     i0 = (t_lo + st_i % ntq) * QT;
   };
-  auto issue_step = [&](int st_i, int buf) {
+  auto issue_step = [&](int st_i, int buf) __attribute__((always_inline)) {
     int h, i0;
     step_rows(st_i, h, i0);
     const size_t qoff = ((size_t)n * p.Hq + h) * p.L;
@@ -582,7 +594,7 @@ void bwd_dkdv_kernel(BwdParams p, int num_k_tiles) {
       dlv = i < p.L ? p.delta[qoff + i] : 0.f;
     }
   };
-  auto finish_step = [&](int buf) {
+  auto finish_step = [&](int buf) __attribute__((always_inline)) {
     if (tid < QT) {
       sMR[buf][tid] = mrv;
       sDL[buf][tid] = dlv;
@@ -590,7 +602,7 @@ void bwd_dkdv_kernel(BwdParams p, int num_k_tiles) {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   };
 
-  auto compute_step = [&](int st_i, int buf) {
+  auto compute_step = [&](int st_i, int buf) __attribute__((always_inline)) {
     int h, i0;
     step_rows(st_i, h, i0);
     (void)h;
@@ -656,16 +668,20 @@ void bwd_dkdv_kernel(BwdParams p, int num_k_tiles) {
     finish_step(0);
   }
   __syncthreads();
-  for (int st_i = 0; st_i < steps; ++st_i) {
-    if (st_i + 1 < steps) issue_step(st_i + 1, (st_i + 1) & 1);
-    compute_step(st_i, st_i & 1);
-    if (st_i + 1 < steps) finish_step((st_i + 1) & 1);
+  auto step = [&](int st_i, int buf) __attribute__((always_inline)) {
+    if (st_i + 1 < steps) issue_step(st_i + 1, buf ^ 1);
+    compute_step(st_i, buf);
+    if (st_i + 1 < steps) finish_step(buf ^ 1);
     __syncthreads();
+  };
+  for (int st_i = 0; st_i < steps; st_i += 2) {
+    step(st_i, 0);
+    if (st_i + 1 < steps) step(st_i + 1, 1);
   }
 
   // dV = P^T dO; dK = scale Q^T dS (dot) or 2 gamma (Q^T dS - k_j sum_i dS_ij) (rbf).
   const float cs = RBF ? pair32_sum(csum) : 0.f;
-  uint16_t* sO = reinterpret_cast<uint16_t*>(sQG) + wave * 32 * (E + 8);
+  uint16_t* sO = reinterpret_cast<uint16_t*>(wave < 2 ? sVR + wave * EPW : wave == 2 ? sQG0 : sQG1);
   store_rows<E, EB>(accv, 1.f, nullptr, 0.f, sO, lane, ja, p.S, p.dv + (kvbase + ja) * E);
   __syncthreads();
   store_rows<E, EB>(acck, RBF ? 2.f * p.gamma : p.scale, RBF ? p.k + (kvbase + ja) * E : nullptr,
