@@ -32,6 +32,8 @@
 //  3. bwd_sink_kernel (with a sink): the partials summed in a fixed order.
 // P and dS are rounded to bf16 as MFMA operands (fp32 accumulation), like P in
 // the forward; outputs are bf16.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "tile_common.h"
@@ -330,12 +332,15 @@ void bwd_dq_kernel(BwdParams p, int num_q_tiles) {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   };
 
-  auto compute_tile = [&](int t, int buf) __attribute__((always_inline)) {
+  // MASKED: a tile not every row of the workgroup sees whole (visibility
+  // tested per element); otherwise no visibility code.
+  auto compute_tile = [&](int t, int buf, auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     int j0, kc;
     tile_keys(t, j0, kc);
     const bool is_reg = t < n_reg_tiles;
     if (qb < qa) return;
-    if (!is_reg) {
+    if (MASKED && !is_reg) {
       const int ra = j0 - p.n_reg, rb = ra + BT - 1;
       const bool any = !((ra >= p.S_real) || (p.causal && ra > qb + p.off) ||
                          (p.window > 0 && qa + p.off - rb >= p.window));
@@ -366,18 +371,20 @@ void bwd_dq_kernel(BwdParams p, int num_q_tiles) {
       }
     }
     // Visible keys of this lane's row: one interval [lo, hi] of tile offsets.
-    int lo, hi;
-    if (is_reg) {
-      lo = 0;
-      hi = kc - 1;
-    } else {
-      const int base = j0 - p.n_reg;
-      const int ip = qi + p.off;
-      hi = min(p.S_real - 1, p.causal ? ip : p.S_real - 1) - base;
-      lo = (p.window > 0 ? ip - p.window + 1 : 0) - base;
+    int lo = 0, hi = BT - 1;
+    if (MASKED) {
+      if (is_reg) {
+        lo = 0;
+        hi = kc - 1;
+      } else {
+        const int base = j0 - p.n_reg;
+        const int ip = qi + p.off;
+        hi = min(p.S_real - 1, p.causal ? ip : p.S_real - 1) - base;
+        lo = (p.window > 0 ? ip - p.window + 1 : 0) - base;
+      }
+      lo -= 4 * g;
+      hi -= 4 * g;
     }
-    lo -= 4 * g;
-    hi -= 4 * g;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -385,7 +392,7 @@ void bwd_dq_kernel(BwdParams p, int num_q_tiles) {
         const int ko = 32 * b + 8 * (r >> 2) + (r & 3);
         float x = st[b][r] * p.c_logit;
         if (RBF) x += sBias[buf][ko + 4 * g];
-        const float pw = ((ko >= lo) & (ko <= hi)) ? fast_exp2(x - mr) : 0.f;
+        const float pw = (!MASKED || ((ko >= lo) & (ko <= hi))) ? fast_exp2(x - mr) : 0.f;
         if (RBF) {
           const float pd = pw * dp[b][r];
           rsa += pd;
@@ -422,16 +429,44 @@ void bwd_dq_kernel(BwdParams p, int num_q_tiles) {
     finish_tile(0);
   }
   __syncthreads();
-  auto step = [&](int t, int buf) __attribute__((always_inline)) {
+  auto step = [&](int t, int buf, auto masked_tag) __attribute__((always_inline)) {
     if (t + 1 < TT) issue_tile(t + 1, buf ^ 1);
-    compute_tile(t, buf);
+    compute_tile(t, buf, masked_tag);
     if (t + 1 < TT) finish_tile(buf ^ 1);
     __syncthreads();
   };
-  for (int t = 0; t < TT; t += 2) {
-    step(t, 0);
-    if (t + 1 < TT) step(t + 1, 1);
+  // Tiles t in [ta, tb), of one class, in pairs (compile-time buffer index).
+  auto run = [&](int ta, int tb, auto masked_tag) __attribute__((always_inline)) {
+    int t = ta;
+    if (t < tb && (t & 1)) step(t++, 1, masked_tag);
+    for (; t + 1 < tb; t += 2) {
+      step(t, 0, masked_tag);
+      step(t + 1, 1, masked_tag);
+    }
+    if (t < tb) step(t, 0, masked_tag);
+  };
+  // Real tiles [k_full0, k_full1] are seen whole by every row of the
+  // workgroup; register tiles and the real tiles before and after them are
+  // of the masked class.
+  int k_full0 = 0, k_full1 = -1;
+  {
+    const int lim = min(p.S_real - 1, p.causal ? i0 + p.off : p.S_real - 1);
+    k_full1 = (lim - r_lo - (BT - 1)) >= 0 ? (lim - r_lo - (BT - 1)) / BT : -1;
+    if (p.window > 0) {
+      const int need = i_last + p.off - p.window + 1 - r_lo;  // first tile start allowed
+      k_full0 = need > 0 ? (need + BT - 1) / BT : 0;
+    }
+    k_full1 = min(k_full1, n_real_tiles - 1);
+    if (k_full0 > k_full1) {
+      k_full0 = 0;
+      k_full1 = -1;
+    }
   }
+  const int t_full0 = n_reg_tiles + k_full0, t_full1 = n_reg_tiles + k_full1 + 1;
+  const int head_end = (t_full1 > t_full0) ? t_full0 : TT;
+  run(0, head_end, std::true_type{});
+  run(head_end, t_full1, std::false_type{});
+  run(max(head_end, t_full1), TT, std::true_type{});
 
   // dQ = scale K^T dS^T (dot) or 2 gamma (acc - D acc2 - q_i D (1 - sum_j P_ij)) (rbf).
   float ext = 0.f;
@@ -602,7 +637,11 @@ void bwd_dkdv_kernel(BwdParams p, int num_k_tiles) {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   };
 
-  auto compute_step = [&](int st_i, int buf) __attribute__((always_inline)) {
+  // MASKED: a query tile not every key of the workgroup sees whole (tested per
+  // element); otherwise no visibility code (rows past L have weight 0 anyway:
+  // their reference is +inf).
+  auto compute_step = [&](int st_i, int buf, auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     int h, i0;
     step_rows(st_i, h, i0);
     (void)h;
@@ -638,7 +677,7 @@ void bwd_dkdv_kernel(BwdParams p, int num_k_tiles) {
           const int r = 4 * rq + e;
           const int ro = 8 * rq + e;
           const float x = __builtin_fmaf(s_acc[r], p.c_logit, kbias);
-          const float w = ((ro >= lo) & (ro <= hi)) ? fast_exp2(x - m4[e]) : 0.f;
+          const float w = (!MASKED || ((ro >= lo) & (ro <= hi))) ? fast_exp2(x - m4[e]) : 0.f;
           pw[r] = w;
           ds[r] = w * (d_acc[r] - d4[e]);
           if (RBF) csum += ds[r];
@@ -668,15 +707,50 @@ void bwd_dkdv_kernel(BwdParams p, int num_k_tiles) {
     finish_step(0);
   }
   __syncthreads();
-  auto step = [&](int st_i, int buf) __attribute__((always_inline)) {
+  auto step = [&](int st_i, int buf, auto masked_tag) __attribute__((always_inline)) {
     if (st_i + 1 < steps) issue_step(st_i + 1, buf ^ 1);
-    compute_step(st_i, buf);
+    compute_step(st_i, buf, masked_tag);
     if (st_i + 1 < steps) finish_step(buf ^ 1);
     __syncthreads();
   };
-  for (int st_i = 0; st_i < steps; st_i += 2) {
-    step(st_i, 0);
-    if (st_i + 1 < steps) step(st_i + 1, 1);
+  // Steps [ta, tb), of one class, in pairs (compile-time buffer index).
+  auto run = [&](int ta, int tb, auto masked_tag) __attribute__((always_inline)) {
+    int t = ta;
+    if (t < tb && (t & 1)) step(t++, 1, masked_tag);
+    for (; t + 1 < tb; t += 2) {
+      step(t, 0, masked_tag);
+      step(t + 1, 1, masked_tag);
+    }
+    if (t < tb) step(t, 0, masked_tag);
+  };
+  // Query tiles j (of each head's ntq) in [jf0, jf1] are seen whole by every
+  // key of the workgroup: causal needs i0 + off >= the last real key, the
+  // window needs the last row i0 + QT - 1 within window - 1 of the first real
+  // key.  Workgroups holding keys past S keep every tile masked.
+  int jf0 = 0, jf1 = ntq - 1;
+  {
+    const int jb = j0 + BR - 1;
+    if (jb >= p.S) {
+      jf0 = 0;
+      jf1 = -1;
+    } else if (jb >= p.n_reg) {
+      const int ra = max(j0, p.n_reg) - p.n_reg, rb = jb - p.n_reg;
+      auto fdiv = [](int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); };
+      if (p.causal) jf0 = max(jf0, -fdiv(-(rb - p.off), QT) - t_lo);  // ceil((rb - off) / QT)
+      if (p.window > 0) jf1 = min(jf1, fdiv(ra - p.off + p.window - QT, QT) - t_lo);
+    }
+    if (jf0 > jf1) {
+      jf0 = 0;
+      jf1 = -1;
+    }
+  }
+  const int nm0 = jf1 >= jf0 ? jf0 : ntq;   // leading masked tiles per head
+  const int nfl = jf1 >= jf0 ? jf1 - jf0 + 1 : 0;
+  for (int hh = 0; hh < G; ++hh) {
+    const int base = hh * ntq;
+    run(base, base + nm0, std::true_type{});
+    run(base + nm0, base + nm0 + nfl, std::false_type{});
+    run(base + nm0 + nfl, base + ntq, std::true_type{});
   }
 
   // dV = P^T dO; dK = scale Q^T dS (dot) or 2 gamma (Q^T dS - k_j sum_i dS_ij) (rbf).

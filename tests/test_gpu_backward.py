@@ -42,6 +42,11 @@ CASES = [
     W("dot_window_registers_sink_e128", L=400, S_real=400, E=128, window=37, n_reg=3, sink=True),
     W("dot_negative_scale", N=2, L=150, S_real=150, causal=False, scale=-0.1),
     W("rbf_noncausal_many_registers_e128", L=130, S_real=90, E=128, mode="rbf", n_reg=70, causal=False),
+    # windows wider than the tiles: query and key tiles seen whole by a whole
+    # workgroup (no visibility code) sit between masked ones on both sides
+    W("dot_wide_window_e64", L=700, S_real=700, window=300),
+    W("rbf_wide_window_registers_sink_e128", L=650, S_real=650, E=128, mode="rbf", window=260, n_reg=4,
+      sink=True, gamma=0.05),
 ]
 
 

@@ -38,6 +38,10 @@ PREFILL_CASES = [
     W("dot_window_gqa_sink_e128", Hq=6, Hkv=3, L=520, S_real=520, E=128, window=128, sink=True),
     W("dot_sink_noncausal_e128", N=2, L=130, S_real=190, E=128, causal=False, sink=True),
     W("dot_registers_window", L=300, S_real=300, n_reg=5, window=50),
+    # windows wider than a workgroup's rows plus a tile: whole-tile steps run
+    # between the masked steps on both sides
+    W("dot_wide_window_registers", L=700, S_real=700, window=300, n_reg=3),
+    W("rbf_wide_window_sink_e128", L=650, S_real=650, E=128, mode="rbf", window=260, sink=True, gamma=0.05),
     W("dot_single_query", N=3, Hq=4, Hkv=1, L=1, S_real=999, E=128),
     W("rbf_causal_registers", L=300, S_real=300, mode="rbf", n_reg=4, k_dist="dir_lognormal"),
     W("rbf_noncausal_many_registers_e128", L=130, S_real=90, E=128, mode="rbf", n_reg=70, causal=False),
