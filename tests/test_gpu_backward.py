@@ -122,3 +122,14 @@ def test_backward_full_c2_sampled():
     krows = _sample(w.N * w.Hkv * w.S, 192, 2)
     got, ref, inp = _run(w, qrows=qrows, krows=krows)
     _check(w, got, ref, inp, qrows=qrows, krows=krows)
+
+
+def test_backward_full_c3_sampled():
+    # RBF, 4 register tokens, magnitude-skewed keys, E = 64, at full size: the
+    # dQ rows and dK/dV keys sampled across every head.
+    w = configs.C3
+    say(f"[bwd full] {w.name}")
+    qrows = _sample(w.N * w.Hq * w.L, 192, 3)
+    krows = _sample(w.N * w.Hkv * w.S, 192, 4)
+    got, ref, inp = _run(w, qrows=qrows, krows=krows)
+    _check(w, got, ref, inp, qrows=qrows, krows=krows)
