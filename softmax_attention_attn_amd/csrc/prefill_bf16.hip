@@ -36,11 +36,14 @@
 // RBF mode K still goes through registers, where |k|^2 is formed on its way to
 // LDS.  Tiles are stored row-major with the 16-byte chunks of row r permuted by
 // an XOR with swz(r), which keeps both the K reads (16 rows, one chunk) and the
-// transposing V reads (4 rows, two chunks) free of bank conflicts.  Several
-// workgroups share a CU, so one wave's softmax overlaps another's MFMAs.  The running max moves lazily: the accumulator is rescaled only when
-// a row max grows by more than 2^8 over the reference (O = acc / l does not
-// depend on the reference; it only bounds p by 256).  With a positive scale the
-// dot-mode max is taken on the raw scores and each weight costs one fma + exp2.
+// transposing V reads (4 rows, two chunks) free of bank conflicts.  The two
+// buffers are separate LDS objects and tiles are taken in pairs, so every LDS
+// address is a base register plus an immediate offset.  Several workgroups
+// share a CU, so one wave's softmax overlaps another's MFMAs.  The running max
+// moves lazily: the accumulator is rescaled only when a row max grows by more
+// than 2^8 over the reference (O = acc / l does not depend on the reference;
+// it only bounds p by 256).  With a positive scale the dot-mode max is taken on
+// the raw scores and each weight costs one fma + exp2.
 // The epilogue transposes O through LDS so that stores are whole rows.
 #include <type_traits>
 
