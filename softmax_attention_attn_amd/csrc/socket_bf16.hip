@@ -440,23 +440,6 @@ __device__ __forceinline__ int wave_prefix3(int x, int* total) {
   return pre;
 }
 
-// Appends the lane's flagged keys (bit e of m: key jb + e) to list at the
-// LDS counter *cnt, at most cap entries in all.  Every lane of the wave calls it.
-__device__ __forceinline__ void wave_append4(int* list, int* cnt, int cap, int m, int jb) {
-  int tot;
-  const int pre = wave_prefix3(__builtin_popcount(m), &tot);
-  if (tot == 0) return;  // wave-uniform
-  int base = 0;
-  if ((threadIdx.x & 63) == 0) base = atomicAdd(cnt, tot);
-  int p = __shfl(base, 0, 64) + pre;
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    if ((m >> e) & 1) {
-      if (p < cap) list[p] = jb + e;
-      ++p;
-    }
-}
-
 constexpr int CAP = 512;          // per-wave capacity of the one-read path's two key lists
 constexpr int SAMPLE_MAX = 8192;  // sample size of the one-read path
 constexpr int SEL_SMEM = 4096 + 3 * SEL_WAVES * CAP;
