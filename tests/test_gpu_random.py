@@ -91,3 +91,42 @@ def test_random_backward(w):
         bound = 1e-2 * np.sum(ps * np.abs(ref["delta"]), axis=(0, 2)) + 1e-6
         d = dsink.cpu().numpy().astype(np.float64)
         assert np.all(np.abs(d - ref["dsink"]) <= bound)
+
+
+# The general bias on random draws: float32 addends with -inf entries or
+# boolean masks (with a fully masked row), broadcast over batch and/or head,
+# with or without per-sequence key lengths.
+def _bias_draw(i):
+    w, _ = _draw(200 + i)
+    w = w.with_(decode=False, L=max(w.L, 2), name=w.name.replace("_dec", "") + "_bias")
+    r = np.random.default_rng(3000 + i)
+    kind = [None, "f32", "bool"][int(r.integers(0, 3))]
+    bn, bh = bool(r.random() < 0.5), bool(r.random() < 0.5)
+    use_kl = bool(r.random() < 0.5) or kind is None
+    p = float(r.choice([0.0, 0.1, 0.5]))
+    return w, kind, bn, bh, use_kl, p
+
+
+BIAS_DRAWS = [_bias_draw(i) for i in range(32)]
+
+
+@pytest.mark.parametrize("w,kind,bn,bh,use_kl,p", BIAS_DRAWS, ids=[d[0].name for d in BIAS_DRAWS])
+def test_random_biased_forward(w, kind, bn, bh, use_kl, p):
+    say(f"[random bias] {w.name} kind={kind} per_batch={bn} per_head={bh} key_len={use_kl} p={p}")
+    inp = gen.generate(w)
+    q, k, v, sink = to_device(inp)
+    b = None
+    if kind is not None:
+        shape = (w.N if bn else 1, w.Hq if bh else 1, w.L, w.S)
+        if kind == "f32":
+            b = gen.bias_f32(w.seed, shape, scale=1.0, p_neg_inf=p)
+        else:
+            b = gen.mask_bool(w.seed, shape, max(p, 0.3))
+            b[..., 1, :] = False
+    kl = gen.key_lengths(w.seed, w.N, w.S_real) if use_kl else None
+    bt = None if b is None else torch.from_numpy(b).to("cuda:0")
+    klt = None if kl is None else torch.from_numpy(kl).to("cuda:0")
+    o, lse = attn.fwd(q, k, v, scale=w.scale, mode=w.mode, gamma=w.gamma, causal=w.causal, window=w.window,
+                      n_reg=w.n_reg, sink=sink, bias=bt, key_len=klt)
+    torch.cuda.synchronize()
+    check(w, inp, o, lse, bias=b, key_len=kl)
