@@ -130,3 +130,137 @@ def test_random_biased_forward(w, kind, bn, bh, use_kl, p):
                       n_reg=w.n_reg, sink=sink, bias=bt, key_len=klt)
     torch.cuda.synchronize()
     check(w, inp, o, lse, bias=b, key_len=kl)
+
+
+# SOCKET sparse decode on random draws: table counts and code widths (packed
+# and byte codes, fast and generic scorers), temperatures, budgets from one key
+# to every key, GQA groups, RBF keys.  Checked as in test_gpu_socket: bucket
+# codes bit-exact, the chosen set valid around the k-th score (fp64 scores),
+# and equal to the oracle's, with the output at the forward bars, wherever the
+# top-k set is unique.
+def _socket_draw(i):
+    r = np.random.default_rng(5000 + i)
+    E = int(r.choice([64, 128]))
+    Hkv = int(r.integers(1, 3))
+    G = int(r.choice([1, 2, 4, 8, 16]))
+    N = int(r.integers(1, 3))
+    S = int(r.choice([int(r.integers(1, 64)), int(r.integers(64, 2000)), int(r.integers(2000, 12000))]))
+    mode = "rbf" if r.random() < 0.3 else "dot"
+    k_dist = "dir_lognormal" if mode == "rbf" and r.random() < 0.5 else "normal"
+    sink = bool(r.random() < 0.5)
+    tables = int(r.choice([1, 3, 8, 16, 32, 64]))
+    bits = int(r.integers(1, 9))
+    tau = float(r.choice([0.5, 1.0, 2.0, 4.0, 8.0]))
+    top_k = int(r.choice([1, max(1, S // 50), max(1, S // 4), S, int(r.integers(1, S + 1))]))
+    splits = int(r.choice([0, 0, 1, 3]))
+    name = f"s{i:02d}_{mode}_e{E}_N{N}_{G * Hkv}to{Hkv}_S{S}_t{tables}b{bits}_tau{tau}_k{top_k}{'_sink' if sink else ''}"
+    w = Workload(name, "bf16", N, G * Hkv, Hkv, 1, S, E, mode, float(1.0 / np.sqrt(E)), 0.05, True, 0, 0, sink,
+                 True, 900 + i, k_dist)
+    return w, tables, bits, tau, top_k, splits
+
+
+SOCKET_DRAWS = [_socket_draw(i) for i in range(32)]
+
+
+@pytest.mark.parametrize("w,tables,bits,tau,top_k,splits", SOCKET_DRAWS, ids=[d[0].name for d in SOCKET_DRAWS])
+def test_random_socket(w, tables, bits, tau, top_k, splits):
+    say(f"[random socket] {w.name} splits={splits}")
+    inp = gen.generate(w)
+    q, k, v, sink = to_device(inp)
+    proj_np = gen.socket_projections(w.seed, tables, bits, w.E)
+    proj = torch.from_numpy(proj_np).to("cuda:0")
+    bk, vn = attn.socket_hash(k, v, proj, tables=tables, bits=bits)
+    b_ref, vn_ref = oracle.socket_hash(inp.k, inp.v, proj_np, tables, bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(attn.unpack_codes(bk, tables, bits).cpu().numpy(), b_ref), "bucket codes differ"
+    assert np.max(np.abs(vn.cpu().numpy() - vn_ref) / np.maximum(vn_ref, 1e-30)) < 1e-5
+    kw = dict(tables=tables, bits=bits, tau=tau, top_k=top_k, scale=w.scale, mode=w.mode, gamma=w.gamma, sink=sink,
+              num_splits=splits, want_selected=True)
+    if (w.Hq // w.Hkv) * tables * (1 << bits) * 4 > 64 * 1024:
+        # the documented limit of the scorer's LDS table: a loud error, nothing computed
+        with pytest.raises(attn.AttnError, match="UNSUPPORTED"):
+            attn.socket_decode(q, k, v, proj, bk, vn, **kw)
+        say("  rejected as documented (probability table over 64 KB)")
+        return
+    o_ref, l_ref, sel_ref, sc_ref = oracle.socket_decode(inp.q, inp.k, inp.v, proj_np, b_ref, vn_ref, tables=tables,
+                                                         bits=bits, tau=tau, top_k=top_k, mode=w.mode,
+                                                         scale=w.scale, gamma=w.gamma, sink=inp.sink)
+    o, lse, sel = attn.socket_decode(q, k, v, proj, bk, vn, **kw)
+    torch.cuda.synchronize()
+    og = o.float().cpu().numpy().astype(np.float64)
+    lg = lse.cpu().numpy().astype(np.float64)
+    sg = sel.cpu().numpy()
+    unique = 0
+    for n in range(w.N):
+        for h in range(w.Hq):
+            sc = sc_ref[n, h]
+            sk = np.sort(sc)[::-1][top_k - 1]
+            hi, lo = sk * (1 + 1e-4), sk * (1 - 1e-4)
+            chosen = np.zeros(w.S, bool)
+            chosen[sg[n, h]] = True
+            assert np.all(np.diff(sg[n, h]) > 0), "selection not ascending / repeated"
+            assert chosen.sum() == top_k
+            assert np.all(chosen[sc > hi]), "a clearly better key was left out"
+            assert np.all(sc[chosen] >= lo), "a clearly worse key was chosen"
+            if np.sum(sc >= lo) == top_k:
+                unique += 1
+                assert np.array_equal(sg[n, h], sel_ref[n, h])
+                assert np.max(np.abs(og[n, h] - o_ref[n, h])) <= 2e-2
+                assert abs(lg[n, h, 0] - l_ref[n, h, 0]) <= 1e-3
+    say(f"  {unique}/{w.N * w.Hq} heads with a unique top-k, compared exactly")
+
+
+# Rolling (StreamingLLM) cache on random draws: sink and window sizes, chunk
+# sequences mixing single tokens with chunks that cross the sink boundary or
+# exceed the window; after every append the kept rows must be bit copies of
+# the history and the newest token's decode must match the oracle.
+def _stream_draw(i):
+    r = np.random.default_rng(7000 + i)
+    E = int(r.choice([64, 128]))
+    Hkv = int(r.integers(1, 3))
+    G = int(r.choice([1, 2, 4, 8]))
+    N = int(r.integers(1, 3))
+    n_sink = int(r.choice([0, 1, 4, int(r.integers(0, 20))]))
+    window = int(r.choice([1, int(r.integers(1, 64)), int(r.integers(64, 600))]))
+    chunks = []
+    while len(chunks) < 10:
+        chunks.append(int(r.choice([1, 1, int(r.integers(1, 40)), int(r.integers(1, window + n_sink + 50))])))
+    P = sum(chunks)
+    mode = "rbf" if r.random() < 0.3 else "dot"
+    sink = bool(r.random() < 0.5)
+    splits = int(r.choice([0, 0, 1, 5]))
+    name = f"st{i:02d}_{mode}_e{E}_N{N}_{G * Hkv}to{Hkv}_sink{n_sink}_win{window}_P{P}{'_lsink' if sink else ''}"
+    w = Workload(name, "bf16", N, G * Hkv, Hkv, P, P, E, mode, float(1.0 / np.sqrt(E)), 0.05, True, 0, 0, sink,
+                 False, 1100 + i, "normal")
+    return w, n_sink, window, chunks, splits
+
+
+STREAM_DRAWS = [_stream_draw(i) for i in range(16)]
+
+
+@pytest.mark.parametrize("w,n_sink,window,chunks,splits", STREAM_DRAWS, ids=[d[0].name for d in STREAM_DRAWS])
+def test_random_stream(w, n_sink, window, chunks, splits):
+    say(f"[random stream] {w.name} chunks={chunks} splits={splits}")
+    inp = gen.generate(w)
+    q, k, v, sink = to_device(inp)
+    C = n_sink + window
+    kc = torch.zeros((w.N, w.Hkv, C, w.E), dtype=torch.bfloat16, device="cuda:0")
+    vc = torch.full((w.N, w.Hkv, C, w.E), 1000.0, dtype=torch.bfloat16, device="cuda:0")
+    pos = -1
+    for T in chunks:
+        first = pos + 1
+        pos += T
+        attn.stream_append(k[:, :, first:pos + 1].contiguous(), v[:, :, first:pos + 1].contiguous(), kc, vc,
+                           n_sink=n_sink, window=window, pos=first)
+        kept = oracle.stream_kept_positions(n_sink, window, pos)
+        slots = [p if p < n_sink else n_sink + (p - n_sink) % window for p in (int(x) for x in kept)]
+        torch.cuda.synchronize()
+        assert torch.equal(kc[:, :, slots].view(torch.int16), k[:, :, torch.as_tensor(kept)].view(torch.int16))
+        assert torch.equal(vc[:, :, slots].view(torch.int16), v[:, :, torch.as_tensor(kept)].view(torch.int16))
+        o_ref, l_ref = oracle.stream_decode(inp.q[:, :, pos:pos + 1], inp.k, inp.v, n_sink=n_sink, window=window,
+                                            pos=pos, mode=w.mode, scale=w.scale, gamma=w.gamma, sink=inp.sink)
+        o, lse = attn.stream_decode(q[:, :, pos:pos + 1].contiguous(), kc, vc, n_sink=n_sink, window=window, pos=pos,
+                                    scale=w.scale, mode=w.mode, gamma=w.gamma, sink=sink, num_splits=splits)
+        torch.cuda.synchronize()
+        assert np.max(np.abs(o.float().cpu().numpy().astype(np.float64) - o_ref)) <= 2e-2
+        assert np.max(np.abs(lse.cpu().numpy().astype(np.float64) - l_ref)) <= 1e-3
