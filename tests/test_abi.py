@@ -80,6 +80,11 @@ def dec(lib, dt=0, N=1, Hq=4, Hkv=2, L=1, S=64, E=64, q=A, k=A, v=A, mode=0, sca
     (dict(v=A + 2), -5),
     (dict(lse=A + 2), -5),
     (dict(sink=A + 1), -5),
+    # maximum sizes: a bf16 (batch, kv head) K/V slice at 2 GiB (32-bit tile
+    # offsets), and tensors past 2^40 elements
+    (dict(S=(1 << 31) // 256 - 64, E=128, n_reg=0), -4),
+    (dict(S=(1 << 31) // 128 - 64, E=64, n_reg=0), -4),
+    (dict(N=1 << 20, Hq=1 << 10, Hkv=1 << 10, L=1 << 10, S=8, E=128), -2),
 ])
 def test_fwd_rejects(lib, kw, code):
     assert fwd(lib, **kw) == code
@@ -165,6 +170,9 @@ def bwd(lib, dt=0, N=1, Hq=4, Hkv=2, L=8, S=8, E=64, q=A, k=A, v=A, o=A, lse=A, 
     (dict(ws=None), -6),
     (dict(wsb=64), -6),
     (dict(L=0), -4),
+    # maximum sizes: K/V or Q/dO (batch, head) slices at 2 GiB (32-bit tile offsets)
+    (dict(S=(1 << 31) // 256 - 64, E=128), -4),
+    (dict(L=(1 << 31) // 128 - 64, E=64, wsb=1 << 40), -4),
 ])
 def test_bwd_rejects(lib, kw, code):
     assert bwd(lib, **kw) == code
