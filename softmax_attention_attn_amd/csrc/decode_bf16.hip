@@ -15,7 +15,8 @@
 // step is two v_mfma_f32_16x16x32_bf16 products S^T = K * Q^T (16 keys x 16
 // query slots; only the group's G heads are real) followed by O^T += V^T * P^T.
 // K rows are loaded straight into the MFMA A operand (64 contiguous bytes per
-// row per load).  V is loaded as whole 256-byte rows -- lane (m, g) takes dims
+// row per load).  K and V are read once, so their loads carry the
+// non-temporal hint.  V is loaded as whole 256-byte rows -- lane (m, g) takes dims
 // 8m..8m+7 of 8 keys -- and transposed in registers, so the 8 PV products of a
 // step each produce the 16 dims {8m + j}.
 //
@@ -136,13 +137,13 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams p) {
       const bool ok = vk < v1;
       const uint16_t* row = kbase + (size_t)key_row(ok ? vk : v0, p, sidx, v0) * E;
 #pragma unroll
-      for (int s = 0; s < QS; ++s) kr[b][s] = load16_or_zero(row + 32 * s + 8 * g, ok);
+      for (int s = 0; s < QS; ++s) kr[b][s] = load16_nt_or_zero(row + 32 * s + 8 * g, ok);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int vk = vb + (i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4));
       const bool ok = vk < v1 && l16 < ECH;
-      vr[i] = load16_or_zero(vbase + (size_t)key_row(ok ? vk : v0, p, sidx, v0) * E + 8 * l16, ok);
+      vr[i] = load16_nt_or_zero(vbase + (size_t)key_row(ok ? vk : v0, p, sidx, v0) * E + 8 * l16, ok);
     }
   };
 
