@@ -13,7 +13,9 @@ streaming decode over a rolling cache (append the newest token, decode it; HBM
 GB/s over the kept rows read once) and the backward pass on the C2 and C3
 shapes (TFLOP/s at 10*E flops per visible pair) and a SOCKET sparse decode step
 on the long-context decode shape (HBM GB/s over the codes, norms and selected
-rows; speedup over the dense decode).
+rows; speedup over the dense decode).  Each timing is the mean over K
+back-to-back calls between two events; a second pass with one event pair per
+call gives the spread of single calls ("ms_spread": p10 / p50 / p90).
 
 The CPU baseline leg times the fp64 oracle on a bounded sample of rows of the
 headline workload, on this host's cores, and checks the GPU output on those
@@ -90,6 +92,36 @@ def to_device(inp, torch, dev):
     return t(inp.q), t(inp.k), t(inp.v), sink
 
 
+SPREAD = {}  # workload name -> per-call ms percentiles from the spread pass
+
+
+def timed(name, call, steps: int, torch, dev):
+    """Mean ms per call over `steps` back-to-back calls between two events on the
+    launching stream; then a second pass with one event pair per call (at most 200
+    calls) records the p10 / p50 / p90 of single calls in SPREAD[name]."""
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        call(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    n = min(steps, 200)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        call(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    pick = lambda f: per[min(n - 1, int(f * (n - 1) + 0.5))]
+    SPREAD[name] = {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9), "calls": n}
+    return ms
+
+
 def time_workload(w, steps: int, warmup: int, rotate: int, torch, attn, keep_first_output=False):
     """Average ms per call over `steps` back-to-back calls, inputs resident in HBM."""
     dev = torch.device("cuda:0")
@@ -125,16 +157,7 @@ def time_workload(w, steps: int, warmup: int, rotate: int, torch, attn, keep_fir
     first = (outs[0][0].clone(), outs[0][1].clone()) if keep_first_output else None
     for i in range(warmup):
         call(i)
-    stream = torch.cuda.current_stream(dev)
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(steps):
-        call(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    ms = timed(w.name, call, steps, torch, dev)
     return ms, inp, first
 
 
@@ -166,16 +189,7 @@ def time_stream(sw, steps: int, warmup: int, rotate: int, torch, attn):
 
     for i in range(warmup + 1):
         call(i)
-    stream = torch.cuda.current_stream(dev)
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(steps):
-        call(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    return timed(sw.name, call, steps, torch, dev)
 
 
 def time_backward(w, steps: int, warmup: int, torch, attn):
@@ -192,18 +206,12 @@ def time_backward(w, steps: int, warmup: int, torch, attn):
     o, lse = attn.fwd(q, k, v, **kw)
     ws = torch.empty(max(16, int(attn.load().attn_bwd_workspace_bytes(w.N, w.Hq, w.L))), dtype=torch.uint8,
                      device=dev)
-    for _ in range(warmup + 1):
+    def call(_i):
         attn.bwd(q, k, v, o, lse, do, workspace=ws, **kw)
-    stream = torch.cuda.current_stream(dev)
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
-        attn.bwd(q, k, v, o, lse, do, workspace=ws, **kw)
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+
+    for i in range(warmup + 1):
+        call(i)
+    return timed(w.name + "__backward", call, steps, torch, dev)
 
 
 def time_socket(sw, steps: int, warmup: int, torch, attn):
@@ -223,18 +231,12 @@ def time_socket(sw, steps: int, warmup: int, torch, attn):
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     kw = dict(tables=sw.tables, bits=sw.bits, tau=sw.tau, top_k=sw.top_k, scale=w.scale, sink=sink, workspace=ws,
               out=o, lse=lse)
-    for _ in range(warmup + 1):
+    def call(_i):
         attn.socket_decode(q, k, v, proj, buckets, vnorm, **kw)
-    stream = torch.cuda.current_stream(dev)
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
-        attn.socket_decode(q, k, v, proj, buckets, vnorm, **kw)
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+
+    for i in range(warmup + 1):
+        call(i)
+    return timed(sw.name, call, steps, torch, dev)
 
 
 def stream_rate(sw, ms: float):
@@ -354,7 +356,7 @@ def main() -> int:
         ms = time_backward(bw, args.steps, args.warmup, torch, attn)
         tf = configs.backward_flops(bw) / (ms * 1e-3) / 1e12
         print(json.dumps({"metric": "backward TFLOP/s", "value": tf, "unit": "TFLOP/s", "n_gpus": 1,
-                          "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+                          "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "ms_spread": SPREAD.get(args.workload), "higher_is_better": True,
                           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                           "data": "synthetic (seeded generator, workloads/gen.py)",
                           "config": {"workload": args.workload},
@@ -367,7 +369,7 @@ def main() -> int:
         ms = time_socket(sk, args.steps, args.warmup, torch, attn)
         gbs = configs.socket_bytes(sk) / (ms * 1e-3) / 1e9
         print(json.dumps({"metric": "SOCKET sparse decode HBM GB/s", "value": gbs, "unit": "GB/s", "n_gpus": 1,
-                          "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+                          "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "ms_spread": SPREAD.get(args.workload), "higher_is_better": True,
                           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                           "data": "synthetic (seeded generator, workloads/gen.py)",
                           "config": {"workload": sk.name},
@@ -381,7 +383,7 @@ def main() -> int:
         ms = time_stream(sw, args.steps, args.warmup, 3, torch, attn)
         r = stream_rate(sw, ms)
         print(json.dumps({"metric": "streaming decode HBM GB/s", "value": r["value"], "unit": r["unit"],
-                          "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+                          "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "ms_spread": SPREAD.get(args.workload),
                           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                           "data": "synthetic (seeded generator, workloads/gen.py)",
                           "config": {"workload": sw.name},
@@ -400,7 +402,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": ms, "ms_spread": SPREAD.get(args.workload),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -431,6 +433,7 @@ def main() -> int:
             torch.cuda.empty_cache()
             xr = rate(x, xms)
             xr["ms"] = xms
+            xr["ms_spread"] = SPREAD.get(x.name)
             xr["kernel"] = kernel_of(x)
             xr["rotated_buffer_sets"] = rot
             extras[x.name] = xr
@@ -440,7 +443,8 @@ def main() -> int:
             tf = configs.backward_flops(bw) / (xms * 1e-3) / 1e12
             extras[bw.name + "__backward"] = {
                 "value": tf, "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_BF16_TFLOPS,
-                "frac": tf / PEAK_BF16_TFLOPS, "ms": xms, "kernel": "bwd_pre + bwd_dq + bwd_dkdv",
+                "frac": tf / PEAK_BF16_TFLOPS, "ms": xms, "ms_spread": SPREAD.get(bw.name + "__backward"),
+                "kernel": "bwd_pre + bwd_dq + bwd_dkdv",
                 "hbm_GBps": configs.backward_bytes(bw) / (xms * 1e-3) / 1e9,
                 "algorithmic_per_step": configs.backward_flops(bw)}
         for sk in configs.SOCKET_BY_NAME.values():
@@ -449,7 +453,7 @@ def main() -> int:
             gbs = configs.socket_bytes(sk) / (xms * 1e-3) / 1e9
             dense = extras.get(sk.base.name, {}).get("ms")
             extras[sk.name] = {"value": gbs, "unit": "GB/s", "bound": "hbm", "peak": PEAK_HBM_GBS,
-                               "frac": gbs / PEAK_HBM_GBS, "ms": xms,
+                               "frac": gbs / PEAK_HBM_GBS, "ms": xms, "ms_spread": SPREAD.get(sk.name),
                                "kernel": "socket_prob + socket_score + socket_select + decode (indexed)",
                                "speedup_vs_dense_decode": (dense / xms) if dense else None}
         for sw in configs.STREAM_BY_NAME.values():
@@ -457,6 +461,7 @@ def main() -> int:
             torch.cuda.empty_cache()
             xr = stream_rate(sw, xms)
             xr["ms"] = xms
+            xr["ms_spread"] = SPREAD.get(sw.name)
             xr["kernel"] = "stream_append + decode_bf16"
             xr["rotated_buffer_sets"] = 3
             extras[sw.name] = xr
