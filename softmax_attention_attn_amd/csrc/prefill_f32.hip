@@ -8,9 +8,11 @@
 // partial states of each row are merged through LDS with log-sum-exp weights,
 // the split-K combine of the decode path.  Same logit frame, visibility rule,
 // sink and LSE conventions as the bf16 kernel: x = c_logit*(q.k) +
-// c_bias*|k|^2 in log2 units, with |k|^2 computed once per staged tile from
-// LDS.  Within a wave keys are taken one at a time: the running max only moves
-// (and the accumulator is only rescaled) when a larger logit arrives.
+// c_bias*|k|^2 in log2 units, with |k|^2 summed over a key row's staged
+// pieces (consecutive lanes) on their way to LDS; tile t+1 is fetched into
+// registers while tile t is consumed.  Within a wave keys are taken one at a
+// time: the running max only moves (and the accumulator is only rescaled) when
+// a larger logit arrives.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -95,40 +97,70 @@ void prefill_f32_kernel(PrefillF32Params p) {
   const int T = n_reg_tiles + n_real_tiles;
   const size_t kvoff = ((size_t)n * p.Hkv + kh) * (size_t)p.S * E;
 
-  for (int t = 0; t < T; ++t) {
-    int j0, kc;
-    const bool is_reg = t < n_reg_tiles;
-    if (is_reg) {
+  // Tile t+1 is fetched into registers while tile t is consumed from LDS.
+  // Thread tid stages 16-byte pieces tid, tid + BQ*W, ... of a tile; the E/4
+  // pieces of one key row sit in consecutive lanes, where |k|^2 is summed on
+  // the way to LDS.
+  constexpr int NPT = BK * E / 4 / (BQ * W);
+  static_assert(NPT * BQ * W * 4 == BK * E, "tile must split evenly over the threads");
+  auto tile_keys = [&](int t, int& j0, int& kc) {
+    if (t < n_reg_tiles) {
       j0 = t * BK;
       kc = min(BK, p.n_reg - j0);
     } else {
       j0 = p.n_reg + r_lo + (t - n_reg_tiles) * BK;
       kc = min(BK, p.S - j0);
     }
-    __syncthreads();
-    for (int idx = tid; idx < BK * E / 4; idx += BQ * W) {
+  };
+  f32x4 kr[NPT], vr[NPT];
+  auto fetch_tile = [&](int t) {
+    int j0, kc;
+    tile_keys(t, j0, kc);
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int idx = tid + i * BQ * W;
       const int row = (idx * 4) / E, col = (idx * 4) % E;
-      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+      kr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      vr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (row < kc) {
-        kv = *reinterpret_cast<const f32x4*>(p.k + kvoff + (size_t)(j0 + row) * E + col);
-        vv = *reinterpret_cast<const f32x4*>(p.v + kvoff + (size_t)(j0 + row) * E + col);
+        kr[i] = *reinterpret_cast<const f32x4*>(p.k + kvoff + (size_t)(j0 + row) * E + col);
+        vr[i] = *reinterpret_cast<const f32x4*>(p.v + kvoff + (size_t)(j0 + row) * E + col);
       }
-      *reinterpret_cast<f32x4*>(&sK[row * E + col]) = kv;
-      *reinterpret_cast<f32x4*>(&sV[row * E + col]) = vv;
+    }
+  };
+  if (T > 0) fetch_tile(0);
+
+  for (int t = 0; t < T; ++t) {
+    int j0, kc;
+    tile_keys(t, j0, kc);
+    const bool is_reg = t < n_reg_tiles;
+    __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int idx = tid + i * BQ * W;
+      const int row = (idx * 4) / E, col = (idx * 4) % E;
+      *reinterpret_cast<f32x4*>(&sK[row * E + col]) = kr[i];
+      *reinterpret_cast<f32x4*>(&sV[row * E + col]) = vr[i];
+      if (RBF) {
+        float ss = kr[i][0] * kr[i][0];
+        ss = __builtin_fmaf(kr[i][1], kr[i][1], ss);
+        ss = __builtin_fmaf(kr[i][2], kr[i][2], ss);
+        ss = __builtin_fmaf(kr[i][3], kr[i][3], ss);
+        ss = group_sum<16>(ss);
+        if (E / 4 == 32) ss += __shfl_xor(ss, 16, 64);
+        if (col == 0) sBias[row] = p.c_bias * ss;
+      }
     }
     __syncthreads();
-    if (RBF && tid < BK) {
-      float ss = 0.f;
-      for (int e = 0; e < E; ++e) ss = __builtin_fmaf(sK[tid * E + e], sK[tid * E + e], ss);
-      sBias[tid] = p.c_bias * ss;
-    }
-    if (RBF) __syncthreads();
+    if (t + 1 < T) fetch_tile(t + 1);
 
 #pragma unroll 1
     for (int kt = wave; kt < BK; kt += W) {
-      float d = 0.f;
+      // q.k as four interleaved partial sums (a quarter of the dependent chain).
+      float d4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < E; ++e) d = __builtin_fmaf(q[e], sK[kt * E + e], d);
+      for (int e = 0; e < E; ++e) d4[e & 3] = __builtin_fmaf(q[e], sK[kt * E + e], d4[e & 3]);
+      const float d = (d4[0] + d4[1]) + (d4[2] + d4[3]);
       float x = d * p.c_logit;
       if (RBF) x += sBias[kt];
       bool vis;
