@@ -51,6 +51,11 @@ PREFILL_CASES = [
     W("f32_dot_window_gqa_sink_e128", dtype="f32", Hq=4, Hkv=2, L=100, S_real=100, E=128, window=30, sink=True),
     W("f32_rbf_registers_L_lt_S", dtype="f32", L=70, S_real=150, mode="rbf", n_reg=3, gamma=0.05),
     W("f32_dot_L_gt_S", dtype="f32", L=90, S_real=40, E=64),
+    # fp32 RBF at E = 128: a key row's norm is summed over 32 staging lanes
+    W("f32_rbf_e128_registers_window_sink", dtype="f32", Hq=2, Hkv=1, L=150, S_real=170, E=128, mode="rbf",
+      n_reg=5, window=60, sink=True, gamma=0.05, k_dist="dir_lognormal"),
+    W("f32_rbf_e128_noncausal_ragged", dtype="f32", N=2, L=70, S_real=333, E=128, mode="rbf", causal=False,
+      gamma=0.02),
 ]
 
 # Wider shapes (hundreds of workgroups, more heads than the small cases) with
