@@ -70,6 +70,8 @@ def _bind(path: str):
     lib.oracle_socket_scores.restype = ctypes.c_int
     lib.oracle_socket_scores.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                          vp, fp, ctypes.c_longlong, u8p, dp, dp]
+    lib.oracle_socket_select.restype = ctypes.c_int
+    lib.oracle_socket_select.argtypes = [ctypes.c_longlong, dp, ctypes.c_longlong, llp]
     lib.oracle_visible.restype = ctypes.c_int
     lib.oracle_visible.argtypes = [ctypes.c_int] * 7
     lib.oracle_num_threads.restype = ctypes.c_int
@@ -328,11 +330,16 @@ def socket_scores(q_row: np.ndarray, proj: np.ndarray, buckets: np.ndarray, vnor
     return out
 
 
-def socket_select(scores: np.ndarray, top_k: int) -> np.ndarray:
+def socket_select(scores: np.ndarray, top_k: int, lib=None) -> np.ndarray:
     """The top_k keys by score, ties to the lower index (method step 4: a deterministic
     top-k), returned in ascending key order."""
-    order = np.lexsort((np.arange(scores.shape[0]), -scores))
-    return np.sort(order[:top_k])
+    sc = np.ascontiguousarray(scores, dtype=np.float64).reshape(-1)
+    out = np.zeros(max(int(top_k), 0), dtype=np.int64)
+    rc = (lib or _load()).oracle_socket_select(sc.shape[0], sc.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                               int(top_k), out.ctypes.data_as(ctypes.POINTER(ctypes.c_longlong)))
+    if rc != 0:
+        raise ValueError(f"oracle_socket_select failed with code {rc}")
+    return out
 
 
 def socket_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, proj: np.ndarray, buckets: np.ndarray,
@@ -352,7 +359,7 @@ def socket_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, proj: np.ndarray,
         for h in range(Hq):
             kh = h // G
             s = socket_scores(q[n, h, 0], proj, buckets[n, kh], vnorm[n, kh], tables, bits, tau, lib=lib)
-            idx = socket_select(s, top_k)
+            idx = socket_select(s, top_k, lib=lib)
             sc[n, h] = s
             sel[n, h] = idx
             kk = np.ascontiguousarray(k[n:n + 1, kh:kh + 1, idx])

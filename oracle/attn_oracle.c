@@ -418,3 +418,42 @@ int oracle_socket_scores(int dtype, int E, int tables, int bits, double tau, con
   free(prob);
   return 0;
 }
+
+/* ------------------------------------------------------------------------ SOCKET top-k selection */
+
+typedef struct {
+  double score;
+  long long idx;
+} scored_key;
+
+/* Order for the deterministic top-k: higher score first, and among equal
+   scores the lower key index first. */
+static int by_score_then_index(const void* a, const void* b) {
+  const scored_key* x = (const scored_key*)a;
+  const scored_key* y = (const scored_key*)b;
+  if (x->score > y->score) return -1;
+  if (x->score < y->score) return 1;
+  return (x->idx < y->idx) ? -1 : 1;
+}
+
+static int by_index(const void* a, const void* b) {
+  const long long x = *(const long long*)a, y = *(const long long*)b;
+  return (x > y) - (x < y);
+}
+
+int oracle_socket_select(long long nkeys, const double* scores, long long top_k, long long* selected) {
+  if (nkeys < 0 || top_k < 0 || top_k > nkeys) return -2;
+  for (long long j = 0; j < nkeys; ++j)
+    if (isnan(scores[j])) return -3;
+  scored_key* all = (scored_key*)malloc(sizeof(scored_key) * (size_t)(nkeys > 0 ? nkeys : 1));
+  if (!all) return -4;
+  for (long long j = 0; j < nkeys; ++j) {
+    all[j].score = scores[j];
+    all[j].idx = j;
+  }
+  qsort(all, (size_t)nkeys, sizeof(scored_key), by_score_then_index);
+  for (long long r = 0; r < top_k; ++r) selected[r] = all[r].idx;
+  free(all);
+  qsort(selected, (size_t)top_k, sizeof(long long), by_index);
+  return 0;
+}

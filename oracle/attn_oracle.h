@@ -140,6 +140,14 @@ int oracle_socket_hash(int dtype, long long nkeys, int E, int tables, int bits, 
 int oracle_socket_scores(int dtype, int E, int tables, int bits, double tau, const void* q, const float* proj,
                          long long nkeys, const unsigned char* buckets, const double* vnorm, double* scores);
 
+/*
+ * SOCKET selection (same page, method step 4: a deterministic top-k).
+ *   oracle_socket_select: the top_k of nkeys scores, higher score first and,
+ *     among equal scores, the lower key index first; selected[0..top_k) gets
+ *     the chosen key indices in ascending order.  A NaN score returns -3.
+ */
+int oracle_socket_select(long long nkeys, const double* scores, long long top_k, long long* selected);
+
 /* Number of OpenMP threads oracle_attn_rows uses for a given `threads`. */
 int oracle_num_threads(int threads);
 

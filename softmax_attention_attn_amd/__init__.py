@@ -112,13 +112,46 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported element type {t.dtype} (bfloat16 or float32)")
 
 
+# Device type every tensor handed to the library must live on (the kernels dereference the
+# pointers on the GPU; a host pointer would fault it).
+_DEVICE_TYPE = "cuda"
+
+
+def _check_like(name: str, t: Optional[torch.Tensor], shape, dtype, device) -> None:
+    """Reject a caller-supplied tensor that the C ABI cannot size or type-check itself:
+    wrong shape, element type, device, or a non-contiguous layout."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_workspace(ws: Optional[torch.Tensor], device) -> None:
+    """A workspace is raw bytes: any element type, but contiguous and on the inputs' device
+    (its size is checked by the library against the *_workspace_bytes query)."""
+    if ws is None:
+        return
+    if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+
+
 def _common(q, k, v, sink, scale, mode, gamma):
     for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a tensor")
         if t.dim() != 4:
             raise ValueError(f"{name} must be 4-D, got {tuple(t.shape)}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-        if t.device.type != "cuda":
+        if t.device.type != _DEVICE_TYPE:
             raise ValueError(f"{name} must be on a GPU")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k and v must share one element type")
@@ -179,6 +212,13 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[fl
     returns (o, lse).  bias: float32 addend or bool mask (True = attend), shape (L, S) or
     (N or 1, Hq or 1, L, S); key_len: (N,) int32, real keys past key_len[n] are padding."""
     N, Hq, Hkv, L, S, E, scale, gamma = _common(q, k, v, sink, scale, mode, gamma)
+    _check_like("out", out, q.shape, q.dtype, q.device)
+    _check_like("lse", lse, (N, Hq, L), torch.float32, q.device)
+    kind, bt, sn, sh = (BIAS_NONE, None, 0, 0) if bias is None else _bias_args(bias, N, Hq, L, S, q.device)
+    if key_len is not None:
+        if not isinstance(key_len, torch.Tensor) or key_len.dtype != torch.int32 or key_len.numel() != N or \
+                key_len.device != q.device or not key_len.is_contiguous():
+            raise ValueError("key_len must be a contiguous int32 tensor of N values on q's device")
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -190,11 +230,6 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[fl
                           _ptr(out), _ptr(lse), _stream(q.device, stream))
         _check(rc)
         return out, lse
-    kind, bt, sn, sh = (BIAS_NONE, None, 0, 0) if bias is None else _bias_args(bias, N, Hq, L, S, q.device)
-    if key_len is not None:
-        if key_len.dtype != torch.int32 or key_len.numel() != N or key_len.device != q.device or \
-                not key_len.is_contiguous():
-            raise ValueError("key_len must be a contiguous int32 tensor of N values on q's device")
     rc = lib.attn_fwd_biased(_dtype_code(q), N, Hq, Hkv, L, S, E, _ptr(q), _ptr(k), _ptr(v), MODES[mode],
                              scale, gamma, int(bool(causal)), int(window), int(n_reg), _ptr(sink),
                              kind, _ptr(bt), sn, sh, _ptr(key_len), _ptr(out), _ptr(lse),
@@ -223,6 +258,9 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional
            lse: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Split-K decode (q has L == 1) through attn_decode; returns (o, lse)."""
     N, Hq, Hkv, L, S, E, scale, gamma = _common(q, k, v, sink, scale, mode, gamma)
+    _check_like("out", out, q.shape, q.dtype, q.device)
+    _check_like("lse", lse, (N, Hq, L), torch.float32, q.device)
+    _check_workspace(workspace, q.device)
     need = decode_workspace_bytes(N, Hq, Hkv, S, E, causal, window, n_reg, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -241,7 +279,7 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional
 
 def _cache_check(k_cache, v_cache, n_sink: int, window: int):
     for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
-        if t.dim() != 4 or not t.is_contiguous() or t.device.type != "cuda":
+        if not isinstance(t, torch.Tensor) or t.dim() != 4 or not t.is_contiguous() or t.device.type != _DEVICE_TYPE:
             raise ValueError(f"{name} must be a contiguous 4-D GPU tensor")
     if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype or k_cache.device != v_cache.device:
         raise ValueError("k_cache and v_cache must match in shape, element type and device")
@@ -255,7 +293,7 @@ def stream_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tenso
     cache (N, Hkv, n_sink + window, E) through attn_stream_append."""
     _cache_check(k_cache, v_cache, n_sink, window)
     for name, t in (("k_new", k_new), ("v_new", v_new)):
-        if t.dim() != 4 or not t.is_contiguous() or t.device != k_cache.device or t.dtype != k_cache.dtype:
+        if not isinstance(t, torch.Tensor) or t.dim() != 4 or not t.is_contiguous() or t.device != k_cache.device or t.dtype != k_cache.dtype:
             raise ValueError(f"{name} must be a contiguous 4-D tensor like the cache")
     if k_new.shape != v_new.shape:
         raise ValueError("k_new and v_new must have the same shape")
@@ -284,6 +322,9 @@ def stream_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     N, Hq, Hkv, L, _, E, scale, gamma = _common(q, k_cache, v_cache, sink, scale, mode, gamma)
     if L != 1:
         raise ValueError(f"stream_decode takes one query per sequence, got q {tuple(q.shape)}")
+    _check_like("out", out, q.shape, q.dtype, q.device)
+    _check_like("lse", lse, (N, Hq, L), torch.float32, q.device)
+    _check_workspace(workspace, q.device)
     need = stream_decode_workspace_bytes(N, Hq, Hkv, E, n_sink, window, pos, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -307,10 +348,10 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
     Returns (dq, dk, dv, dsink); dsink is None without a sink."""
     N, Hq, Hkv, L, S, E, scale, gamma = _common(q, k, v, sink, scale, mode, gamma)
     for name, t in (("o", o), ("dout", dout)):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
+        if not isinstance(t, torch.Tensor) or t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
             raise ValueError(f"{name} must be a contiguous tensor like q")
-    if lse.shape != (N, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 (N, Hq, L) tensor")
+    _check_like("lse", lse, (N, Hq, L), torch.float32, q.device)
+    _check_workspace(workspace, q.device)
     lib = load()
     need = int(lib.attn_bwd_workspace_bytes(N, Hq, L))
     if workspace is None:
@@ -348,10 +389,13 @@ def socket_hash(k: torch.Tensor, v: torch.Tensor, proj: torch.Tensor, *, tables:
     C = socket_code_bytes(tables, bits) (codes of at most 4 bits packed two per byte, see
     unpack_codes) and value norms (N, Hkv, S) float32 of a bf16 key/value cache; proj
     (tables*bits, E) float32."""
-    if k.dim() != 4 or not k.is_contiguous() or k.shape != v.shape or not v.is_contiguous():
-        raise ValueError("k and v must be contiguous 4-D tensors of one shape")
-    if proj.dtype != torch.float32 or not proj.is_contiguous() or proj.shape != (tables * bits, k.shape[3]):
-        raise ValueError(f"proj must be a contiguous float32 ({tables * bits}, {k.shape[3]}) tensor")
+    for name, t in (("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4 or not t.is_contiguous() or \
+                t.device.type != _DEVICE_TYPE:
+            raise ValueError(f"{name} must be a contiguous 4-D GPU tensor")
+    if k.shape != v.shape or k.dtype != v.dtype or k.device != v.device:
+        raise ValueError("k and v must match in shape, element type and device")
+    _check_like("proj", proj, (tables * bits, k.shape[3]), torch.float32, k.device)
     N, Hkv, S, E = k.shape
     buckets = torch.empty((N, Hkv, S, socket_code_bytes(tables, bits)), dtype=torch.uint8, device=k.device)
     vnorm = torch.empty((N, Hkv, S), dtype=torch.float32, device=k.device)
@@ -371,6 +415,12 @@ def socket_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, proj: torch
     N, Hq, Hkv, L, S, E, scale, gamma = _common(q, k, v, sink, scale, mode, gamma)
     if L != 1:
         raise ValueError(f"socket_decode takes one query per sequence, got q {tuple(q.shape)}")
+    _check_like("proj", proj, (tables * bits, E), torch.float32, q.device)
+    _check_like("buckets", buckets, (N, Hkv, S, socket_code_bytes(tables, bits)), torch.uint8, q.device)
+    _check_like("vnorm", vnorm, (N, Hkv, S), torch.float32, q.device)
+    _check_like("out", out, q.shape, q.dtype, q.device)
+    _check_like("lse", lse, (N, Hq, 1), torch.float32, q.device)
+    _check_workspace(workspace, q.device)
     lib = load()
     need = int(lib.attn_socket_decode_workspace_bytes(N, Hq, Hkv, S, E, tables, bits, top_k, num_splits))
     if workspace is None:

@@ -89,3 +89,48 @@ def check(w: Workload, inp: gen.Inputs, o_gpu, lse_gpu, rows=None, threads=0, bi
     assert eo <= TOL_O[w.dtype], f"{w.name}: O error {eo:.3e} > {TOL_O[w.dtype]}"
     assert el <= TOL_LSE, f"{w.name}: LSE error {el:.3e} > {TOL_LSE}"
     return eo, el
+
+
+def check_socket_heads(w: Workload, inp: gen.Inputs, top_k: int, sc_ref, sel_ref, o_ref, l_ref, og, lg, sg,
+                       heads=None):
+    """Check a SOCKET sparse decode head by head; returns the number of heads whose top-k is unique.
+
+    sc_ref, sel_ref, o_ref, l_ref: the oracle's scores (fp64), selection and sparse output;
+    og, lg, sg: the GPU's output, LSE and selected key indices (numpy).  heads: (n, h) pairs
+    to check (default: all).  For every head the selection must be valid against the
+    oracle's scores (ascending, top_k keys, every key clearly above the k-th score s_k
+    chosen, every chosen key at least s_k (1 - 1e-4): fp32 against fp64 scores); where it
+    is unique (no other key within that band) it must equal the oracle's.  Several
+    selections are correct only when scores tie within the band; for every head, unique or
+    not, the output must then be exact attention (oracle) over the keys the GPU chose,
+    within 2e-2 (O) / 1e-3 (LSE), and for unique heads the oracle's own sparse output too.
+    """
+    G = w.Hq // w.Hkv
+    unique = 0
+    heads = heads if heads is not None else [(n, h) for n in range(w.N) for h in range(w.Hq)]
+    for n, h in heads:
+        sc = sc_ref[n, h]
+        sk = np.sort(sc)[::-1][top_k - 1]
+        hi, lo = sk * (1 + 1e-4), sk * (1 - 1e-4)
+        chosen = np.zeros(sc.shape[0], bool)
+        chosen[sg[n, h]] = True
+        assert np.all(np.diff(sg[n, h]) > 0), f"head {(n, h)}: selection not ascending / repeated"
+        assert chosen.sum() == top_k
+        assert np.all(chosen[sc > hi]), f"head {(n, h)}: a clearly better key was left out"
+        assert np.all(sc[chosen] >= lo), f"head {(n, h)}: a clearly worse key was chosen"
+        if np.sum(sc >= lo) == top_k:  # the top-k set is unique
+            unique += 1
+            assert np.array_equal(sg[n, h], sel_ref[n, h]), f"head {(n, h)}: selection differs"
+            assert np.max(np.abs(og[n, h] - o_ref[n, h])) <= 2e-2
+            assert abs(lg[n, h, 0] - l_ref[n, h, 0]) <= 1e-3
+        kh = h // G
+        idx = np.asarray(sg[n, h], dtype=np.int64)
+        kk = np.ascontiguousarray(inp.k[n:n + 1, kh:kh + 1, idx])
+        vv = np.ascontiguousarray(inp.v[n:n + 1, kh:kh + 1, idx])
+        sk_h = None if inp.sink is None else np.asarray(inp.sink, dtype=np.float64)[h:h + 1]
+        o_sel, l_sel = oracle.attn(np.ascontiguousarray(inp.q[n:n + 1, h:h + 1]), kk, vv, mode=w.mode,
+                                   scale=w.scale, gamma=w.gamma, sink=sk_h)
+        eo = float(np.max(np.abs(og[n, h] - o_sel[0, 0])))
+        el = float(abs(lg[n, h, 0] - l_sel[0, 0, 0]))
+        assert eo <= 2e-2 and el <= 1e-3, f"head {(n, h)}: attention over the chosen keys off by {eo:.3e} / {el:.3e}"
+    return unique

@@ -652,4 +652,89 @@ def pin_socket_selection_is_top_k_by_score(lib):
         assert chosen.sum() == 20 and s[chosen].min() >= s[~chosen].max()
 
 
+def pin_socket_selection_ties_to_lower_index(lib):
+    # Method step 4 asks for a deterministic top-k; the reading taken is: higher score first,
+    # equal scores by lower key index.  (1) A hand-worked case whose ties straddle the cut:
+    # scores 5 5 | 3 3 3 3 | 1 at keys 0,6 | 1,2,3,5 | 4, top 4 -> keys 0, 6, then 1, 2.
+    sel = oracle.socket_select(np.array([5.0, 3.0, 3.0, 3.0, 1.0, 3.0, 5.0]), 4, lib=lib)
+    assert sel.tolist() == [0, 1, 2, 6]
+    # every key tied: the first top_k keys
+    assert oracle.socket_select(np.full(9, 2.5), 3, lib=lib).tolist() == [0, 1, 2]
+    assert oracle.socket_select(np.array([1.0, 2.0]), 0, lib=lib).tolist() == []
+    # (2) Brute force over every subset on tiny inputs with many ties: the chosen set holds
+    # the top_k largest scores (as a multiset), and of all such sets it is the one whose
+    # ascending index list is lexicographically smallest.
+    import itertools
+    r = _rng(90)
+    for trial in range(60):
+        S = int(r.integers(1, 10))
+        k = int(r.integers(0, S + 1))
+        sc = r.integers(0, 3, size=S).astype(np.float64)
+        best = None
+        for comb in itertools.combinations(range(S), k):
+            key = (sorted((-sc[list(comb)]).tolist()), list(comb))
+            if best is None or key < best:
+                best = key
+        assert oracle.socket_select(sc, k, lib=lib).tolist() == best[1], (sc, k)
+
+
+def _round_f32_exact(x):
+    """x (a Fraction) rounded to the nearest float32, ties to even (normal range only)."""
+    from fractions import Fraction
+    if x == 0:
+        return Fraction(0)
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    elif Fraction(2) ** (e + 1) <= a:
+        e += 1
+    assert -126 <= e < 128
+    quantum = Fraction(2) ** (e - 23)
+    m = a / quantum
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return (fl * quantum) if x > 0 else -(fl * quantum)
+
+
+def _f32_chain_sign(k, w, order, fused):
+    """Sign bit (x > 0) of a float32 dot product accumulated over `order` with exact
+    rational arithmetic and one IEEE rounding per step (a fused multiply-add, or a
+    rounded product then a rounded sum)."""
+    from fractions import Fraction
+    x = Fraction(0)
+    for e in order:
+        prod = Fraction(float(k[e])) * Fraction(float(w[e]))
+        if fused:
+            x = _round_f32_exact(prod + x)
+        else:
+            x = _round_f32_exact(_round_f32_exact(prod) + x)
+    return 1 if x > 0 else 0
+
+
+def pin_socket_hash_fp32_fma_in_element_order(lib):
+    # The bucket bit is decided in float32 (reading of method step 1: the precision that
+    # makes the integer decision).  Keys are built so that their projection nearly cancels
+    # (the last element undoes the others to float32 precision); there the sign depends on
+    # the rounding order, and the oracle must follow a fused multiply-add per element in
+    # element order, modelled here with exact rational arithmetic.
+    E, nkeys = 8, 400
+    r = _rng(91)
+    w = r.standard_normal(E).astype(np.float32)
+    keys = r.standard_normal((nkeys, E)).astype(np.float32)
+    head = keys[:, :E - 1].astype(np.float64) @ w[:E - 1].astype(np.float64)
+    keys[:, E - 1] = (-head / float(w[E - 1])).astype(np.float32)
+    codes, _ = oracle.socket_hash(keys[None, None], keys[None, None], w[None, :], 1, 1, lib=lib)
+    fwd = list(range(E))
+    want = np.array([_f32_chain_sign(keys[j], w, fwd, True) for j in range(nkeys)])
+    got = codes[0, 0, :, 0].astype(np.int64)
+    assert np.array_equal(got, want)
+    # the construction really separates the conventions: element order and fusion both matter
+    rev = np.array([_f32_chain_sign(keys[j], w, fwd[::-1], True) for j in range(nkeys)])
+    unf = np.array([_f32_chain_sign(keys[j], w, fwd, False) for j in range(nkeys)])
+    assert np.sum(rev != want) >= 10 and np.sum(unf != want) >= 10
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

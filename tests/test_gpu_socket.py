@@ -8,8 +8,10 @@ the k-th and (k+1)-th scores are apart: with the oracle's fp64 scores, every
 key scoring above s_k (1 + 1e-4) must be chosen and every chosen key must score
 at least s_k (1 - 1e-4) (s_k the k-th largest score); where no other key lies
 in that band the chosen set must equal the oracle's and the output must match
-the oracle's sparse attention within 2e-2 (O) / 1e-3 (LSE).  With top_k = S the
-sparse decode must equal the dense decode.
+the oracle's sparse attention within 2e-2 (O) / 1e-3 (LSE).  Where scores tie
+within the band several selections are correct; for every head the output must
+be exact attention (the oracle) over the keys the GPU chose, to the same bars.
+With top_k = S the sparse decode must equal the dense decode.
 
 Exact ties: keys that are copies of one key (same K and V rows) get bit-equal
 scores on both sides, so a selection whose only near-threshold keys are such a
@@ -24,7 +26,7 @@ import torch
 
 import oracle
 import softmax_attention_attn_amd as attn
-from gpu_util import say, to_device
+from gpu_util import check_socket_heads, say, to_device
 from workloads import gen
 from workloads.configs import Workload
 
@@ -84,25 +86,9 @@ def test_socket_decode(w, tables, bits, tau, top_k, splits):
         og = o.float().cpu().numpy().astype(np.float64)
         lg = lse.cpu().numpy().astype(np.float64)
         sg = sel.cpu().numpy()
-        unique = 0
-        for n in range(w.N):
-            for h in range(w.Hq):
-                sc = sc_ref[n, h]
-                sk = np.sort(sc)[::-1][top_k - 1]
-                hi, lo = sk * (1 + 1e-4), sk * (1 - 1e-4)
-                chosen = np.zeros(w.S, bool)
-                chosen[sg[n, h]] = True
-                assert np.all(np.diff(sg[n, h]) > 0), "selection not ascending / repeated"
-                assert chosen.sum() == top_k
-                assert np.all(chosen[sc > hi]), "a clearly better key was left out"
-                assert np.all(sc[chosen] >= lo), "a clearly worse key was chosen"
-                if np.sum(sc >= lo) == top_k:  # the top-k set is unique: compare exactly
-                    unique += 1
-                    assert np.array_equal(sg[n, h], sel_ref[n, h])
-                    assert np.max(np.abs(og[n, h] - o_ref[n, h])) <= 2e-2
-                    assert abs(lg[n, h, 0] - l_ref[n, h, 0]) <= 1e-3
-        say(f"  splits={s}: {unique}/{w.N * w.Hq} heads with a unique top-k, all checked")
-        assert unique >= 0.75 * w.N * w.Hq
+        unique = check_socket_heads(w, inp, top_k, sc_ref, sel_ref, o_ref, l_ref, og, lg, sg)
+        say(f"  splits={s}: {unique}/{w.N * w.Hq} heads with a unique top-k; every head's output checked "
+            f"against exact attention over its chosen keys")
 
 
 def test_socket_full_budget_equals_dense_decode():
@@ -171,9 +157,6 @@ def test_socket_exact_ties(name, S, E, rank, group, keep, seed, extra):
         sg = sel.cpu().numpy()
         og = o.float().cpu().numpy().astype(np.float64)
         lg = lse.cpu().numpy().astype(np.float64)
-        for h in range(w.Hq):
-            if h == 0:  # the copies were placed by head 0's ranking
-                assert np.array_equal(sg[0, h], sel_ref[0, h]), "tie-broken selection differs"
-                assert np.max(np.abs(og[0, h] - o_ref[0, h])) <= 2e-2
-                assert abs(lg[0, h, 0] - l_ref[0, h, 0]) <= 1e-3
-            assert np.all(np.diff(sg[0, h]) > 0)
+        # the copies were placed by head 0's ranking: its tie-broken selection is fixed by the rule
+        assert np.array_equal(sg[0, 0], sel_ref[0, 0]), "tie-broken selection differs"
+        check_socket_heads(w, inp, top_k, sc_ref, sel_ref, o_ref, l_ref, og, lg, sg)

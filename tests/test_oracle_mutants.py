@@ -44,6 +44,12 @@ MUTANTS = {
     "socket_tau_inverted": ("a += ((c >> b) & 1 ? 1.0 : -1.0) * y[b] / tau;", "a += ((c >> b) & 1 ? 1.0 : -1.0) * y[b] * tau;"),
     "socket_bits_reversed": ("a += ((c >> b) & 1 ? 1.0 : -1.0) * y[b] / tau;",
                              "a += ((c >> (bits - 1 - b)) & 1 ? 1.0 : -1.0) * y[b] / tau;"),
+    "socket_select_ties_to_higher_index": ("return (x->idx < y->idx) ? -1 : 1;", "return (x->idx > y->idx) ? -1 : 1;"),
+    "socket_select_lowest_first": ("if (x->score > y->score) return -1;", "if (x->score < y->score) return -2;"),
+    "socket_hash_reverse_element_order": ("for (int e = 0; e < E; ++e) x = fmaf(",
+                                          "for (int e = E - 1; e >= 0; --e) x = fmaf("),
+    "socket_hash_unfused": ("x = fmaf((float)load_elem(dtype, k, (size_t)j * E + e), w[e], x);",
+                            "x = x + (float)load_elem(dtype, k, (size_t)j * E + e) * w[e];"),
     "bwd_dv_unweighted": ("gv[e] += p * load_elem(dtype, dout, qoff + e);", "gv[e] += load_elem(dtype, dout, qoff + e);"),
     "head_dim_truncated": ("for (int e = 0; e < E; ++e) acc += load_elem(dtype, q, qoff + e)",
                            "for (int e = 0; e < E - 1; ++e) acc += load_elem(dtype, q, qoff + e)"),
