@@ -187,6 +187,29 @@ size_t attn_decode_workspace_bytes(int N, int Hq, int Hkv, int S, int E, int cau
                                    int n_reg, int num_splits);
 
 /*
+ * attn_decode_noalloc -- attn_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, semantics, kernels and results as
+ * attn_decode with the same split count, but no workspace: the split partials
+ * go to a static device array of ATTN_DECODE_NOALLOC_SCRATCH_BYTES (8 MiB) that
+ * the library holds on every GPU it runs on until the process ends.  Sizes
+ * whose partials (attn_decode_workspace_bytes(...) for the same arguments)
+ * exceed it return ATTN_ERR_WORKSPACE before any HIP call: 8 MiB holds, e.g.,
+ * 8 sequences x 32 query heads x 64 splits at E = 128.  Calls no allocator.
+ * Every call on one GPU shares that GPU's array and overwrites what the last
+ * call left there (nothing is read before it is written, so no clearing is
+ * needed); calls that may overlap on one GPU (different streams, or host
+ * threads) race and must be serialised by the caller.  The first call on a
+ * device looks the array's address up (hipGetSymbolAddress) and caches it.
+ */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int attn_decode_noalloc(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E,
+                        const void* q, const void* k, const void* v,
+                        attn_mode mode, float scale, float gamma,
+                        int causal, int window, int n_reg, const float* sink,
+                        void* o, float* lse, int num_splits, void* stream);
+
+/*
  * Rolling key/value cache for streaming decode ("Attention Sink LLM..." page,
  * section 3.2, StreamingLLM): the key/value rows of the first n_sink tokens
  * stay in the cache for good, and only the `window` most recent tokens after

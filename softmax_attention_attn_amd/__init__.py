@@ -34,6 +34,7 @@ BF16, F32 = 0, 1
 MODES = {"dot": 0, "rbf": 1}
 
 EXPORTS = ("attn_fwd", "attn_fwd_biased", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_num_splits", "attn_decode_workspace_bytes",
+           "attn_decode_noalloc",
            "attn_stream_append", "attn_stream_decode", "attn_stream_decode_workspace_bytes",
            "attn_socket_hash", "attn_socket_code_bytes", "attn_socket_decode", "attn_socket_decode_workspace_bytes",
            "attn_status_string", "attn_last_error")
@@ -67,6 +68,8 @@ def load() -> ctypes.CDLL:
         lib.attn_bwd_workspace_bytes.argtypes = [I, I, I]
         lib.attn_decode.restype = I
         lib.attn_decode.argtypes = [I, I, I, I, I, I, I, P, P, P, I, F, F, I, I, I, P, P, P, I, P, Z, P]
+        lib.attn_decode_noalloc.restype = I
+        lib.attn_decode_noalloc.argtypes = [I, I, I, I, I, I, I, P, P, P, I, F, F, I, I, I, P, P, P, I, P]
         lib.attn_decode_num_splits.restype = I
         lib.attn_decode_num_splits.argtypes = [I] * 8
         lib.attn_decode_workspace_bytes.restype = Z
@@ -273,6 +276,28 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional
                          scale, gamma, int(bool(causal)), int(window), int(n_reg), _ptr(sink),
                          _ptr(out), _ptr(lse), int(num_splits), _ptr(workspace),
                          workspace.numel() * workspace.element_size(), _stream(q.device, stream))
+    _check(rc)
+    return out, lse
+
+
+DECODE_NOALLOC_SCRATCH_BYTES = 8 << 20  # ATTN_DECODE_NOALLOC_SCRATCH_BYTES of include/attn.h
+
+
+def decode_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
+                   mode: str = "dot", gamma: Optional[float] = None, causal: bool = True, window: int = 0,
+                   n_reg: int = 0, sink: Optional[torch.Tensor] = None, num_splits: int = 0,
+                   out: torch.Tensor, lse: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-K decode through attn_decode_noalloc: like decode, but the split partials go to
+    the library's static device scratch (no workspace, no allocation by the library or
+    here: out and lse must be given).  Calls that overlap on one GPU race."""
+    N, Hq, Hkv, L, S, E, scale, gamma = _common(q, k, v, sink, scale, mode, gamma)
+    if out is None or lse is None:
+        raise ValueError("decode_noalloc needs out and lse (it allocates nothing)")
+    _check_like("out", out, q.shape, q.dtype, q.device)
+    _check_like("lse", lse, (N, Hq, L), torch.float32, q.device)
+    rc = load().attn_decode_noalloc(_dtype_code(q), N, Hq, Hkv, L, S, E, _ptr(q), _ptr(k), _ptr(v), MODES[mode],
+                                    scale, gamma, int(bool(causal)), int(window), int(n_reg), _ptr(sink),
+                                    _ptr(out), _ptr(lse), int(num_splits), _stream(q.device, stream))
     _check(rc)
     return out, lse
 

@@ -132,6 +132,32 @@ long long stream_rows(int n_sink, int window, long long pos) {
   return pos + 1 < cap ? pos + 1 : cap;
 }
 
+// Validation and launch set-up shared by attn_decode and attn_decode_noalloc:
+// everything but the partial-result buffers.  *need = their size in bytes.
+// Returns ATTN_OK (with *empty set when there is nothing to compute) or an error.
+int decode_setup(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, const void* q, const void* k,
+                 const void* v, attn_mode mode, float scale, float gamma, int causal, int window, int n_reg,
+                 const float* sink, void* o, float* lse, int num_splits, attn_impl::DecodeArgs* d, size_t* need,
+                 bool* empty) {
+  *empty = false;
+  if (L != 1) return fail(ATTN_ERR_SHAPE, "decode takes exactly one query per sequence (L=%d)", L);
+  int rc = check_args(dt, N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o, lse);
+  if (rc != ATTN_OK) return rc;
+  if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode is implemented for bf16 only");
+  if (num_splits < 0) return fail(ATTN_ERR_ARG, "num_splits=%d must be >= 0", num_splits);
+  if (N == 0) {
+    *empty = true;
+    return ATTN_OK;
+  }
+  const int splits = resolve_splits(N, Hq, Hkv, S, causal, window, n_reg, num_splits);
+  *need = workspace_for(N, Hq, E, splits);
+  if ((long long)N * Hkv * ((Hq / Hkv + 15) / 16) > 65535LL || (long long)N * Hq > kMaxGrid)
+    return fail(ATTN_ERR_SHAPE, "grid too large");
+  d->f = make_args(N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o, lse);
+  d->num_splits = splits;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 #pragma GCC visibility push(default)
@@ -373,26 +399,44 @@ int attn_decode(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, cons
                 const void* v, attn_mode mode, float scale, float gamma, int causal, int window, int n_reg,
                 const float* sink, void* o, float* lse, int num_splits, void* workspace, size_t workspace_bytes,
                 void* stream) {
-  if (L != 1) return fail(ATTN_ERR_SHAPE, "decode takes exactly one query per sequence (L=%d)", L);
-  int rc = check_args(dt, N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o, lse);
+  attn_impl::DecodeArgs d;
+  size_t need = 0;
+  bool empty = false;
+  const int rc = decode_setup(dt, N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o,
+                              lse, num_splits, &d, &need, &empty);
   if (rc != ATTN_OK) return rc;
-  if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode is implemented for bf16 only");
-  if (num_splits < 0) return fail(ATTN_ERR_ARG, "num_splits=%d must be >= 0", num_splits);
-  if (N == 0) return ok();
-  const int splits = resolve_splits(N, Hq, Hkv, S, causal, window, n_reg, num_splits);
-  const size_t need = workspace_for(N, Hq, E, splits);
+  if (empty) return ok();
   if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
   if (workspace_bytes < need)
     return fail(ATTN_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, need);
   if (!aligned(workspace, 16)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
-  if ((long long)N * Hkv * ((Hq / Hkv + 15) / 16) > 65535LL || (long long)N * Hq > kMaxGrid)
-    return fail(ATTN_ERR_SHAPE, "grid too large");
-  attn_impl::DecodeArgs d;
-  d.f = make_args(N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o, lse);
-  d.num_splits = splits;
   d.part_o = static_cast<float*>(workspace);
-  d.part_ml = d.part_o + (size_t)N * Hq * splits * E;
+  d.part_ml = d.part_o + (size_t)N * Hq * d.num_splits * E;
   return hip_status(attn_impl::launch_decode_bf16(d, static_cast<hipStream_t>(stream)), "attn_decode launch");
+}
+
+int attn_decode_noalloc(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, const void* q, const void* k,
+                        const void* v, attn_mode mode, float scale, float gamma, int causal, int window, int n_reg,
+                        const float* sink, void* o, float* lse, int num_splits, void* stream) {
+  attn_impl::DecodeArgs d;
+  size_t need = 0;
+  bool empty = false;
+  const int rc = decode_setup(dt, N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o,
+                              lse, num_splits, &d, &need, &empty);
+  if (rc != ATTN_OK) return rc;
+  if (empty) return ok();
+  if (need > attn_impl::kDecodeScratchBytes)
+    return fail(ATTN_ERR_WORKSPACE,
+                "these sizes need %zu bytes of split partials; the library's static scratch holds %zu "
+                "(use fewer splits, or attn_decode with a workspace)", need, attn_impl::kDecodeScratchBytes);
+  float* scratch = nullptr;
+  const hipError_t e = attn_impl::decode_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e, "attn_decode_noalloc scratch lookup");
+  // Every split writes all of its partials (an empty split writes max -inf, sum 0),
+  // so nothing left by an earlier call is read: no clearing is needed.
+  d.part_o = scratch;
+  d.part_ml = scratch + (size_t)N * Hq * d.num_splits * E;
+  return hip_status(attn_impl::launch_decode_bf16(d, static_cast<hipStream_t>(stream)), "attn_decode_noalloc launch");
 }
 
 // ----------------------------------------------------------------------------- rolling cache

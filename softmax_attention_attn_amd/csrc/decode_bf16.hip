@@ -25,12 +25,25 @@
 // first copies its split's part of the list (at most kDecodeIndexMax rows)
 // into LDS, where the row addresses of every step are then read without a
 // global-memory round trip.
+#include <mutex>
+
 #include "device_common.h"
 #include "kernels.h"
 
 using namespace attn_dev;
 
 namespace {
+
+// Scratch for attn_decode_noalloc: the split partials of one call live in this
+// file-scope device array instead of a caller workspace.  Each GPU the library
+// runs on holds its own copy (at its own address) until the process ends; the
+// host reaches it only through the address hipGetSymbolAddress returns for the
+// current device, never through the array's name.
+static __device__ __align__(256) unsigned char scratch[attn_impl::kDecodeScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 constexpr int NT = 256;   // threads per workgroup
 constexpr int NWAVE = 4;
@@ -379,6 +392,23 @@ DecodeKeys decode_keys(int S, int n_reg, int causal, int window) {
   dk.first_real = (causal && window > 0) ? (S_real > window ? S_real - window : 0) : 0;
   dk.count = n_reg + (S_real - dk.first_real);
   return dk;
+}
+
+hipError_t decode_scratch(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<float*>(g_scratch_ptr[dev]);
+  return hipSuccess;
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {

@@ -9,6 +9,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "attn.h"
+
 namespace attn_impl {
 
 // Everything a forward kernel needs; element pointers are raw bit storage
@@ -51,6 +53,12 @@ struct DecodeArgs {
 hipError_t launch_prefill_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+
+// Device scratch for the no-allocation decode (decode_bf16.hip): a static
+// device array of kDecodeScratchBytes per GPU.  decode_scratch() returns its
+// address on the current device (looked up once per device, then cached).
+constexpr size_t kDecodeScratchBytes = ATTN_DECODE_NOALLOC_SCRATCH_BYTES;
+hipError_t decode_scratch(float** out);
 
 // Backward: gradients of O for the upstream gradient dout (bf16, no user bias).
 // workspace: backward_workspace_bytes(N, Hq, L) bytes (D_i, reference max per

@@ -318,3 +318,18 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(attn, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         attn.load()
+
+
+def test_decode_noalloc_rejects_before_any_hip_call(lib):
+    # partials beyond the static scratch, L != 1, bad dtype: all refused on the host
+    big = lib.attn_decode_noalloc(0, 64, 64, 8, 1, 1 << 20, 128, A, A, A, 0, 0.1, 0.0, 1, 0, 0, None, A, A, 4096,
+                                  None)
+    assert big == -6 and b"static scratch" in lib.attn_last_error()
+    assert lib.attn_decode_noalloc(0, 1, 4, 2, 2, 64, 64, A, A, A, 0, 0.1, 0.0, 1, 0, 0, None, A, A, 0, None) == -2
+    assert lib.attn_decode_noalloc(1, 1, 4, 2, 1, 64, 64, A, A, A, 0, 0.1, 0.0, 1, 0, 0, None, A, A, 0, None) == -4
+    assert lib.attn_decode_noalloc(0, 1, 4, 3, 1, 64, 64, A, A, A, 0, 0.1, 0.0, 1, 0, 0, None, A, A, 0, None) == -2
+    # nothing to compute: no HIP call either
+    assert lib.attn_decode_noalloc(0, 0, 4, 2, 1, 64, 64, None, None, None, 0, 0.1, 0.0, 1, 0, 0, None, None, None,
+                                   0, None) == 0
+    # the bytes the scratch holds, as the header states
+    assert attn.DECODE_NOALLOC_SCRATCH_BYTES == 8 << 20
