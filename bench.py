@@ -18,8 +18,12 @@ back-to-back calls between two events; a second pass with one event pair per
 call gives the spread of single calls ("ms_spread": p10 / p50 / p90).
 
 The CPU baseline leg times the fp64 oracle on a bounded sample of rows of the
-headline workload, on this host's cores, and checks the GPU output on those
-rows against it.
+headline workload (about 15 s) and of every other forward and decode workload
+(about 4 s each), on this host's cores, and checks the GPU output on those rows
+against it ("cpu_baseline" and "parity" of the line and of each extra).  Every
+workload is warmed up for at least 200 ms before its K timed calls, so that no
+timing falls in the clock ramp of the first calls.  The long-context decode
+figure is repeated at top level under "decode" (the metric's second half).
 
 Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits with a
 message.
@@ -48,6 +52,7 @@ METRIC = "prefill TFLOP/s + decode HBM GB/s, as % of MI355X roofline, oracle-exa
 
 KERNEL_FILES = {
     "prefill_bf16": "softmax_attention_attn_amd/csrc/prefill_bf16.hip",
+    "prefill_bf16_band": "softmax_attention_attn_amd/csrc/prefill_bf16_band.hip",
     "prefill_f32": "softmax_attention_attn_amd/csrc/prefill_f32.hip",
     "decode_bf16": "softmax_attention_attn_amd/csrc/decode_bf16.hip",
 }
@@ -58,9 +63,15 @@ def log(msg: str) -> None:
 
 
 def kernel_of(w) -> str:
+    """Source file (KERNEL_FILES key) of the kernel the library runs for this workload."""
     if w.decode:
         return "decode_bf16"
-    return "prefill_bf16" if w.dtype == "bf16" else "prefill_f32"
+    if w.dtype != "bf16":
+        return "prefill_f32"
+    # the library's key-band kernel: narrow causal windows, E = 64, dot, GQA 4 or 8, nothing else
+    band = (w.E == 64 and w.mode == "dot" and w.causal and 0 < w.window <= 128 and w.n_reg == 0
+            and w.bias == "none" and not w.key_len and w.Hq // w.Hkv in (4, 8))
+    return "prefill_bf16_band" if band else "prefill_bf16"
 
 
 def source_sha(kernel: str) -> str:
@@ -79,6 +90,25 @@ def measured_traffic(kernel: str, workload: str):
     if not m_sha or not m_b or m_sha.group(1) != source_sha(kernel):
         return None
     return float(m_b.group(1))
+
+
+def measured_mfma_busy(kernel: str, workload: str):
+    """MFMA busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over all SIMDs' active cycles) from the
+    committed counter summary, if it was taken on this source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}__mfma_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"mfma_busy_fraction:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != source_sha(kernel):
+        return None
+    return float(m_b.group(1))
+
+
+def default_rotation(w) -> int:
+    """Buffer sets to cycle through so that HBM, not the 256 MB on-die cache, serves the inputs."""
+    return 3 if (not w.decode and configs.algorithmic_bytes(w) < 256e6 and w.name == configs.C4.name) else 1
 
 
 def to_device(inp, torch, dev):
@@ -122,6 +152,22 @@ def timed(name, call, steps: int, torch, dev):
     return ms
 
 
+WARM_MS = 200.0  # every workload is warmed up for at least this long (clocks ramp up over the first calls)
+
+
+def warm(call, warmup: int, torch):
+    """At least `warmup` calls and at least WARM_MS of back-to-back calls."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < warmup or (time.perf_counter() - t0) * 1e3 < WARM_MS:
+        call(i)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return i
+
+
 def time_workload(w, steps: int, warmup: int, rotate: int, torch, attn, keep_first_output=False):
     """Average ms per call over `steps` back-to-back calls, inputs resident in HBM."""
     dev = torch.device("cuda:0")
@@ -155,8 +201,7 @@ def time_workload(w, steps: int, warmup: int, rotate: int, torch, attn, keep_fir
     call(0)
     torch.cuda.synchronize()
     first = (outs[0][0].clone(), outs[0][1].clone()) if keep_first_output else None
-    for i in range(warmup):
-        call(i)
+    warm(call, warmup, torch)
     ms = timed(w.name, call, steps, torch, dev)
     return ms, inp, first
 
@@ -187,8 +232,7 @@ def time_stream(sw, steps: int, warmup: int, rotate: int, torch, attn):
         attn.stream_decode(q, k_c, v_c, scale=sw.scale, mode=sw.mode, gamma=sw.gamma, sink=sink, workspace=ws,
                            out=o, lse=lse, **kw)
 
-    for i in range(warmup + 1):
-        call(i)
+    warm(call, warmup + 1, torch)
     return timed(sw.name, call, steps, torch, dev)
 
 
@@ -209,8 +253,7 @@ def time_backward(w, steps: int, warmup: int, torch, attn):
     def call(_i):
         attn.bwd(q, k, v, o, lse, do, workspace=ws, **kw)
 
-    for i in range(warmup + 1):
-        call(i)
+    warm(call, warmup + 1, torch)
     return timed(w.name + "__backward", call, steps, torch, dev)
 
 
@@ -234,8 +277,7 @@ def time_socket(sw, steps: int, warmup: int, torch, attn):
     def call(_i):
         attn.socket_decode(q, k, v, proj, buckets, vnorm, **kw)
 
-    for i in range(warmup + 1):
-        call(i)
+    warm(call, warmup + 1, torch)
     return timed(sw.name, call, steps, torch, dev)
 
 
@@ -263,7 +305,8 @@ def rate(w, ms: float):
 
 
 def cpu_baseline(w, inp, o_gpu, lse_gpu, seconds: float):
-    """Time the fp64 oracle on a bounded row sample; compare the GPU rows with it."""
+    """Time the fp64 oracle on a bounded row sample (all rows when they fit the time budget);
+    compare the GPU rows with it.  Returns (cpu_baseline, parity) dicts."""
     import numpy as np
 
     import oracle
@@ -281,11 +324,13 @@ def cpu_baseline(w, inp, o_gpu, lse_gpu, seconds: float):
     t0 = time.perf_counter()
     o_ref, lse_ref = oracle.attn_workload(inp, rows=rows, threads=threads)
     el = time.perf_counter() - t0
-    # algorithmic work of exactly these rows
+    # algorithmic work of exactly these rows (visible pairs, padding keys excluded)
     off = w.S_real - w.L
     i = rows % w.L
+    nn = rows // (w.Hq * w.L)
+    kl = np.asarray(w.key_len, dtype=np.int64)[nn] if w.key_len else np.full_like(i, w.S_real)
     ip = i + off
-    hi = np.minimum(w.S_real - 1, ip) if w.causal else np.full_like(i, w.S_real - 1)
+    hi = np.minimum(kl - 1, ip) if w.causal else kl - 1
     lo = np.maximum(0, ip - w.window + 1) if w.window > 0 else np.zeros_like(i)
     pairs = float(np.maximum(0, hi - lo + 1).sum() + w.n_reg * len(rows))
     flops = 4.0 * w.E * pairs
@@ -294,12 +339,19 @@ def cpu_baseline(w, inp, o_gpu, lse_gpu, seconds: float):
     eo = float(np.abs(og - o_ref).max())
     finite = np.isfinite(lse_ref)
     el_lse = float(np.abs(lg[finite] - lse_ref[finite]).max()) if finite.any() else 0.0
+    same_inf = bool(np.array_equal(np.isneginf(lg), np.isneginf(lse_ref)))
     tol = 2e-2 if w.dtype == "bf16" else 1e-4
-    base = {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(rows)} of {total} output rows of {w.name} (seeded uniform sample), "
-                      f"{pairs:.4g} visible pairs, {el:.1f}s wall, fp64, OpenMP over rows"}
+    if w.decode:
+        # decode is priced in bytes: the K/V rows the sampled query heads read
+        byts = float(len(rows) * (w.S * 2 * w.E * (2 if w.dtype == "bf16" else 4)))
+        base = {"value": byts / el / 1e9, "unit": "GB/s"}
+    else:
+        base = {"value": flops / el / 1e12, "unit": "TFLOP/s"}
+    base.update({"cores": threads, "kind": "oracle",
+                 "sample": f"{len(rows)} of {total} output rows of {w.name} (seeded uniform sample), "
+                           f"{pairs:.4g} visible pairs, {el:.2f}s wall, fp64, OpenMP over rows"})
     parity = {"rows": len(rows), "max_abs_err_o": eo, "max_abs_err_lse": el_lse, "tol_o": tol,
-              "tol_lse": 1e-3, "pass": bool(eo <= tol and el_lse <= 1e-3)}
+              "tol_lse": 1e-3, "pass": bool(eo <= tol and el_lse <= 1e-3 and same_inf)}
     return base, parity
 
 
@@ -312,7 +364,13 @@ def main() -> int:
                     choices=sorted(configs.BY_NAME) + sorted(configs.STREAM_BY_NAME) + sorted(configs.SOCKET_BY_NAME) +
                     sorted(w.name + "__backward" for w in configs.BACKWARD))
     ap.add_argument("--extras", default="all", choices=["all", "none"])
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="oracle time budget for the headline workload's CPU baseline")
+    ap.add_argument("--cpu-seconds-extra", type=float, default=4.0,
+                    help="oracle time budget for each other forward / decode workload")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input/output buffer sets cycled through (0: 3 for workloads whose bytes fit the "
+                         "256 MB on-die cache, else 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of attention, time a plain device-to-device copy of this many bytes "
@@ -391,7 +449,8 @@ def main() -> int:
                                        "frac": r["frac"], "traffic": None, "kernel": "decode_bf16"}}), flush=True)
         return 0
     w = configs.BY_NAME[args.workload]
-    ms, inp, first = time_workload(w, args.steps, args.warmup, 1, torch, attn, keep_first_output=True)
+    rot = args.rotate if args.rotate > 0 else default_rotation(w)
+    ms, inp, first = time_workload(w, args.steps, args.warmup, rot, torch, attn, keep_first_output=True)
     r = rate(w, ms)
     kern = kernel_of(w)
     traffic = measured_traffic(kern, w.name)
@@ -410,12 +469,15 @@ def main() -> int:
         "data": "synthetic (seeded generator, workloads/gen.py)",
         "config": {"workload": w.name, "N": w.N, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.L, "S": w.S, "E": w.E,
                    "mode": w.mode, "causal": w.causal, "window": w.window, "n_reg": w.n_reg, "sink": w.sink,
-                   "decode": w.decode, "parallelism": "single GPU"},
+                   "decode": w.decode, "parallelism": "single GPU", "rotated_buffer_sets": rot},
         "roofline": {"bound": r["bound"], "achieved": r["value"], "peak": r["peak"], "unit": r["unit"],
                      "frac": r["frac"], "traffic": traffic, "kernel": kern,
                      "algorithmic_per_launch": configs.algorithmic_bytes(w) if w.decode
                      else configs.algorithmic_flops(w)},
     }
+    mf = measured_mfma_busy(kern, w.name)
+    if mf is not None:
+        result["roofline"]["mfma_busy_counter"] = mf
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: timing the oracle on a row sample")
         base, parity = cpu_baseline(w, inp, first[0], first[1], args.cpu_seconds)
@@ -427,28 +489,39 @@ def main() -> int:
         for x in configs.ALL + configs.EXTRA:
             if x.name == w.name:
                 continue
-            rot = 3 if (not x.decode and configs.algorithmic_bytes(x) < 256e6 and x.name == configs.C4.name) else 1
-            xms, xinp, _ = time_workload(x, max(5, args.steps // 2), max(2, args.warmup // 2), rot, torch, attn)
-            del xinp
-            torch.cuda.empty_cache()
+            rot = default_rotation(x)
+            xms, xinp, xfirst = time_workload(x, args.steps, args.warmup, rot, torch, attn,
+                                              keep_first_output=not args.no_cpu_baseline)
             xr = rate(x, xms)
             xr["ms"] = xms
             xr["ms_spread"] = SPREAD.get(x.name)
             xr["kernel"] = kernel_of(x)
             xr["rotated_buffer_sets"] = rot
+            xt = measured_traffic(kernel_of(x), x.name)
+            if xt is not None:
+                xr["traffic"] = xt
+            xm = measured_mfma_busy(kernel_of(x), x.name)
+            if xm is not None:
+                xr["mfma_busy_counter"] = xm
+            if not args.no_cpu_baseline:
+                log(f"[bench] {x.name}: oracle on a row sample")
+                xr["cpu_baseline"], xr["parity"] = cpu_baseline(x, xinp, xfirst[0], xfirst[1],
+                                                                args.cpu_seconds_extra)
+            del xinp, xfirst
+            torch.cuda.empty_cache()
             extras[x.name] = xr
         for bw in configs.BACKWARD:
-            xms = time_backward(bw, max(5, args.steps // 4), max(2, args.warmup // 4), torch, attn)
+            xms = time_backward(bw, args.steps, args.warmup, torch, attn)
             torch.cuda.empty_cache()
             tf = configs.backward_flops(bw) / (xms * 1e-3) / 1e12
             extras[bw.name + "__backward"] = {
                 "value": tf, "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_BF16_TFLOPS,
                 "frac": tf / PEAK_BF16_TFLOPS, "ms": xms, "ms_spread": SPREAD.get(bw.name + "__backward"),
-                "kernel": "bwd_pre + bwd_dq + bwd_dkdv",
+                "kernel": "bwd_dq + bwd_dkdv",
                 "hbm_GBps": configs.backward_bytes(bw) / (xms * 1e-3) / 1e9,
                 "algorithmic_per_step": configs.backward_flops(bw)}
         for sk in configs.SOCKET_BY_NAME.values():
-            xms = time_socket(sk, max(5, args.steps // 4), max(2, args.warmup // 4), torch, attn)
+            xms = time_socket(sk, args.steps, args.warmup, torch, attn)
             torch.cuda.empty_cache()
             gbs = configs.socket_bytes(sk) / (xms * 1e-3) / 1e9
             dense = extras.get(sk.base.name, {}).get("ms")
@@ -457,7 +530,7 @@ def main() -> int:
                                "kernel": "socket_prob + socket_score + socket_select + decode (indexed)",
                                "speedup_vs_dense_decode": (dense / xms) if dense else None}
         for sw in configs.STREAM_BY_NAME.values():
-            xms = time_stream(sw, max(5, args.steps // 2), max(2, args.warmup // 2), 3, torch, attn)
+            xms = time_stream(sw, args.steps, args.warmup, 3, torch, attn)
             torch.cuda.empty_cache()
             xr = stream_rate(sw, xms)
             xr["ms"] = xms
@@ -466,6 +539,12 @@ def main() -> int:
             xr["rotated_buffer_sets"] = 3
             extras[sw.name] = xr
         result["extras"] = extras
+        dec = extras.get(configs.C5.name)
+        if dec is not None:
+            # the metric's second half: long-context split-K decode against the HBM roofline
+            result["decode"] = {"workload": configs.C5.name, "value": dec["value"], "unit": dec["unit"],
+                                "peak": dec["peak"], "frac": dec["frac"], "ms": dec["ms"],
+                                "parity_pass": dec.get("parity", {}).get("pass")}
     print(json.dumps(result), flush=True)
     return 0
 

@@ -98,6 +98,13 @@ attn_impl::FwdArgs make_args(int N, int Hq, int Hkv, int L, int S, int E, const 
   return a;
 }
 
+// bf16 forward kernel choice: narrow causal windows at E = 64 take the key-band
+// kernel, everything else the tiled kernel.
+hipError_t launch_bf16_forward(const attn_impl::FwdArgs& a, hipStream_t st) {
+  if (attn_impl::prefill_band_fits(a)) return attn_impl::launch_prefill_bf16_band(a, st);
+  return attn_impl::launch_prefill_bf16(a, st);
+}
+
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -178,7 +185,7 @@ int attn_fwd(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, const v
   const attn_impl::FwdArgs a =
       make_args(N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o, lse);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const hipError_t e = dt == ATTN_BF16 ? attn_impl::launch_prefill_bf16(a, st) : attn_impl::launch_prefill_f32(a, st);
+  const hipError_t e = dt == ATTN_BF16 ? launch_bf16_forward(a, st) : attn_impl::launch_prefill_f32(a, st);
   return hip_status(e, "attn_fwd launch");
 }
 
@@ -216,7 +223,7 @@ int attn_fwd_biased(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, 
     a.bias_sh = bias_stride_h;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const hipError_t e = dt == ATTN_BF16 ? attn_impl::launch_prefill_bf16(a, st) : attn_impl::launch_prefill_f32(a, st);
+  const hipError_t e = dt == ATTN_BF16 ? launch_bf16_forward(a, st) : attn_impl::launch_prefill_f32(a, st);
   return hip_status(e, "attn_fwd_biased launch");
 }
 

@@ -51,6 +51,10 @@ struct DecodeArgs {
 };
 
 hipError_t launch_prefill_bf16(const FwdArgs& a, hipStream_t stream);
+// Sliding-window variant: one key band in LDS per (kv head, query block), shared by
+// the GQA group; prefill_band_fits() tells whether a call is in its scope.
+bool prefill_band_fits(const FwdArgs& a);
+hipError_t launch_prefill_bf16_band(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 

@@ -104,10 +104,15 @@ __device__ __forceinline__ void map_block(int bid, const PrefillParams& p, int& 
 }
 
 // Softmax front end, fixed per launch:
-//   kDotPos: dot mode, scale > 0 -- max over raw scores, weight = exp2(fma(s, c, -m));
-//   kDotAny: dot mode, any finite scale -- x = c*s first;
-//   kRbf:    x = c*s + bias_k with bias_k = -gamma*log2(e)*|k|^2 from the staged tile.
-enum { kDotPos = 0, kDotAny = 1, kRbf = 2 };
+//   kDotPos:  dot mode, scale > 0 -- max over raw scores, weight = exp2(fma(s, c, -m));
+//   kDotAny:  dot mode, any finite scale -- x = c*s first;
+//   kRbf:     x = c*s + bias_k with bias_k = -gamma*log2(e)*|k|^2 from the staged tile;
+//   kRbfFold: RBF with gamma > 0 -- the key term goes into the matrix product instead:
+//             one more 16-wide K step whose A operand holds -|k|^2/2 split into three
+//             bf16 parts (hi + mid + lo, ~24 significant bits, summed exactly in the
+//             fp32 accumulator) against ones in Q^T, so s' = q.k - |k|^2/2 and the
+//             weights are formed as in kDotPos: exp2(fma(s', c, -m)), c = 2*gamma*log2(e).
+enum { kDotPos = 0, kDotAny = 1, kRbf = 2, kRbfFold = 3 };
 
 // User bias kinds (a compile-time parameter): none, float32 added to the
 // logits, uint8 mask (0 hides the pair).
@@ -119,14 +124,15 @@ enum { kBiasNone = 0, kBiasF32 = 1, kBiasBool = 2 };
 // bias it needs up to ~210 (2 waves).
 template <int E, int MODE, int UB>
 struct Occupancy {
-  static constexpr int kWaves = (E == 128 || UB != 0) ? 2 : (MODE == kRbf ? 3 : 4);
+  static constexpr int kWaves = (E == 128 || UB != 0) ? 2 : ((MODE == kRbf || MODE == kRbfFold) ? 3 : 4);
 };
 
 template <int E, int MODE, int UB>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Occupancy<E, MODE, UB>::kWaves, Occupancy<E, MODE, UB>::kWaves)))
 void prefill_bf16_kernel(PrefillParams p) {
-  constexpr bool RBF = MODE == kRbf;
-  constexpr bool FAST = MODE == kDotPos;
+  constexpr bool RBF = MODE == kRbf || MODE == kRbfFold;  // K staged through registers, |k|^2 on chip
+  constexpr bool FOLD = MODE == kRbfFold;
+  constexpr bool FAST = MODE == kDotPos || FOLD;
   static_assert(UB == kBiasNone || !FAST, "a user bias needs the logits formed before the max");
   constexpr int OSTR = E + 8;   // epilogue O row stride (elements)
   constexpr int QS = E / 16;    // MFMA steps over the head dimension
@@ -150,6 +156,7 @@ void prefill_bf16_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t sKV0[2 * TILEB];
   __shared__ __attribute__((aligned(16))) uint8_t sKV1[2 * TILEB];
   __shared__ __attribute__((aligned(16))) float sBias[2][BN];
+  __shared__ __attribute__((aligned(16))) u32x2 sKn[FOLD ? 2 : 1][FOLD ? BN : 1];  // kRbfFold: -|k|^2/2 as 3 bf16
   auto k_tile = [&](int buf) { return buf ? sKV1 : sKV0; };
   auto v_tile = [&](int buf) { return (buf ? sKV1 : sKV0) + TILEB; };
 
@@ -180,6 +187,9 @@ void prefill_bf16_kernel(PrefillParams p) {
     if (RBF) qn2 += sumsq8(c);
   }
   if (RBF) qn2 = pair32_sum(qn2);
+  // kRbfFold: Q^T fragment of the extra K step, ones in K-dims 0..2 (lanes g = 0).
+  const u32x4 qone_w = (FOLD && g == 0) ? u32x4{0x3f803f80u, 0x00003f80u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+  const bf16x8 qone = as_bf16x8(qone_w);
 
   // Running state in log2 units: m is the reference max, lsum this lane's share
   // of the row sum (its 16 keys per block); the halves are added at the end.
@@ -286,7 +296,21 @@ void prefill_bf16_kernel(PrefillParams p) {
         *reinterpret_cast<u32x4*>(k_tile(buf) + row * ROWB + ((c ^ tile_swz<E>(row)) * 16)) = kreg[i];
         // |k|^2 of this key row: its ECH chunks sit in ECH consecutive lanes.
         const float ss = group_sum<ECH>(sumsq8(kreg[i]));
-        if (c == 0) sBias[buf][row] = p.c_bias * ss;
+        if (FOLD) {
+          if (c == 0) {
+            // -|k|^2/2 = hi + mid + lo, each rounded to bf16 (nearest even) in turn
+            const float v0 = -0.5f * ss;
+            const __bf16 hi = (__bf16)v0;
+            const float v1 = v0 - (float)hi;
+            const __bf16 mid = (__bf16)v1;
+            const __bf16 lo = (__bf16)(v1 - (float)mid);
+            sKn[buf][row] = u32x2{(uint32_t)__builtin_bit_cast(uint16_t, hi) |
+                                      ((uint32_t)__builtin_bit_cast(uint16_t, mid) << 16),
+                                  (uint32_t)__builtin_bit_cast(uint16_t, lo)};
+          }
+        } else if (c == 0) {
+          sBias[buf][row] = p.c_bias * ss;
+        }
       }
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
@@ -379,6 +403,16 @@ void prefill_bf16_kernel(PrefillParams p) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) st[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[b], qf[s], st[b], 0, 0, 0);
     }
+    if (FOLD) {
+      // The extra K step: key row l32 of block b contributes its three parts of
+      // -|k|^2/2 in K-dims 0..2 (lanes g = 0), the query side ones there.
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const u32x2 kn = sKn[buf][32 * b + l32];
+        const u32x4 av = g == 0 ? u32x4{kn[0], kn[1], 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+        st[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), qone, st[b], 0, 0, 0);
+      }
+    }
     __builtin_amdgcn_s_setprio(0);
 
     // Accumulator row of register r in block b = key 32b + 8(r/4) + 4g + r%4 of
@@ -390,7 +424,7 @@ void prefill_bf16_kernel(PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float x = st[b][r] * p.c_logit;
-          if (RBF) x += sBias[buf][32 * b + 8 * (r >> 2) + 4 * g + (r & 3)];
+          if (RBF && !FOLD) x += sBias[buf][32 * b + 8 * (r >> 2) + 4 * g + (r & 3)];
           if (UB != kBiasNone) x += ubv[b][r];
           st[b][r] = x;
         }
@@ -585,7 +619,7 @@ template <int E>
 hipError_t launch_e(const PrefillParams& p, bool rbf, int ub, hipStream_t stream) {
   if (ub == kBiasF32) return rbf ? launch_t<E, kRbf, kBiasF32>(p, stream) : launch_t<E, kDotAny, kBiasF32>(p, stream);
   if (ub == kBiasBool) return rbf ? launch_t<E, kRbf, kBiasBool>(p, stream) : launch_t<E, kDotAny, kBiasBool>(p, stream);
-  if (rbf) return launch_t<E, kRbf, kBiasNone>(p, stream);
+  if (rbf) return p.c_logit > 0.f ? launch_t<E, kRbfFold, kBiasNone>(p, stream) : launch_t<E, kRbf, kBiasNone>(p, stream);
   if (p.c_logit > 0.f) return launch_t<E, kDotPos, kBiasNone>(p, stream);
   return launch_t<E, kDotAny, kBiasNone>(p, stream);
 }

@@ -238,9 +238,193 @@ void prefill_f32_kernel(PrefillF32Params p) {
   }
 }
 
+// Small problems (a few row tiles, e.g. one head of 256 rows) leave the tiled
+// kernel above on a handful of CUs, where each lane walks its row's keys one
+// after another.  This kernel spreads them instead: one workgroup (256 threads)
+// per query row.  The row's visible keys (registers, then the real keys of its
+// causal / window interval: a contiguous run) are taken in chunks of 256, one key
+// per thread: every thread loads its key row and forms its logit, so all the
+// loads of a chunk are in flight together; the chunk's max and sum are reduced
+// across the workgroup (shuffles, then LDS) and fold into the running state,
+// the weights go to LDS, and the threads then take (4 output dims, every KG-th
+// key of the chunk) for the weighted value sum, requesting all their value rows
+// before using any.  The KG partial outputs are summed through LDS at the end.
+// Same logit frame, sink, bias and LSE conventions as the tiled kernel.
+constexpr int RT = 256;   // threads per workgroup = keys per chunk
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int s = 32; s > 0; s >>= 1) v = fmaxf(v, __shfl_xor(v, s, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int s = 32; s > 0; s >>= 1) v += __shfl_xor(v, s, 64);
+  return v;
+}
+
+template <int E, bool RBF>
+__global__ __launch_bounds__(RT) void prefill_f32_rows_kernel(PrefillF32Params p) {
+  constexpr int NQ = E / 4;        // float4 quads of a row
+  constexpr int KG = RT / NQ;      // key groups in the value sum (16 at E = 64, 8 at E = 128)
+  constexpr int PER = RT / KG;     // value rows per thread per chunk (16 or 32)
+  __shared__ float sP[RT];
+  __shared__ float sRed[2][4];
+  __shared__ __attribute__((aligned(16))) f32x4 sAcc[KG][NQ];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const long long row = blockIdx.x;  // flat (n, h, i)
+  const int i = (int)(row % p.L);
+  const int nh = (int)(row / p.L);
+  const int h = nh % p.Hq, n = nh / p.Hq;
+  const int kh = h / (p.Hq / p.Hkv);
+
+  // The query row, whole in every thread (one address for all: broadcast loads).
+  const float* qrow = p.q + (size_t)row * E;
+  float q[E];
+  float qn2 = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; e += 4) {
+    const f32x4 c = *reinterpret_cast<const f32x4*>(qrow + e);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      q[e + u] = c[u];
+      qn2 = __builtin_fmaf(c[u], c[u], qn2);
+    }
+  }
+
+  // Visible keys: registers [0, n_reg), then real keys [lo, hi] (virtual index v -> row).
+  const int kl = p.key_len ? max(0, min(p.S_real, p.key_len[n])) : p.S_real;
+  const int ip = i + p.off;
+  const int hi = p.causal ? min(kl - 1, ip) : kl - 1;
+  const int lo = p.window > 0 ? max(0, ip - p.window + 1) : 0;
+  const int cnt = p.n_reg + max(0, hi - lo + 1);
+  auto key_of = [&](int v) { return v < p.n_reg ? v : p.n_reg + lo + (v - p.n_reg); };
+  const size_t kvoff = ((size_t)n * p.Hkv + kh) * (size_t)p.S * E;
+  const long long ub_row = (long long)n * p.ub_sn + (long long)h * p.ub_sh + (long long)i * p.S;
+
+  float m = kNegInf, l = 0.f;
+  if (p.sink) {
+    float s0 = p.sink[h];
+    if (RBF) s0 += p.gamma * qn2;
+    m = s0 * kLog2e;
+    l = 1.f;
+  }
+  const int quad = tid % NQ, grp = tid / NQ;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = 0; c0 < cnt; c0 += RT) {
+    // this thread's key: its logit (keys past the list take the list's first key,
+    // so that every thread loads, and are masked)
+    const int v = c0 + tid;
+    const bool ok = v < cnt;
+    float x;
+    {
+      const int j = key_of(ok ? v : 0);
+      const float* krow = p.k + kvoff + (size_t)j * E;
+      float d4[4] = {0.f, 0.f, 0.f, 0.f};
+      float k2 = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; e += 4) {
+        const f32x4 kc = *reinterpret_cast<const f32x4*>(krow + e);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          d4[u] = __builtin_fmaf(q[e + u], kc[u], d4[u]);
+          if (RBF) k2 = __builtin_fmaf(kc[u], kc[u], k2);
+        }
+      }
+      x = ((d4[0] + d4[1]) + (d4[2] + d4[3])) * p.c_logit;
+      if (RBF) x = __builtin_fmaf(p.c_bias, k2, x);
+      if (p.ubias) {  // user bias: natural-log addend, or a mask where 0 hides the pair
+        if (p.ub_kind == 1) {
+          const float b = static_cast<const float*>(p.ubias)[ub_row + j];
+          x = (b == kNegInf) ? kNegInf : __builtin_fmaf(b, kLog2e, x);
+        } else if (!static_cast<const uint8_t*>(p.ubias)[ub_row + j]) {
+          x = kNegInf;
+        }
+      }
+      if (!ok) x = kNegInf;
+    }
+    // chunk max across the workgroup
+    float cm = wave_max(x);
+    if (lane == 0) sRed[0][wave] = cm;
+    __syncthreads();
+    cm = fmaxf(fmaxf(sRed[0][0], sRed[0][1]), fmaxf(sRed[0][2], sRed[0][3]));
+    const float m_new = fmaxf(m, cm);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = exp2f(m - m_use);
+    const float pv = exp2f(x - m_use);
+    sP[tid] = pv;
+    const float ws = wave_sum(pv);
+    if (lane == 0) sRed[1][wave] = ws;
+    __syncthreads();  // weights and partial sums visible
+    l = __builtin_fmaf(l, alpha, (sRed[1][0] + sRed[1][1]) + (sRed[1][2] + sRed[1][3]));
+    m = m_new;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] *= alpha;
+    // value rows: keys grp, grp + KG, ... of the chunk, all requested first
+    const int n_here = min(RT, cnt - c0);
+    f32x4 vr[PER];
+    float pw[PER];
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {
+      const int vi = grp + t * KG;
+      const bool okv = vi < n_here;
+      pw[t] = okv ? sP[vi] : 0.f;
+      vr[t] = *reinterpret_cast<const f32x4*>(p.v + kvoff + (size_t)key_of(c0 + (okv ? vi : 0)) * E + 4 * quad);
+    }
+    f32x4 a2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < PER; ++t)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (t & 1)
+          a2[u] = __builtin_fmaf(pw[t], vr[t][u], a2[u]);
+        else
+          acc[u] = __builtin_fmaf(pw[t], vr[t][u], acc[u]);
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] += a2[u];
+    __syncthreads();  // every thread is done with sP and sRed before the next chunk
+  }
+  // Sum the key groups' partial outputs through LDS.
+  sAcc[grp][quad] = acc;
+  __syncthreads();
+  if (tid < NQ) {
+    f32x4 o = sAcc[0][tid];
+#pragma unroll
+    for (int gi = 1; gi < KG; ++gi)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o[u] += sAcc[gi][tid][u];
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] *= inv;
+    *reinterpret_cast<f32x4*>(p.o + (size_t)row * E + 4 * tid) = o;
+  }
+  if (tid == 0) {
+    float lv = kNegInf;
+    if (l > 0.f) {
+      lv = (m + log2f(l)) * kLn2;
+      if (RBF) lv -= p.gamma * qn2;
+    }
+    p.lse[row] = lv;
+  }
+}
+
+template <int E, bool RBF>
+hipError_t launch_rows_t(const PrefillF32Params& p, hipStream_t stream) {
+  const long long rows = (long long)p.N * p.Hq * p.L;
+  hipLaunchKernelGGL((prefill_f32_rows_kernel<E, RBF>), dim3((unsigned)rows), dim3(RT), 0, stream, p);
+  return hipGetLastError();
+}
+
+// Below this many row tiles the tiled kernel would leave most of the chip idle.
+constexpr long long kRowsKernelTiles = 64;
+
 template <int E, bool RBF>
 hipError_t launch_t(const PrefillF32Params& p, hipStream_t stream) {
   const long long blocks = (long long)p.num_q_tiles * p.N * p.Hq;
+  if (blocks < kRowsKernelTiles) return launch_rows_t<E, RBF>(p, stream);
   hipLaunchKernelGGL((prefill_f32_kernel<E, RBF>), dim3((unsigned)blocks), dim3(BQ * F32Waves<E>::W), 0, stream, p);
   return hipGetLastError();
 }

@@ -41,6 +41,9 @@ CASES = [
     (W("f32_f32bias_keylen", dtype="f32", L=100, S_real=120, E=64, n_reg=3, sink=True), "f32", "N", "H", True, 0.1),
     (W("f32_boolmask_rbf_e128", dtype="f32", N=1, L=90, S_real=90, E=128, mode="rbf", window=30), "bool", "1",
      "1", False, 0.6),
+    # 80 row tiles: the tiled fp32 kernel with a bias and key lengths
+    (W("f32_tiled_f32bias_keylen_gqa", dtype="f32", N=2, Hq=8, Hkv=4, L=257, S_real=300, E=64, sink=True), "f32",
+     "N", "H", True, 0.05),
 ]
 
 

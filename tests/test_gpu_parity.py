@@ -56,6 +56,26 @@ PREFILL_CASES = [
       n_reg=5, window=60, sink=True, gamma=0.05, k_dist="dir_lognormal"),
     W("f32_rbf_e128_noncausal_ragged", dtype="f32", N=2, L=70, S_real=333, E=128, mode="rbf", causal=False,
       gamma=0.02),
+    # narrow causal windows at E = 64 (dot) with GQA groups of 4 or 8 heads take the
+    # key-band kernel: L above and below S, ragged row counts and workgroups with
+    # fewer than four query blocks, a one-key window with a negative scale, kv heads
+    # spread over the XCDs (N * Hkv = 8) or not; groups of 1 and 2 heads stay on the
+    # tiled kernel
+    W("band_gqa4_L_lt_S_window128_sink", Hq=8, Hkv=2, L=300, S_real=777, window=128, sink=True),
+    W("band_gqa8_L_gt_S_window100", N=2, Hq=16, Hkv=2, L=270, S_real=200, window=100),
+    W("band_gqa4_window1_negative_scale", Hq=4, Hkv=1, L=150, S_real=150, window=1, scale=-0.1),
+    W("band_gqa4_xcd_window127_sink", N=2, Hq=16, Hkv=4, L=333, S_real=333, window=127, sink=True),
+    W("band_gqa8_window32_one_block", Hq=8, Hkv=1, L=31, S_real=64, window=32),
+    W("band_gqa8_xcd_window128_sink", Hq=64, Hkv=8, L=700, S_real=700, window=128, sink=True),
+    W("tiled_gqa2_window64", Hq=4, Hkv=2, L=300, S_real=300, window=64, sink=True),
+    # fp32 problems of 64 row tiles and more go to the tiled kernel (smaller ones to the
+    # one-wave-per-row kernel, which every fp32 case above takes)
+    W("f32_tiled_dot_causal_gqa_sink_e128", dtype="f32", N=2, Hq=8, Hkv=2, L=300, S_real=300, E=128, sink=True),
+    W("f32_tiled_rbf_registers_window_e64", dtype="f32", Hq=16, Hkv=4, L=260, S_real=270, mode="rbf", n_reg=3,
+      window=90, gamma=0.05, k_dist="dir_lognormal"),
+    # one-wave-per-row kernel: rows longer than its 256-key chunk, a sink and registers
+    W("f32_rows_long_noncausal_registers_sink", dtype="f32", Hq=2, Hkv=1, L=40, S_real=1300, n_reg=2,
+      causal=False, sink=True),
 ]
 
 # Wider shapes (hundreds of workgroups, more heads than the small cases) with
