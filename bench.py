@@ -24,6 +24,9 @@ against it ("cpu_baseline" and "parity" of the line and of each extra).  Every
 workload is warmed up for at least 200 ms before its K timed calls, so that no
 timing falls in the clock ramp of the first calls.  The long-context decode
 figure is repeated at top level under "decode" (the metric's second half).
+"probe_peaks" holds what this GPU sustains on a bf16 GEMM and a device copy
+(vendor library work), and each roofline entry gives its fraction of the probe
+peak of its bound beside the fraction of the published one.
 
 Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits with a
 message.
@@ -74,9 +77,18 @@ def kernel_of(w) -> str:
     return "prefill_bf16_band" if band else "prefill_bf16"
 
 
+# Headers every kernel source includes: a change there changes the kernels too.
+KERNEL_HEADERS = ("softmax_attention_attn_amd/csrc/device_common.h", "softmax_attention_attn_amd/csrc/tile_common.h",
+                  "softmax_attention_attn_amd/csrc/kernels.h", "include/attn.h")
+
+
 def source_sha(kernel: str) -> str:
-    with open(os.path.join(ROOT, KERNEL_FILES[kernel]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 (first 16 hex digits) of a kernel source followed by the shared headers."""
+    h = hashlib.sha256()
+    for path in (KERNEL_FILES[kernel],) + KERNEL_HEADERS:
+        with open(os.path.join(ROOT, path), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -166,6 +178,56 @@ def warm(call, warmup: int, torch):
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     return i
+
+
+def probe_peaks(torch):
+    """What this GPU sustains on plain library work, beside the published peaks:
+    a bf16 GEMM 8192 x 8192 x 8192 (torch.matmul, i.e. the vendor BLAS) in
+    TFLOP/s, and a 1 GiB device-to-device copy in GB/s (bytes read + written).
+    Each is warmed up for WARM_MS, then timed over back-to-back calls."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+
+    def rate_of(call, calls):
+        warm(lambda _i: call(), 3, torch)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(calls):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / calls
+
+    n = 8192
+    x = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    y = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    z = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    ms = rate_of(lambda: torch.matmul(x, y, out=z), 20)
+    out["bf16_gemm"] = {"value": 2.0 * n ** 3 / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+                        "what": "torch.matmul bf16 8192x8192x8192", "ms": ms}
+    del x, y, z
+    nb = 1 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    ms = rate_of(lambda: dst.copy_(src), 20)
+    out["hbm_copy"] = {"value": 2.0 * nb / (ms * 1e-3) / 1e9, "unit": "GB/s",
+                       "what": "1 GiB device copy, read + write bytes", "ms": ms}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def attach_probe(entry: dict, probes) -> None:
+    """Adds the probe peak of the entry's bound and the fraction of it reached."""
+    if not probes:
+        return
+    p = {"mfma": probes.get("bf16_gemm"), "hbm": probes.get("hbm_copy")}.get(entry.get("bound"))
+    if p is None or p["unit"] != entry.get("unit"):
+        return
+    entry["probe_peak"] = p["value"]
+    entry["frac_of_probe"] = entry["achieved" if "achieved" in entry else "value"] / p["value"]
 
 
 def time_workload(w, steps: int, warmup: int, rotate: int, torch, attn, keep_first_output=False):
@@ -372,6 +434,8 @@ def main() -> int:
                     help="input/output buffer sets cycled through (0: 3 for workloads whose bytes fit the "
                          "256 MB on-die cache, else 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the probe-measured peaks (bf16 GEMM and device copy)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of attention, time a plain device-to-device copy of this many bytes "
                          "(the reference kernel for calibrating HBM byte counters)")
@@ -478,6 +542,12 @@ def main() -> int:
     mf = measured_mfma_busy(kern, w.name)
     if mf is not None:
         result["roofline"]["mfma_busy_counter"] = mf
+    probes = None
+    if not args.no_probe:
+        log("[bench] probe peaks: bf16 GEMM and device copy")
+        probes = probe_peaks(torch)
+        result["probe_peaks"] = probes
+        attach_probe(result["roofline"], probes)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: timing the oracle on a row sample")
         base, parity = cpu_baseline(w, inp, first[0], first[1], args.cpu_seconds)
@@ -503,6 +573,7 @@ def main() -> int:
             xm = measured_mfma_busy(kernel_of(x), x.name)
             if xm is not None:
                 xr["mfma_busy_counter"] = xm
+            attach_probe(xr, probes)
             if not args.no_cpu_baseline:
                 log(f"[bench] {x.name}: oracle on a row sample")
                 xr["cpu_baseline"], xr["parity"] = cpu_baseline(x, xinp, xfirst[0], xfirst[1],
@@ -520,6 +591,7 @@ def main() -> int:
                 "kernel": "bwd_dq + bwd_dkdv",
                 "hbm_GBps": configs.backward_bytes(bw) / (xms * 1e-3) / 1e9,
                 "algorithmic_per_step": configs.backward_flops(bw)}
+            attach_probe(extras[bw.name + "__backward"], probes)
         for sk in configs.SOCKET_BY_NAME.values():
             xms = time_socket(sk, args.steps, args.warmup, torch, attn)
             torch.cuda.empty_cache()
@@ -529,6 +601,7 @@ def main() -> int:
                                "frac": gbs / PEAK_HBM_GBS, "ms": xms, "ms_spread": SPREAD.get(sk.name),
                                "kernel": "socket_prob + socket_score + socket_select + decode (indexed)",
                                "speedup_vs_dense_decode": (dense / xms) if dense else None}
+            attach_probe(extras[sk.name], probes)
         for sw in configs.STREAM_BY_NAME.values():
             xms = time_stream(sw, args.steps, args.warmup, 3, torch, attn)
             torch.cuda.empty_cache()
@@ -537,6 +610,7 @@ def main() -> int:
             xr["ms_spread"] = SPREAD.get(sw.name)
             xr["kernel"] = "stream_append + decode_bf16"
             xr["rotated_buffer_sets"] = 3
+            attach_probe(xr, probes)
             extras[sw.name] = xr
         result["extras"] = extras
         dec = extras.get(configs.C5.name)
@@ -544,6 +618,7 @@ def main() -> int:
             # the metric's second half: long-context split-K decode against the HBM roofline
             result["decode"] = {"workload": configs.C5.name, "value": dec["value"], "unit": dec["unit"],
                                 "peak": dec["peak"], "frac": dec["frac"], "ms": dec["ms"],
+                                "probe_peak": dec.get("probe_peak"), "frac_of_probe": dec.get("frac_of_probe"),
                                 "parity_pass": dec.get("parity", {}).get("pass")}
     print(json.dumps(result), flush=True)
     return 0

@@ -22,14 +22,16 @@ constexpr float kNegInf = -__builtin_huge_valf();
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Sum of squares of the 8 bf16 values in a 16-byte chunk, in fp32 (products are exact).
+// Sum of squares of the 8 bf16 values in a 16-byte chunk, in fp32 (products are
+// exact): v_dot2_f32_bf16 of each packed pair with itself, two squares per instruction.
 __device__ __forceinline__ float sumsq8(u32x4 c) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   float s = 0.f;
+  const uint32_t w[4] = {c[0], c[1], c[2], c[3]};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float a = bf16_lo(c[i]), b = bf16_hi(c[i]);
-    s = __builtin_fmaf(a, a, s);
-    s = __builtin_fmaf(b, b, s);
+    const bf16x2 x = __builtin_bit_cast(bf16x2, w[i]);
+    s = __builtin_amdgcn_fdot2_f32_bf16(x, x, s, false);
   }
   return s;
 }

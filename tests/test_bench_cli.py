@@ -36,3 +36,24 @@ def test_help_lists_every_workload():
                  "stream_sink4_win4092_bf16_8x32to8x128_pos100000", "socket_decode_sink_bf16_8x32to8x131072x128_k3972",
                  "rbf_causal_reg4_bf16_2x16x8192x64__backward"):
         assert name in r.stdout
+
+
+def test_probe_fraction_follows_the_entry_bound():
+    sys.path.insert(0, ROOT)
+    import bench
+    probes = {"bf16_gemm": {"value": 2000.0, "unit": "TFLOP/s"}, "hbm_copy": {"value": 5000.0, "unit": "GB/s"}}
+    mfma = {"bound": "mfma", "unit": "TFLOP/s", "achieved": 500.0, "value": 1.0}
+    bench.attach_probe(mfma, probes)
+    assert mfma["probe_peak"] == 2000.0 and abs(mfma["frac_of_probe"] - 0.25) < 1e-12
+    hbm = {"bound": "hbm", "unit": "GB/s", "value": 4000.0}
+    bench.attach_probe(hbm, probes)
+    assert abs(hbm["frac_of_probe"] - 0.8) < 1e-12
+    alu = {"bound": "alu", "unit": "TFLOP/s", "value": 1.0}
+    bench.attach_probe(alu, probes)
+    assert "probe_peak" not in alu
+    mixed = {"bound": "hbm", "unit": "TFLOP/s", "value": 1.0}
+    bench.attach_probe(mixed, probes)
+    assert "probe_peak" not in mixed
+    none = {"bound": "mfma", "unit": "TFLOP/s", "value": 1.0}
+    bench.attach_probe(none, None)
+    assert "probe_peak" not in none
