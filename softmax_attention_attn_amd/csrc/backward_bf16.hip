@@ -164,7 +164,8 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[EB], float mul, c
     const int id = lane + 64 * it;
     const int rloc = id / ECH, c = id % ECH;
     if (row0 + rloc < nrows)
-      *reinterpret_cast<u32x4*>(dst + (size_t)rloc * E + 8 * c) = *reinterpret_cast<const u32x4*>(&sO[rloc * OSTR + 8 * c]);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&sO[rloc * OSTR + 8 * c]),
+                                  reinterpret_cast<u32x4*>(dst + (size_t)rloc * E + 8 * c));  // written once
   }
 }
 

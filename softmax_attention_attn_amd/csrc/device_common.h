@@ -103,6 +103,21 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
 }
 
+// Stores through a buffer resource: a byte offset at or past the resource's
+// size writes nothing (the hardware's range check), so a store of a row that may
+// lie past the end of a tensor needs no branch around it.
+__device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)byte_off, 0, 0);
+}
+// The same with the non-temporal hint (cache policy bit 1), for outputs written
+// once and not read back by the kernel.
+__device__ __forceinline__ void buffer_store16_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)byte_off, 0, 2);
+}
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)byte_off, 0, 0);
+}
+
 // Two bf16 halves (low halves when hi == false, else high halves) of a and b
 // packed as {a_half, b_half} (v_perm_b32).
 __device__ __forceinline__ uint32_t pack_halves(uint32_t a, uint32_t b, bool hi) {

@@ -603,7 +603,7 @@ void prefill_bf16_kernel(PrefillParams p) {
     const int row = qa + rloc;
     if (row < p.L) {
       const u32x4 val = *reinterpret_cast<const u32x4*>(&sO[rloc * OSTR + 8 * c]);
-      *reinterpret_cast<u32x4*>(p.o + (obase + row) * E + 8 * c) = val;
+      __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(p.o + (obase + row) * E + 8 * c));  // written once
     }
   }
 }

@@ -6,11 +6,13 @@
 // sees at most W + 31 keys, the same band for all Hq/Hkv query heads that share
 // a key/value head ("SDPA란 무엇인가?" section 5).  A workgroup takes one kv head
 // and a run of QPW consecutive 32-position query blocks; its four waves split the
-// group's query heads.  The keys live in a ring of 32-row blocks in LDS (K and V,
-// LDS-direct buffer loads, rows past the slice end read as zeros): the first
-// block's band is loaded once, and while the waves compute block b the 32 keys
-// block b+1 adds and its Q rows are already on their way (one barrier per
-// block), so HBM latency is exposed once per workgroup.  Per (head, block) a wave
+// group's query heads.  The keys live in LDS as 32-row blocks of K and V
+// (LDS-direct buffer loads, rows past the slice end read as zeros): the first
+// query block's band in one pair of arrays, and the one block the second query
+// block adds in another pair, loaded while the waves compute the first (its Q
+// rows too, one (head, block) pair ahead), so HBM latency is exposed once per
+// workgroup.  The reads of the first block's compute never touch the array the
+// loads in flight write, which lets them go without waiting for those loads.  Per (head, block) a wave
 // forms S^T = K * Q^T for every 32-key block of its part of the band
 // (v_mfma_f32_32x32x16_bf16, one query per lane as in prefill_bf16.hip), so the
 // whole row of logits is in registers: one max (with the sink logit of
@@ -21,6 +23,8 @@
 //
 // Scope (the caller checks it): bf16, dot logits, causal, 0 < W <= 128, E = 64,
 // Hq/Hkv = 4 or 8, no register tokens, no key lengths, no user bias.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "tile_common.h"
@@ -35,8 +39,7 @@ constexpr int QB = 32;              // query positions per block (one MFMA colum
 constexpr int KB = 32;              // keys per key block
 constexpr int WMAX = 128;           // longest window this kernel takes
 constexpr int NKB = (WMAX + QB - 1 + KB - 1) / KB + 1;  // key blocks one query block can touch: 6
-constexpr int NRING = NKB + 1;      // ring slots: the blocks in use plus the one being loaded
-constexpr int QPW = 2;              // query blocks per workgroup
+constexpr int QPW = 2;              // query blocks per workgroup (the layout below is for two)
 constexpr int ROWB = E * 2;
 constexpr int BLKB = KB * ROWB;     // bytes of one 32-row block of K (or V)
 constexpr int ECH = E / 8;
@@ -59,8 +62,10 @@ struct BandParams {
 template <int PPW, bool FAST>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_band_kernel(BandParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t sK[NRING * BLKB];
-  __shared__ __attribute__((aligned(16))) uint8_t sV[NRING * BLKB];
+  __shared__ __attribute__((aligned(16))) uint8_t sK[NKB * BLKB];   // band of the first query block
+  __shared__ __attribute__((aligned(16))) uint8_t sV[NKB * BLKB];
+  __shared__ __attribute__((aligned(16))) uint8_t sKn[BLKB];        // the block the second one adds
+  __shared__ __attribute__((aligned(16))) uint8_t sVn[BLKB];
   __shared__ __attribute__((aligned(16))) uint16_t sO[4][QB * OSTR];
 
   const int tid = threadIdx.x;
@@ -89,15 +94,14 @@ void prefill_band_kernel(BandParams p) {
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + kvoff, (uint32_t)p.S * ROWB);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + kvoff, (uint32_t)p.S * ROWB);
 
-  // Key block kb (keys 32 kb ..) lives in ring slot kb % NRING.  Each wave moves
-  // 8 of its 32 rows per tensor: lane l takes row 8 wave + l/8, logical chunk
-  // (l % 8) ^ swz(row), landing at physical chunk l % 8 (conflict-free reads).
-  auto load_block = [&](int kb) __attribute__((always_inline)) {
-    const int slot = kb % NRING;
+  // Key block kb (keys 32 kb ..) into the 32-row LDS blocks dk, dv.  Each wave
+  // moves 8 of the 32 rows per tensor: lane l takes row 8 wave + l/8, logical
+  // chunk (l % 8) ^ swz(row), landing at physical chunk l % 8 (conflict-free reads).
+  auto load_block = [&](int kb, uint8_t* dk, uint8_t* dv) __attribute__((always_inline)) {
     const int row = 8 * wave + lane / ECH;
     const uint32_t soff = (uint32_t)((kb * KB + row) * ROWB + (((lane % ECH) ^ tile_swz<E>(row)) * 16));
-    buffer_load16_to_lds(krs, sK + slot * BLKB + 8 * wave * ROWB, soff);
-    buffer_load16_to_lds(vrs, sV + slot * BLKB + 8 * wave * ROWB, soff);
+    buffer_load16_to_lds(krs, dk + 8 * wave * ROWB, soff);
+    buffer_load16_to_lds(vrs, dv + 8 * wave * ROWB, soff);
   };
   // Keys query block qb sees: real positions [lo_b, hi_b]; blocks lo_b/32 .. hi_b/32.
   auto key_range = [&](int qb, int& lo_b, int& hi_b) __attribute__((always_inline)) {
@@ -134,28 +138,40 @@ void prefill_band_kernel(BandParams p) {
   }
 
   // One (query head h, query block at row qa) on this wave: all its logits, one
-  // softmax, PV, and the stores.
-  auto compute_pair = [&](int h, int qa, int lo_b, int hi_b, const bf16x8 (&qf)[4]) __attribute__((always_inline)) {
+  // softmax, PV, and the stores.  Key block kb sits in slot kb - kb0 of sK/sV
+  // when that is below n0, else (second query block only) in sKn/sVn.
+  auto compute_pair = [&](auto second, int h, int qa, int lo_b, int hi_b, const bf16x8 (&qf)[4], float sink2,
+                          int kb0, int n0) __attribute__((always_inline)) {
+    constexpr bool SECOND = decltype(second)::value;
+    auto slot_k = [&](int kb) __attribute__((always_inline)) -> const uint8_t* {
+      if (!SECOND) return sK + (kb - kb0) * BLKB;
+      const int sl = kb - kb0;
+      return (sl >= 0 && sl < n0) ? sK + sl * BLKB : sKn;
+    };
+    auto slot_v = [&](int kb) __attribute__((always_inline)) -> const uint8_t* {
+      if (!SECOND) return sV + (kb - kb0) * BLKB;
+      const int sl = kb - kb0;
+      return (sl >= 0 && sl < n0) ? sV + sl * BLKB : sVn;
+    };
     const int qi = qa + l32;
-    const bool qvalid = qi < p.L;
     const int qlast = min(qa + QB - 1, p.L - 1);
     const int kb_lo = lo_b / KB;
     const int nj = hi_b >= lo_b ? min(NKB, hi_b / KB - kb_lo + 1) : 0;
     const int ip = qi + p.off;
     const int lo = ip - p.window + 1, hi = min(ip, p.S - 1);
 
+    // Blocks j >= nj are never read (every later loop stops at nj).
     f32x16 st[NKB];
 #pragma unroll
     for (int j = 0; j < NKB; ++j) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[j][r] = 0.f;
       if (j < nj) {
-        const uint8_t* kt = sK + ((kb_lo + j) % NRING) * BLKB;
+        const uint8_t* kt = slot_k(kb_lo + j);
+        const f32x16 zero = {};
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + krd[s]);
-          st[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st[j], 0, 0, 0);
+          st[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? zero : st[j], 0, 0, 0);
         }
         __builtin_amdgcn_s_setprio(0);
       }
@@ -178,13 +194,33 @@ void prefill_band_kernel(BandParams p) {
           // this lane's visible offsets within the block; the empty asm keeps the
           // comparisons here (hoisted, the 16 x NKB lane masks would not fit the
           // scalar registers)
+          // A block cut only by the window start (or only by the diagonal or
+          // the slice end) tests one bound.
           int lo_r = lo - base - 4 * g, hi_r = hi - base - 4 * g;
           asm volatile("" : "+v"(lo_r), "+v"(hi_r));
+          const bool cut_lo = base < qlast + p.off - p.window + 1;
+          const bool cut_hi = base + KB - 1 > qa + p.off;
+          if (cut_lo && cut_hi) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ko = 8 * (r >> 2) + (r & 3);
-            const float x = FAST ? st[j][r] : st[j][r] * p.c_logit;
-            st[j][r] = (ko >= lo_r && ko <= hi_r) ? x : kNegInf;
+            for (int r = 0; r < 16; ++r) {
+              const int ko = 8 * (r >> 2) + (r & 3);
+              const float x = FAST ? st[j][r] : st[j][r] * p.c_logit;
+              st[j][r] = (ko >= lo_r && ko <= hi_r) ? x : kNegInf;
+            }
+          } else if (cut_lo) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int ko = 8 * (r >> 2) + (r & 3);
+              const float x = FAST ? st[j][r] : st[j][r] * p.c_logit;
+              st[j][r] = ko >= lo_r ? x : kNegInf;
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int ko = 8 * (r >> 2) + (r & 3);
+              const float x = FAST ? st[j][r] : st[j][r] * p.c_logit;
+              st[j][r] = ko <= hi_r ? x : kNegInf;
+            }
           }
         }
 #pragma unroll
@@ -193,8 +229,6 @@ void prefill_band_kernel(BandParams p) {
     }
     mx = pair32_max(mx);
     if (FAST) mx = (mx == kNegInf) ? kNegInf : mx * p.c_logit;
-    float sink2 = kNegInf;
-    if (p.sink) sink2 = p.sink[h] * kLog2e;
     const float M = fmaxf(mx, sink2);
     const float Mu = (M == kNegInf) ? 0.f : M;
 
@@ -207,7 +241,7 @@ void prefill_band_kernel(BandParams p) {
 #pragma unroll
     for (int j = 0; j < NKB; ++j) {
       if (j < nj) {
-        const uint8_t* vt_s = sV + ((kb_lo + j) % NRING) * BLKB;
+        const uint8_t* vt_s = slot_v(kb_lo + j);
         float ps = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -235,7 +269,7 @@ void prefill_band_kernel(BandParams p) {
 
     // Epilogue: O = acc / l through this wave's LDS rows (whole-row stores), LSE.
     const float ltot = pair32_sum(lsum);
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    const float inv = ltot > 0.f ? __builtin_amdgcn_rcpf(ltot) : 0.f;
     uint16_t* so = sO[wave];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -245,8 +279,18 @@ void prefill_band_kernel(BandParams p) {
                                       acc[c][4 * rq + 3] * inv);
         *reinterpret_cast<bf16x4*>(&so[l32 * OSTR + 32 * c + 8 * rq + 4 * g]) = pk;
       }
+    // Stores go through resources over this head's L rows: rows at or past L
+    // are dropped by the range check, so no store sits behind a branch (a
+    // skipped store would make the wait for the next pair's Q rows, issued
+    // before these stores, wait for them as well).  Both halves of the wave
+    // write the same LSE value.  O goes out with the non-temporal hint: it is
+    // written once, and kept out of the caches it leaves them to the K/V bands
+    // that neighbouring workgroups read again (measured 14 % faster on the
+    // window-128 GQA shape).
     const size_t obase = ((size_t)n * p.Hq + h) * p.L;
-    if (g == 0 && qvalid) p.lse[obase + qi] = ltot > 0.f ? (M + log2f(ltot)) * kLn2 : kNegInf;
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(p.lse + obase, (uint32_t)p.L * 4u);
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(p.o + obase * E, (uint32_t)p.L * ROWB);
+    buffer_store4(lrs, (uint32_t)qi * 4u, ltot > 0.f ? (M + __builtin_amdgcn_logf(ltot)) * kLn2 : kNegInf);
     // the staging rows are this wave's own: wait for its LDS writes, then read them back
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     __builtin_amdgcn_wave_barrier();
@@ -254,56 +298,67 @@ void prefill_band_kernel(BandParams p) {
     for (int it = 0; it < (QB * ECH) / 64; ++it) {
       const int id = lane + 64 * it;
       const int rloc = id / ECH, c = id % ECH;
-      const int row = qa + rloc;
-      if (row < p.L) {
-        const u32x4 val = *reinterpret_cast<const u32x4*>(&so[rloc * OSTR + 8 * c]);
-        *reinterpret_cast<u32x4*>(p.o + (obase + row) * E + 8 * c) = val;
-      }
+      const u32x4 val = *reinterpret_cast<const u32x4*>(&so[rloc * OSTR + 8 * c]);
+      buffer_store16_nt(ors, (uint32_t)((qa + rloc) * ROWB + 16 * c), val);
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next pair overwrites the rows
     __builtin_amdgcn_wave_barrier();
   };
 
-  // First block: its whole band, and the Q rows of this wave's first head.
+  // First query block: its whole band into sK/sV, and the Q rows of this wave's
+  // first head.
   const int qb0 = grp * QPW;
-  const int nqb = min(QPW, (p.L + QB - 1) / QB - qb0);  // query blocks of this workgroup (>= 1)
-  int lo_b, hi_b;
-  key_range(qb0, lo_b, hi_b);
-  int loaded_hi = -1;  // highest key block loaded so far (the bands only move forward)
-  if (hi_b >= lo_b) {
-    for (int kb = lo_b / KB; kb <= hi_b / KB; ++kb) load_block(kb);
-    loaded_hi = hi_b / KB;
+  const int nqb = min(QPW, (p.L + QB - 1) / QB - qb0);  // query blocks of this workgroup (1 or 2)
+  int lo0, hi0;
+  key_range(qb0, lo0, hi0);
+  const int n0 = hi0 >= lo0 ? hi0 / KB - lo0 / KB + 1 : 0;  // at most NKB (window <= WMAX)
+  const int kb0 = hi0 >= lo0 ? lo0 / KB : 0;
+  for (int sl = 0; sl < n0; ++sl) load_block(kb0 + sl, sK + sl * BLKB, sV + sl * BLKB);
+  // Sink logits (log2 units) of this wave's heads, read once here: a load in
+  // the pair loop would wait for every memory operation in flight before it.
+  float sink_l2[2] = {kNegInf, kNegInf};
+  if (p.sink) {
+#pragma unroll
+    for (int pp = 0; pp < PPW; ++pp) sink_l2[pp] = p.sink[kh * G + wave + 4 * pp] * kLog2e;
   }
   bf16x8 qcur[4], qnext[4];
   load_q(qb0, 0, qcur);
+  // (the empty asm keeps these loads above the barrier, in flight with the band's)
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) asm volatile("" : "+v"(qcur[s4]));
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   __syncthreads();
 
-  for (int b = 0; b < nqb; ++b) {
-    // Block b+1: the keys it adds, loaded while block b is computed.
-    int lo_n = 0, hi_n = -1;
-    if (b + 1 < nqb) {
-      key_range(qb0 + b + 1, lo_n, hi_n);
-      if (hi_n >= lo_n) {
-        for (int kb = max(loaded_hi + 1, lo_n / KB); kb <= hi_n / KB; ++kb) load_block(kb);
-        loaded_hi = max(loaded_hi, hi_n / KB);
-      }
-    }
+  // Second query block: its band ends at most one block past the first one's
+  // (both ends move by 32 positions); that block goes to sKn/sVn now.
+  int lo1 = 0, hi1 = -1;
+  if (nqb > 1) {
+    key_range(qb0 + 1, lo1, hi1);
+    if (hi1 >= lo1 && (n0 == 0 || hi1 / KB > kb0 + n0 - 1)) load_block(hi1 / KB, sKn, sVn);
+  }
+
 #pragma unroll 1
-    for (int pp = 0; pp < PPW; ++pp) {
-      // the next (head, block) pair's Q rows, one pair ahead
-      if (pp + 1 < PPW)
-        load_q(qb0 + b, pp + 1, qnext);
-      else if (b + 1 < nqb)
-        load_q(qb0 + b + 1, 0, qnext);
-      compute_pair(kh * G + wave + 4 * pp, (qb0 + b) * QB, lo_b, hi_b, qcur);
+  for (int pp = 0; pp < PPW; ++pp) {
+    // the next (head, block) pair's Q rows, one pair ahead
+    if (pp + 1 < PPW)
+      load_q(qb0, pp + 1, qnext);
+    else if (nqb > 1)
+      load_q(qb0 + 1, 0, qnext);
+    compute_pair(std::false_type{}, kh * G + wave + 4 * pp, qb0 * QB, lo0, hi0, qcur,
+                 pp == 0 ? sink_l2[0] : sink_l2[1], kb0, n0);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) qcur[s] = qnext[s];
-    }
-    lo_b = lo_n;
-    hi_b = hi_n;
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's part of block b+1 landed
-    __syncthreads();
+    for (int s4 = 0; s4 < 4; ++s4) qcur[s4] = qnext[s4];
+  }
+  if (nqb < 2) return;
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's part of the added block landed
+  __syncthreads();
+#pragma unroll 1
+  for (int pp = 0; pp < PPW; ++pp) {
+    if (pp + 1 < PPW) load_q(qb0 + 1, pp + 1, qnext);
+    compute_pair(std::true_type{}, kh * G + wave + 4 * pp, (qb0 + 1) * QB, lo1, hi1, qcur,
+                 pp == 0 ? sink_l2[0] : sink_l2[1], kb0, n0);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) qcur[s4] = qnext[s4];
   }
 }
 
@@ -324,7 +379,8 @@ namespace attn_impl {
 bool prefill_band_fits(const FwdArgs& a) {
   const int G = a.Hq / a.Hkv;
   return a.E == E && !a.rbf && a.causal && a.window > 0 && a.window <= WMAX && a.n_reg == 0 && !a.key_len &&
-         !a.bias && a.L > 0 && (G == 4 || G == 8);
+         !a.bias && a.L > 0 && (long long)a.L * ROWB < (1LL << 31) && (long long)a.S * ROWB < (1LL << 31) &&
+         (G == 4 || G == 8);
 }
 
 hipError_t launch_prefill_bf16_band(const FwdArgs& a, hipStream_t stream) {
