@@ -56,7 +56,6 @@ using namespace attn_dev;
 namespace {
 
 constexpr int BM = 128;  // query rows per workgroup
-constexpr int BN = 64;   // keys per staged tile
 constexpr int NT = 256;  // threads per workgroup
 constexpr float kLazy = 8.f;  // rescale when a row max grows by more than this (log2 units)
 
@@ -118,23 +117,34 @@ enum { kDotPos = 0, kDotAny = 1, kRbf = 2, kRbfFold = 3 };
 // logits, uint8 mask (0 hides the pair).
 enum { kBiasNone = 0, kBiasF32 = 1, kBiasBool = 2 };
 
-// Waves per SIMD the register budget allows: E = 128 needs ~230 VGPRs (2 waves);
-// E = 64 fits in 128 VGPRs in dot mode (4 waves = 4 workgroups per CU, 128 KB of
-// LDS) and under 168 in RBF mode (3 waves), where 128 would spill; with a user
-// bias it needs up to ~210 (2 waves).
+// Keys per staged tile, and waves per SIMD the register budget allows.  64-key
+// tiles: E = 128 needs ~230 VGPRs (2 waves); E = 64 fits in 128 VGPRs in dot
+// mode (4 waves = 4 workgroups per CU, 128 KB of LDS) and under 168 in RBF mode
+// (3 waves), where 128 would spill; with a user bias it needs up to ~210 (2
+// waves).  Dot mode at E = 128 without a user bias takes 32-key tiles instead:
+// S^T then holds 16 registers instead of 32 and the kernel fits 160 VGPRs, so
+// three waves per SIMD (three workgroups of 32 KB LDS per CU) -- 2.7 % faster on
+// the causal 4x16x2048x128 prefill than 64-key tiles at two waves (32-key tiles
+// at two waves: 5 % slower; 64-key tiles at three waves spill).
 template <int E, int MODE, int UB>
-struct Occupancy {
-  static constexpr int kWaves = (E == 128 || UB != 0) ? 2 : ((MODE == kRbf || MODE == kRbfFold) ? 3 : 4);
+struct TileShape {
+  static constexpr bool kNarrow = E == 128 && UB == 0 && (MODE == kDotPos || MODE == kDotAny);
+  static constexpr int kKeys = kNarrow ? 32 : 64;
+  static constexpr int kWaves = kNarrow ? 3 : (E == 128 || UB != 0) ? 2 : ((MODE == kRbf || MODE == kRbfFold) ? 3 : 4);
 };
 
 template <int E, int MODE, int UB>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Occupancy<E, MODE, UB>::kWaves, Occupancy<E, MODE, UB>::kWaves)))
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(TileShape<E, MODE, UB>::kWaves, TileShape<E, MODE, UB>::kWaves)))
 void prefill_bf16_kernel(PrefillParams p) {
   constexpr bool RBF = MODE == kRbf || MODE == kRbfFold;  // K staged through registers, |k|^2 on chip
   constexpr bool FOLD = MODE == kRbfFold;
   constexpr bool FAST = MODE == kDotPos || FOLD;
   static_assert(UB == kBiasNone || !FAST, "a user bias needs the logits formed before the max");
-  constexpr int OSTR = E + 8;   // epilogue O row stride (elements)
+  constexpr int BN = TileShape<E, MODE, UB>::kKeys;  // keys per staged tile
+  // Epilogue O staging: padded rows, or (32-key tiles, where padded rows of two
+  // waves would not fit one tile buffer) unpadded rows with XOR-swizzled chunks.
+  constexpr bool OSWZ = BN == 32;
+  constexpr int OSTR = OSWZ ? E : E + 8;  // O row stride (elements)
   constexpr int QS = E / 16;    // MFMA steps over the head dimension
   constexpr int EB = E / 32;    // 32-row blocks of O^T
   constexpr int NB = BN / 32;   // 32-key blocks of S^T per tile
@@ -194,6 +204,14 @@ void prefill_bf16_kernel(PrefillParams p) {
   // Running state in log2 units: m is the reference max, lsum this lane's share
   // of the row sum (its 16 keys per block); the halves are added at the end.
   float m = kNegInf, lsum = 0.f;
+  // lsum is a compensated (Kahan) sum: lcomp carries the low-order part lost by
+  // each tile's addition.  With every tile adding nearly the same amount (long
+  // rows of near-equal logits) the plain fp32 sum's rounding is systematic: over
+  // 8M keys in 32-key tiles it drifted by 2.4e-3 relative (1.7e-4 in 64-key
+  // tiles).  The four-wave kernels (E = 64 dot, 128 VGPRs) keep the plain sum:
+  // the extra register spills there.
+  constexpr bool KSUM = TileShape<E, MODE, UB>::kWaves < 4;
+  float lcomp = 0.f;
   if (p.sink) {
     float s0 = p.sink[h];
     if (RBF) s0 += p.gamma * qn2;
@@ -468,6 +486,7 @@ void prefill_bf16_kernel(PrefillParams p) {
       const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m - m_new);
       m = m_new;
       lsum *= alpha;
+      if (KSUM) lcomp *= alpha;
 #pragma unroll
       for (int c = 0; c < EB; ++c)
 #pragma unroll
@@ -485,7 +504,14 @@ void prefill_bf16_kernel(PrefillParams p) {
         st[b][r] = pv;
         ps += pv;
       }
-    lsum += ps;
+    if (KSUM) {
+      const float y = ps - lcomp;
+      const float t = lsum + y;
+      lcomp = (t - lsum) - y;
+      lsum = t;
+    } else {
+      lsum += ps;
+    }
 
     // O^T += V^T * P^T, 16 keys per MFMA step.
     __builtin_amdgcn_s_setprio(1);
@@ -578,13 +604,14 @@ void prefill_bf16_kernel(PrefillParams p) {
   const float ltot = pair32_sum(lsum);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   uint16_t* sO = reinterpret_cast<uint16_t*>(wave < 2 ? sKV0 : sKV1) + (wave & 1) * 32 * OSTR;
+  auto ochunk = [&](int row, int ch) { return OSWZ ? (ch ^ (row & (ECH - 1))) : ch; };
 #pragma unroll
   for (int c = 0; c < EB; ++c)
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       const bf16x4 pk = pack_bf16x4(acc[c][4 * rq + 0] * inv, acc[c][4 * rq + 1] * inv,
                                     acc[c][4 * rq + 2] * inv, acc[c][4 * rq + 3] * inv);
-      *reinterpret_cast<bf16x4*>(&sO[l32 * OSTR + 32 * c + 8 * rq + 4 * g]) = pk;
+      *reinterpret_cast<bf16x4*>(&sO[l32 * OSTR + 8 * ochunk(l32, 4 * c + rq) + 4 * g]) = pk;
     }
   if (g == 0 && qvalid) {
     float l = kNegInf;
@@ -602,7 +629,7 @@ void prefill_bf16_kernel(PrefillParams p) {
     const int rloc = id / ECH, c = id % ECH;
     const int row = qa + rloc;
     if (row < p.L) {
-      const u32x4 val = *reinterpret_cast<const u32x4*>(&sO[rloc * OSTR + 8 * c]);
+      const u32x4 val = *reinterpret_cast<const u32x4*>(&sO[rloc * OSTR + 8 * ochunk(rloc, c)]);
       __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(p.o + (obase + row) * E + 8 * c));  // written once
     }
   }
