@@ -24,9 +24,9 @@ against it ("cpu_baseline" and "parity" of the line and of each extra).  Every
 workload is warmed up for at least 200 ms before its K timed calls, so that no
 timing falls in the clock ramp of the first calls.  The long-context decode
 figure is repeated at top level under "decode" (the metric's second half).
-"probe_peaks" holds what this GPU sustains on a bf16 GEMM and a device copy
-(vendor library work), and each roofline entry gives its fraction of the probe
-peak of its bound beside the fraction of the published one.
+"probe_peaks" holds what this GPU sustains on a bf16 GEMM, a device copy and a
+read-only sum (vendor library work), and each roofline entry gives its fraction
+of the probe peak of its bound beside the fraction of the published one.
 
 Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits with a
 message.
@@ -183,8 +183,9 @@ def warm(call, warmup: int, torch):
 def probe_peaks(torch):
     """What this GPU sustains on plain library work, beside the published peaks:
     a bf16 GEMM 8192 x 8192 x 8192 (torch.matmul, i.e. the vendor BLAS) in
-    TFLOP/s, and a 1 GiB device-to-device copy in GB/s (bytes read + written).
-    Each is warmed up for WARM_MS, then timed over back-to-back calls."""
+    TFLOP/s, a 1 GiB device-to-device copy in GB/s (bytes read + written) and a
+    sum over 1 GiB of bf16 (bytes read).  Each is warmed up for WARM_MS, then
+    timed over back-to-back calls."""
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     out = {}
@@ -214,16 +215,25 @@ def probe_peaks(torch):
     ms = rate_of(lambda: dst.copy_(src), 20)
     out["hbm_copy"] = {"value": 2.0 * nb / (ms * 1e-3) / 1e9, "unit": "GB/s",
                        "what": "1 GiB device copy, read + write bytes", "ms": ms}
-    del src, dst
+    del dst
+    xs = src.view(torch.bfloat16)
+    acc = torch.empty((), dtype=torch.float32, device=dev)
+    ms = rate_of(lambda: torch.sum(xs, dtype=torch.float32, out=acc), 20)
+    out["hbm_read"] = {"value": nb / (ms * 1e-3) / 1e9, "unit": "GB/s",
+                       "what": "torch.sum over 1 GiB of bf16, bytes read", "ms": ms}
+    del src, xs, acc
     torch.cuda.empty_cache()
     return out
 
 
 def attach_probe(entry: dict, probes) -> None:
-    """Adds the probe peak of the entry's bound and the fraction of it reached."""
+    """Adds the probe peak of the entry's bound and the fraction of it reached (for
+    HBM the better of the copy and the read-only sum)."""
     if not probes:
         return
-    p = {"mfma": probes.get("bf16_gemm"), "hbm": probes.get("hbm_copy")}.get(entry.get("bound"))
+    hbm = max((p for p in (probes.get("hbm_copy"), probes.get("hbm_read")) if p), key=lambda p: p["value"],
+              default=None)
+    p = {"mfma": probes.get("bf16_gemm"), "hbm": hbm}.get(entry.get("bound"))
     if p is None or p["unit"] != entry.get("unit"):
         return
     entry["probe_peak"] = p["value"]

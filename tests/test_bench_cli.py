@@ -41,7 +41,8 @@ def test_help_lists_every_workload():
 def test_probe_fraction_follows_the_entry_bound():
     sys.path.insert(0, ROOT)
     import bench
-    probes = {"bf16_gemm": {"value": 2000.0, "unit": "TFLOP/s"}, "hbm_copy": {"value": 5000.0, "unit": "GB/s"}}
+    probes = {"bf16_gemm": {"value": 2000.0, "unit": "TFLOP/s"}, "hbm_copy": {"value": 4000.0, "unit": "GB/s"},
+              "hbm_read": {"value": 5000.0, "unit": "GB/s"}}
     mfma = {"bound": "mfma", "unit": "TFLOP/s", "achieved": 500.0, "value": 1.0}
     bench.attach_probe(mfma, probes)
     assert mfma["probe_peak"] == 2000.0 and abs(mfma["frac_of_probe"] - 0.25) < 1e-12

@@ -41,6 +41,11 @@ PREFILL_CASES = [
     # windows wider than a workgroup's rows plus a tile: whole-tile steps run
     # between the masked steps on both sides
     W("dot_wide_window_registers", L=700, S_real=700, window=300, n_reg=3),
+    # E = 128 dot mode runs 32-key tiles: register rows over two tiles, a window
+    # edge inside a tile, a sink; and a non-causal ragged case with a few registers
+    W("dot_registers_window_sink_e128", Hq=4, Hkv=2, L=270, S_real=270, E=128, n_reg=40, window=100, sink=True),
+    W("dot_noncausal_registers_e128", N=2, L=90, S_real=150, E=128, n_reg=3, causal=False),
+    W("dot_negative_scale_registers_e128", L=100, S_real=130, E=128, n_reg=33, scale=-0.07),
     W("rbf_wide_window_sink_e128", L=650, S_real=650, E=128, mode="rbf", window=260, sink=True, gamma=0.05),
     W("dot_single_query", N=3, Hq=4, Hkv=1, L=1, S_real=999, E=128),
     W("rbf_causal_registers", L=300, S_real=300, mode="rbf", n_reg=4, k_dist="dir_lognormal"),
