@@ -43,7 +43,7 @@ constexpr int QPW = 2;              // query blocks per workgroup (the layout be
 constexpr int ROWB = E * 2;
 constexpr int BLKB = KB * ROWB;     // bytes of one 32-row block of K (or V)
 constexpr int ECH = E / 8;
-constexpr int OSTR = E + 8;
+constexpr int OSTR = E;             // O staging row stride (elements); 16-byte chunks XOR-swizzled by row
 
 struct BandParams {
   const uint16_t* q;
@@ -277,7 +277,7 @@ void prefill_band_kernel(BandParams p) {
       for (int rq = 0; rq < 4; ++rq) {
         const bf16x4 pk = pack_bf16x4(acc[c][4 * rq + 0] * inv, acc[c][4 * rq + 1] * inv, acc[c][4 * rq + 2] * inv,
                                       acc[c][4 * rq + 3] * inv);
-        *reinterpret_cast<bf16x4*>(&so[l32 * OSTR + 32 * c + 8 * rq + 4 * g]) = pk;
+        *reinterpret_cast<bf16x4*>(&so[l32 * OSTR + 8 * ((4 * c + rq) ^ (l32 & 7)) + 4 * g]) = pk;
       }
     // Stores go through resources over this head's L rows: rows at or past L
     // are dropped by the range check, so no store sits behind a branch (a
@@ -298,7 +298,7 @@ void prefill_band_kernel(BandParams p) {
     for (int it = 0; it < (QB * ECH) / 64; ++it) {
       const int id = lane + 64 * it;
       const int rloc = id / ECH, c = id % ECH;
-      const u32x4 val = *reinterpret_cast<const u32x4*>(&so[rloc * OSTR + 8 * c]);
+      const u32x4 val = *reinterpret_cast<const u32x4*>(&so[rloc * OSTR + 8 * (c ^ (rloc & 7))]);
       buffer_store16_nt(ors, (uint32_t)((qa + rloc) * ROWB + 16 * c), val);
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next pair overwrites the rows
