@@ -180,13 +180,13 @@ def warm(call, warmup: int, torch):
     return i
 
 
-def probe_peaks(torch):
+def probe_peaks(torch, n: int = 8192, nbytes: int = 1 << 30, device: str = "cuda:0"):
     """What this GPU sustains on plain library work, beside the published peaks:
     a bf16 GEMM 8192 x 8192 x 8192 (torch.matmul, i.e. the vendor BLAS) in
     TFLOP/s, a 1 GiB device-to-device copy in GB/s (bytes read + written) and a
     sum over 1 GiB of bf16 (bytes read).  Each is warmed up for WARM_MS, then
     timed over back-to-back calls."""
-    dev = torch.device("cuda:0")
+    dev = torch.device(device)
     stream = torch.cuda.current_stream(dev)
     out = {}
 
@@ -201,26 +201,25 @@ def probe_peaks(torch):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / calls
 
-    n = 8192
     x = torch.randn(n, n, device=dev).to(torch.bfloat16)
     y = torch.randn(n, n, device=dev).to(torch.bfloat16)
     z = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
     ms = rate_of(lambda: torch.matmul(x, y, out=z), 20)
     out["bf16_gemm"] = {"value": 2.0 * n ** 3 / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
-                        "what": "torch.matmul bf16 8192x8192x8192", "ms": ms}
+                        "what": f"torch.matmul bf16 {n}x{n}x{n}", "ms": ms}
     del x, y, z
-    nb = 1 << 30
+    nb = nbytes
     src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     ms = rate_of(lambda: dst.copy_(src), 20)
     out["hbm_copy"] = {"value": 2.0 * nb / (ms * 1e-3) / 1e9, "unit": "GB/s",
-                       "what": "1 GiB device copy, read + write bytes", "ms": ms}
+                       "what": f"{nb >> 20} MiB device copy, read + write bytes", "ms": ms}
     del dst
     xs = src.view(torch.bfloat16)
     acc = torch.empty((), dtype=torch.float32, device=dev)
-    ms = rate_of(lambda: torch.sum(xs, dtype=torch.float32, out=acc), 20)
+    ms = rate_of(lambda: torch.sum(xs, dim=0, dtype=torch.float32, out=acc), 20)
     out["hbm_read"] = {"value": nb / (ms * 1e-3) / 1e9, "unit": "GB/s",
-                       "what": "torch.sum over 1 GiB of bf16, bytes read", "ms": ms}
+                       "what": f"torch.sum over {nb >> 20} MiB of bf16, bytes read", "ms": ms}
     del src, xs, acc
     torch.cuda.empty_cache()
     return out

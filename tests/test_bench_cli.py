@@ -58,3 +58,35 @@ def test_probe_fraction_follows_the_entry_bound():
     none = {"bound": "mfma", "unit": "TFLOP/s", "value": 1.0}
     bench.attach_probe(none, None)
     assert "probe_peak" not in none
+
+
+def test_probe_peaks_runs_on_small_sizes():
+    """The probe leg's torch calls, on the CPU with tiny sizes and a stand-in for the
+    GPU's events and streams (the real leg runs the same calls on the GPU)."""
+    import types
+    import torch
+    sys.path.insert(0, ROOT)
+    import bench
+
+    class Event:
+        def __init__(self, enable_timing=True):
+            pass
+
+        def record(self, stream=None):
+            pass
+
+        def elapsed_time(self, other):
+            return 1.0
+
+    cuda = types.SimpleNamespace(Event=Event, synchronize=lambda: None, current_stream=lambda dev=None: None,
+                                 empty_cache=lambda: None)
+    shim = types.SimpleNamespace(**{k: getattr(torch, k) for k in dir(torch) if not k.startswith("__")})
+    shim.cuda = cuda
+    saved = bench.WARM_MS
+    bench.WARM_MS = 0.0
+    try:
+        out = bench.probe_peaks(shim, n=32, nbytes=1 << 16, device="cpu")
+    finally:
+        bench.WARM_MS = saved
+    assert set(out) == {"bf16_gemm", "hbm_copy", "hbm_read"}
+    assert all(v["value"] > 0 for v in out.values())
