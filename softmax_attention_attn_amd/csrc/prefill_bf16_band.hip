@@ -5,21 +5,28 @@
 // "Attention Sink LLM..." section 1) a block of 32 consecutive query positions
 // sees at most W + 31 keys, the same band for all Hq/Hkv query heads that share
 // a key/value head ("SDPA란 무엇인가?" section 5).  A workgroup takes one kv head
-// and a run of QPW consecutive 32-position query blocks; its four waves split the
+// and two consecutive 32-position query blocks; its four waves split the
 // group's query heads.  The keys live in LDS as 32-row blocks of K and V
 // (LDS-direct buffer loads, rows past the slice end read as zeros): the first
 // query block's band in one pair of arrays, and the one block the second query
-// block adds in another pair, loaded while the waves compute the first (its Q
-// rows too, one (head, block) pair ahead), so HBM latency is exposed once per
-// workgroup.  The reads of the first block's compute never touch the array the
-// loads in flight write, which lets them go without waiting for those loads.  Per (head, block) a wave
-// forms S^T = K * Q^T for every 32-key block of its part of the band
-// (v_mfma_f32_32x32x16_bf16, one query per lane as in prefill_bf16.hip), so the
-// whole row of logits is in registers: one max (with the sink logit of
-// "Attention Sink" section 4.2), one pass of exp2 and sums, bf16 weights
-// straight into O^T = V^T * P^T -- no running rescale and no per-tile loop.
+// block adds in another pair, loaded while the waves compute the first (the Q
+// rows of the next (head, block) pair are requested ahead too), so HBM latency
+// is exposed once per workgroup.  The reads of the first block's compute never
+// touch the array the loads in flight write, which lets them go without
+// waiting for those loads.  Per (head, block) a wave forms S^T = K * Q^T for the
+// 32-key blocks of the band (v_mfma_f32_32x32x16_bf16, one query per lane as in
+// prefill_bf16.hip), the row max with the sink logit of "Attention Sink"
+// section 4.2, exp2 and sums, and bf16 weights straight into O^T = V^T * P^T.
 // Only the key blocks on the band's two edges (window start, causal diagonal)
 // carry the visibility mask.
+//
+// With eight query heads per kv head each wave takes two heads of a block at
+// once: every K and V^T fragment read from LDS feeds both heads' MFMAs and the
+// two heads' instruction streams interleave (the kernel is bound by the
+// latency of each head's chain of steps, not by any one unit); the band then
+// goes in chunks of two key blocks with an online softmax across chunks.  With
+// four heads per kv head a wave takes one head and the whole band at once
+// (all its logits in registers, one max, no rescale).
 //
 // Scope (the caller checks it): bf16, dot logits, causal, 0 < W <= 128, E = 64,
 // Hq/Hkv = 4 or 8, no register tokens, no key lengths, no user bias.
@@ -43,6 +50,7 @@ constexpr int QPW = 2;              // query blocks per workgroup (the layout be
 constexpr int ROWB = E * 2;
 constexpr int BLKB = KB * ROWB;     // bytes of one 32-row block of K (or V)
 constexpr int ECH = E / 8;
+constexpr float kLazyBand = 8.f;     // rescale when a chunk's row max exceeds the reference by more (log2)
 constexpr int OSTR = E;             // O staging row stride (elements); 16-byte chunks XOR-swizzled by row
 
 struct BandParams {
@@ -305,6 +313,203 @@ void prefill_band_kernel(BandParams p) {
     __builtin_amdgcn_wave_barrier();
   };
 
+  // Both query heads of this wave (kh*G + wave and + 4) on one query block at
+  // once: each K and V^T fragment read from LDS feeds both heads' MFMAs, and
+  // the two heads' chains interleave.  The band goes in chunks of up to two
+  // key blocks with an online softmax across chunks (running reference max,
+  // lazy rescale as in the tiled kernel).  After the last chunk's QK^T the Q
+  // registers are refilled with the next pair's rows (nq >= 0).
+  auto compute_pair2 = [&](auto second, int qa, int lo_b, int hi_b, bf16x8 (&qA)[4], bf16x8 (&qB)[4],
+                           float sinkA, float sinkB, int kb0, int n0, int nq) __attribute__((always_inline)) {
+    constexpr bool SECOND = decltype(second)::value;
+    auto slot_k = [&](int kb) __attribute__((always_inline)) -> const uint8_t* {
+      if (!SECOND) return sK + (kb - kb0) * BLKB;
+      const int sl = kb - kb0;
+      return (sl >= 0 && sl < n0) ? sK + sl * BLKB : sKn;
+    };
+    auto slot_v = [&](int kb) __attribute__((always_inline)) -> const uint8_t* {
+      if (!SECOND) return sV + (kb - kb0) * BLKB;
+      const int sl = kb - kb0;
+      return (sl >= 0 && sl < n0) ? sV + sl * BLKB : sVn;
+    };
+    const int hA = kh * G + wave, hB = hA + 4;
+    const int qi = qa + l32;
+    const int qlast = min(qa + QB - 1, p.L - 1);
+    const int kb_lo = lo_b / KB;
+    const int nj = hi_b >= lo_b ? min(NKB, hi_b / KB - kb_lo + 1) : 0;
+    const int ip = qi + p.off;
+    const int lo = ip - p.window + 1, hi = min(ip, p.S - 1);
+    constexpr int CH = 2;  // key blocks per chunk
+    // running state (log2 units), seeded with the sink as in the tiled kernel
+    float mA = p.sink ? sinkA : kNegInf, mB = p.sink ? sinkB : kNegInf;
+    float lA = (p.sink && g == 0) ? 1.f : 0.f, lB = lA;
+    f32x16 aA[2], aB[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        aA[c][r] = 0.f;
+        aB[c][r] = 0.f;
+      }
+#pragma unroll
+    for (int ck = 0; ck < (NKB + CH - 1) / CH; ++ck) {
+      if (ck * CH < nj) {
+        f32x16 sA[CH], sB[CH];
+#pragma unroll
+        for (int jj = 0; jj < CH; ++jj) {
+          const int j = ck * CH + jj;
+          if (j < nj) {
+            const uint8_t* kt = slot_k(kb_lo + j);
+            const f32x16 zero = {};
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+              const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + krd[s4]);
+              sA[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qA[s4], s4 == 0 ? zero : sA[jj], 0, 0, 0);
+              sB[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qB[s4], s4 == 0 ? zero : sB[jj], 0, 0, 0);
+            }
+            __builtin_amdgcn_s_setprio(0);
+          }
+        }
+        if (nq >= 0 && (ck + 1) * CH >= nj) {  // last chunk: Q no longer needed
+          load_q(nq, 0, qA);
+          load_q(nq, 1, qB);
+        }
+        // edge masks (the same for both heads) and the chunk's row maxima
+        float xA = kNegInf, xB = kNegInf;
+#pragma unroll
+        for (int jj = 0; jj < CH; ++jj) {
+          const int j = ck * CH + jj;
+          if (j < nj) {
+            const int base = (kb_lo + j) * KB;
+            const bool whole = base >= qlast + p.off - p.window + 1 && base + KB - 1 <= qa + p.off;
+            if (!FAST) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                sA[jj][r] *= p.c_logit;
+                sB[jj][r] *= p.c_logit;
+              }
+            }
+            if (!whole) {
+              int lo_r = lo - base - 4 * g, hi_r = hi - base - 4 * g;
+              asm volatile("" : "+v"(lo_r), "+v"(hi_r));
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int ko = 8 * (r >> 2) + (r & 3);
+                const bool vis = (ko >= lo_r) & (ko <= hi_r);
+                sA[jj][r] = vis ? sA[jj][r] : kNegInf;
+                sB[jj][r] = vis ? sB[jj][r] : kNegInf;
+              }
+            }
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+              xA = fmaxf(fmaxf(xA, sA[jj][r]), sA[jj][r + 1]);
+              xB = fmaxf(fmaxf(xB, sB[jj][r]), sB[jj][r + 1]);
+            }
+          }
+        }
+        xA = pair32_max(xA);
+        xB = pair32_max(xB);
+        if (FAST) {
+          xA = (xA == kNegInf) ? kNegInf : xA * p.c_logit;
+          xB = (xB == kNegInf) ? kNegInf : xB * p.c_logit;
+        }
+        if (__any(xA > mA + kLazyBand)) {
+          const float mn = fmaxf(mA, xA);
+          const float al = (mn == kNegInf) ? 1.f : fast_exp2(mA - mn);
+          mA = mn;
+          lA *= al;
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) aA[c][r] *= al;
+        }
+        if (__any(xB > mB + kLazyBand)) {
+          const float mn = fmaxf(mB, xB);
+          const float al = (mn == kNegInf) ? 1.f : fast_exp2(mB - mn);
+          mB = mn;
+          lB *= al;
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) aB[c][r] *= al;
+        }
+        const float uA = (mA == kNegInf) ? 0.f : mA, uB = (mB == kNegInf) ? 0.f : mB;
+#pragma unroll
+        for (int jj = 0; jj < CH; ++jj) {
+          const int j = ck * CH + jj;
+          if (j < nj) {
+            const uint8_t* vt_s = slot_v(kb_lo + j);
+            float pa = 0.f, pb = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float wa = FAST ? fast_exp2(__builtin_fmaf(sA[jj][r], p.c_logit, -uA)) : fast_exp2(sA[jj][r] - uA);
+              const float wb = FAST ? fast_exp2(__builtin_fmaf(sB[jj][r], p.c_logit, -uB)) : fast_exp2(sB[jj][r] - uB);
+              sA[jj][r] = wa;
+              sB[jj][r] = wb;
+              pa += wa;
+              pb += wb;
+            }
+            lA += pa;
+            lB += pb;
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+              const bf16x8 fa = pack_bf16x8(sA[jj][8 * s2 + 0], sA[jj][8 * s2 + 1], sA[jj][8 * s2 + 2], sA[jj][8 * s2 + 3],
+                                            sA[jj][8 * s2 + 4], sA[jj][8 * s2 + 5], sA[jj][8 * s2 + 6], sA[jj][8 * s2 + 7]);
+              const bf16x8 fb = pack_bf16x8(sB[jj][8 * s2 + 0], sB[jj][8 * s2 + 1], sB[jj][8 * s2 + 2], sB[jj][8 * s2 + 3],
+                                            sB[jj][8 * s2 + 4], sB[jj][8 * s2 + 5], sB[jj][8 * s2 + 6], sB[jj][8 * s2 + 7]);
+#pragma unroll
+              for (int c = 0; c < 2; ++c) {
+                const shortx4 lo4 = lds_read_tr(vt_s + vrd[c][0] + 16 * s2 * ROWB);
+                const shortx4 hi4 = lds_read_tr(vt_s + vrd[c][1] + 16 * s2 * ROWB);
+                const bf16x8 vt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+                aA[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, fa, aA[c], 0, 0, 0);
+                aB[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, fb, aB[c], 0, 0, 0);
+              }
+            }
+            __builtin_amdgcn_s_setprio(0);
+          }
+        }
+      }
+    }
+    if (nq >= 0 && nj == 0) {  // nothing visible: the rows are still needed next
+      load_q(nq, 0, qA);
+      load_q(nq, 1, qB);
+    }
+    // Epilogue, one head after the other through this wave's staging rows.
+    auto out = [&](int h, const f32x16 (&ac)[2], float lsum, float M) __attribute__((always_inline)) {
+      const float ltot = pair32_sum(lsum);
+      const float inv = ltot > 0.f ? __builtin_amdgcn_rcpf(ltot) : 0.f;
+      uint16_t* so = sO[wave];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const bf16x4 pk = pack_bf16x4(ac[c][4 * rq + 0] * inv, ac[c][4 * rq + 1] * inv, ac[c][4 * rq + 2] * inv,
+                                        ac[c][4 * rq + 3] * inv);
+          *reinterpret_cast<bf16x4*>(&so[l32 * OSTR + 8 * ((4 * c + rq) ^ (l32 & 7)) + 4 * g]) = pk;
+        }
+      const size_t obase = ((size_t)n * p.Hq + h) * p.L;
+      const __amdgpu_buffer_rsrc_t lrs = make_rsrc(p.lse + obase, (uint32_t)p.L * 4u);
+      const __amdgpu_buffer_rsrc_t ors = make_rsrc(p.o + obase * E, (uint32_t)p.L * ROWB);
+      buffer_store4(lrs, (uint32_t)qi * 4u, ltot > 0.f ? (M + __builtin_amdgcn_logf(ltot)) * kLn2 : kNegInf);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int it = 0; it < (QB * ECH) / 64; ++it) {
+        const int id = lane + 64 * it;
+        const int rloc = id / ECH, c = id % ECH;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(&so[rloc * OSTR + 8 * (c ^ (rloc & 7))]);
+        buffer_store16_nt(ors, (uint32_t)((qa + rloc) * ROWB + 16 * c), val);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the rows are written again
+      __builtin_amdgcn_wave_barrier();
+    };
+    out(hA, aA, lA, mA);
+    out(hB, aB, lB, mB);
+  };
+
   // First query block: its whole band into sK/sV, and the Q rows of this wave's
   // first head.
   const int qb0 = grp * QPW;
@@ -337,6 +542,16 @@ void prefill_band_kernel(BandParams p) {
     if (hi1 >= lo1 && (n0 == 0 || hi1 / KB > kb0 + n0 - 1)) load_block(hi1 / KB, sKn, sVn);
   }
 
+  if constexpr (PPW == 2) {
+    load_q(qb0, 1, qnext);  // the second head's rows
+    compute_pair2(std::false_type{}, qb0 * QB, lo0, hi0, qcur, qnext, sink_l2[0], sink_l2[1], kb0, n0,
+                  nqb > 1 ? qb0 + 1 : -1);
+    if (nqb < 2) return;
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's part of the added block landed
+    __syncthreads();
+    compute_pair2(std::true_type{}, (qb0 + 1) * QB, lo1, hi1, qcur, qnext, sink_l2[0], sink_l2[1], kb0, n0, -1);
+    return;
+  }
 #pragma unroll 1
   for (int pp = 0; pp < PPW; ++pp) {
     // the next (head, block) pair's Q rows, one pair ahead
