@@ -72,6 +72,11 @@ PREFILL_CASES = [
     W("band_gqa4_xcd_window127_sink", N=2, Hq=16, Hkv=4, L=333, S_real=333, window=127, sink=True),
     W("band_gqa8_window32_one_block", Hq=8, Hkv=1, L=31, S_real=64, window=32),
     W("band_gqa8_xcd_window128_sink", Hq=64, Hkv=8, L=700, S_real=700, window=128, sink=True),
+    # logits with a spread of tens of units: the two-heads-per-wave path's
+    # chunk maxima move its reference (the online rescale), positive and
+    # negative scale (raw scores vs logits formed first)
+    W("band_gqa8_large_logits_rescale", Hq=16, Hkv=2, L=300, S_real=300, window=128, scale=1.0, sink=True),
+    W("band_gqa8_negative_large_logits", Hq=8, Hkv=1, L=200, S_real=260, window=100, scale=-1.0),
     W("tiled_gqa2_window64", Hq=4, Hkv=2, L=300, S_real=300, window=64, sink=True),
     # fp32 problems of 64 row tiles and more go to the tiled kernel (smaller ones to the
     # one-wave-per-row kernel, which every fp32 case above takes)
