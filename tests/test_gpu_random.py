@@ -93,6 +93,39 @@ def test_random_backward(w):
         assert np.all(np.abs(d - ref["dsink"]) <= bound)
 
 
+# The key-band kernel (bf16, dot, causal window <= 128, E = 64, GQA groups of 4
+# or 8, no registers) on random draws: L below, equal to and above S (rows
+# with nothing visible), ragged block counts, windows from one key to 128,
+# sinks, and dot scales from -2 to 2 (large ones move the reference max
+# between the key-block chunks of the eight-heads path).
+def _band_draw(i):
+    r = np.random.default_rng(5000 + i)
+    G = int(r.choice([4, 8]))
+    Hkv = int(r.integers(1, 4))
+    N = int(r.integers(1, 3))
+    S_real = int(r.integers(1, 600))
+    L = int(r.choice([S_real, int(r.integers(1, 600))]))
+    window = int(r.choice([1, 31, 32, 33, 64, 100, 127, 128, int(r.integers(1, 129))]))
+    sink = bool(r.random() < 0.5)
+    scale = float(r.choice([0.125, 0.125, 1.0, 2.0, -0.125, -1.0]))
+    name = f"b{i:02d}_N{N}_{G * Hkv}to{Hkv}_L{L}_S{S_real}_w{window}_s{scale}{'_sink' if sink else ''}"
+    return Workload(name, "bf16", N, G * Hkv, Hkv, L, S_real, 64, "dot", scale, 0.125, True, window, 0, sink,
+                    False, 7000 + i, "normal")
+
+
+BAND_DRAWS = [_band_draw(i) for i in range(32)]
+
+
+@pytest.mark.parametrize("w", BAND_DRAWS, ids=[w.name for w in BAND_DRAWS])
+def test_random_band_forward(w):
+    say(f"[random band] {w.name}")
+    inp = gen.generate(w)
+    q, k, v, sink = to_device(inp)
+    o, lse = run_gpu(w, q, k, v, sink)
+    torch.cuda.synchronize()
+    check(w, inp, o, lse)
+
+
 # The general bias on random draws: float32 addends with -inf entries or
 # boolean masks (with a fully masked row), broadcast over batch and/or head,
 # with or without per-sequence key lengths.
