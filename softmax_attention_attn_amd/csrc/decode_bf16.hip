@@ -150,13 +150,15 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams p) {
       const bool ok = vk < v1;
       const uint16_t* row = kbase + (size_t)key_row(ok ? vk : v0, p, sidx, v0) * E;
 #pragma unroll
-      for (int s = 0; s < QS; ++s) kr[b][s] = load16_nt_or_zero(row + 32 * s + 8 * g, ok);
+      for (int s = 0; s < QS; ++s)
+        kr[b][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + 32 * s + 8 * g));
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int vk = vb + (i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4));
-      const bool ok = vk < v1 && l16 < ECH;
-      vr[i] = load16_nt_or_zero(vbase + (size_t)key_row(ok ? vk : v0, p, sidx, v0) * E + 8 * l16, ok);
+      const bool ok = vk < v1;
+      vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+          vbase + (size_t)key_row(ok ? vk : v0, p, sidx, v0) * E + 8 * min(l16, ECH - 1)));
     }
   };
 
@@ -224,23 +226,24 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams p) {
     }
   };
 
-  {
+  // Step st + 4 is requested while step st is computed.  The requests are
+  // unconditional (a step past the end reads row v0 for every key, all masked):
+  // a conditional one leaves the compiler unable to count the loads in flight,
+  // and it then waits for all of them -- the prefetch included -- before each step.
+  if (steps > 0) {
     u32x4 kA[2][QS], vA[8];
     int st = wave;
-    if (st < steps) load_step(st, kA, vA);
+    load_step(st, kA, vA);
     for (; st < steps; st += NWAVE) {
       u32x4 kB[2][QS], vB[8];
-      const bool nxt = st + NWAVE < steps;
-      if (nxt) load_step(st + NWAVE, kB, vB);
+      load_step(st + NWAVE, kB, vB);
       compute_step(st, kA, vA);
-      if (nxt) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int s = 0; s < QS; ++s) kA[b][s] = kB[b][s];
+        for (int s = 0; s < QS; ++s) kA[b][s] = kB[b][s];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) vA[i] = vB[i];
-      }
+      for (int i = 0; i < 8; ++i) vA[i] = vB[i];
     }
   }
 
