@@ -58,6 +58,7 @@ namespace {
 constexpr int BM = 128;  // query rows per workgroup
 constexpr int NT = 256;  // threads per workgroup
 constexpr float kLazy = 8.f;  // rescale when a row max grows by more than this (log2 units)
+constexpr float kLazyBound = 16.f;  // RBF: skip the tile max once the reference is this close to the bound
 
 struct PrefillParams {
   const uint16_t* q;
@@ -217,6 +218,8 @@ void prefill_bf16_kernel(PrefillParams p) {
   // the extra register spills there.
   constexpr bool KSUM = TileShape<E, MODE, UB>::kWaves < 4;
   float lcomp = 0.f;
+  // RBF (folded): the largest logit a key can give this row, c * |q|^2 / 2.
+  const float qbound = FOLD ? 0.5f * p.c_logit * qn2 : 0.f;
   if (p.sink) {
     float s0 = p.sink[h];
     if (RBF) s0 += p.gamma * qn2;
@@ -476,6 +479,10 @@ void prefill_bf16_kernel(PrefillParams p) {
           st[b][r] = vis ? st[b][r] : kNegInf;
         }
     }
+    // RBF: no logit of this row exceeds qbound (the logit of a key equal to q),
+    // so once every row's reference is within kLazyBound of it no weight can
+    // pass 2^kLazyBound and the tile's max is not needed.
+    if (!FOLD || __any(qbound - m > kLazyBound)) {
     float mx = kNegInf;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -496,6 +503,7 @@ void prefill_bf16_kernel(PrefillParams p) {
       for (int c = 0; c < EB; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[c][r] *= alpha;
+    }
     }
     const float m_use = (m == kNegInf) ? 0.f : m;
 
