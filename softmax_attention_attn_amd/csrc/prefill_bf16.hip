@@ -1,8 +1,8 @@
 // prefill_bf16.hip -- fused tiled attention forward for bf16 inputs on gfx950.
 //
 // One workgroup = 4 waves = 128 query rows of one (batch, query head); each
-// wave owns 32 rows.  Keys are streamed in tiles of 64 through LDS; the score
-// tile is never written to memory (the tiling + online softmax of the
+// wave owns 32 rows.  Keys are streamed in tiles of 64 (32 in dot mode at
+// E = 128, see TileShape) through LDS; the score tile is never written to memory (the tiling + online softmax of the
 // FlashAttention row in "어텐션 메커니즘" section 6, and the running max /
 // running sum described in "SDPA란 무엇인가?" section 2).
 //
@@ -43,7 +43,10 @@
 // moves lazily: the accumulator is rescaled only when a row max grows by more
 // than 2^8 over the reference (O = acc / l does not depend on the reference;
 // it only bounds p by 256).  With a positive scale the dot-mode max is taken on
-// the raw scores and each weight costs one fma + exp2.
+// the raw scores and each weight costs one fma + exp2.  In folded RBF mode no
+// logit of a row exceeds c|q|^2/2, and the tile max is skipped once the
+// reference is within 2^16 of that bound.  Row sums are compensated (Kahan)
+// where a register allows it.
 // The epilogue transposes O through LDS so that stores are whole rows.
 #include <type_traits>
 
