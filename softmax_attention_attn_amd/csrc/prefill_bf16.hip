@@ -229,6 +229,13 @@ void prefill_bf16_kernel(PrefillParams p) {
     m = s0 * kLog2e;
     lsum = (g == 0) ? 1.f : 0.f;
   }
+  // Derived from m, updated only where m moves: thr, the value a raw score (FAST)
+  // or logit must pass to grow the row max by more than kLazy, and -m (0 while
+  // the row has seen nothing).
+  const float inv_c = FAST ? 1.f / p.c_logit : 1.f;
+  auto lazy_thr = [&](float mref) { return FAST ? (mref + kLazy) * inv_c : mref + kLazy; };
+  float thr = lazy_thr(m);
+  float negm = (m == kNegInf) ? 0.f : -m;
   f32x16 acc[EB];
 #pragma unroll
   for (int c = 0; c < EB; ++c)
@@ -486,20 +493,24 @@ void prefill_bf16_kernel(PrefillParams p) {
     // so once every row's reference is within kLazyBound of it no weight can
     // pass 2^kLazyBound and the tile's max is not needed.
     if (!FOLD || __any(qbound - m > kLazyBound)) {
+    // This lane's half of its row's max (the other half sits in lane ^ 32).
     float mx = kNegInf;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, st[b][r]), st[b][r + 1]);  // v_max3 chain
-    mx = pair32_max(mx);
-    if (FAST) mx = (mx == kNegInf) ? kNegInf : mx * p.c_logit;
 
     // Lazy reference max: move it (and rescale) only when a row max would grow
-    // by more than kLazy; otherwise weights stay below 2^kLazy.
-    if (__any(mx > m + kLazy)) {
+    // by more than kLazy -- i.e. when some half-row max passes thr; otherwise
+    // weights stay below 2^kLazy.  Only then is the whole row's max formed.
+    if (__any(mx > thr)) {
+      mx = pair32_max(mx);
+      if (FAST) mx = (mx == kNegInf) ? kNegInf : mx * p.c_logit;
       const float m_new = fmaxf(m, mx);
       const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m - m_new);
       m = m_new;
+      thr = lazy_thr(m);
+      negm = (m == kNegInf) ? 0.f : -m;
       lsum *= alpha;
       if (KSUM) lcomp *= alpha;
 #pragma unroll
@@ -508,15 +519,14 @@ void prefill_bf16_kernel(PrefillParams p) {
         for (int r = 0; r < 16; ++r) acc[c][r] *= alpha;
     }
     }
-    const float m_use = (m == kNegInf) ? 0.f : m;
 
-    float ps = 0.f;
+    float ps = -0.f;  // (-0 + x == x: the first addition folds away)
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pv = FAST ? fast_exp2(__builtin_fmaf(st[b][r], p.c_logit, -m_use))
-                              : fast_exp2(st[b][r] - m_use);
+        const float pv = FAST ? fast_exp2(__builtin_fmaf(st[b][r], p.c_logit, negm))
+                              : fast_exp2(st[b][r] + negm);
         st[b][r] = pv;
         ps += pv;
       }
