@@ -343,6 +343,13 @@ void prefill_band_kernel(BandParams p) {
     // running state (log2 units), seeded with the sink as in the tiled kernel
     float mA = p.sink ? sinkA : kNegInf, mB = p.sink ? sinkB : kNegInf;
     float lA = (p.sink && g == 0) ? 1.f : 0.f, lB = lA;
+    // Derived from the references, updated only where they move: the value a
+    // half-row max (raw scores when FAST) must pass to grow the row max by more
+    // than kLazyBand, and -m (0 while the row has seen nothing).
+    const float inv_c = FAST ? 1.f / p.c_logit : 1.f;
+    auto lazy_thr = [&](float mref) { return FAST ? (mref + kLazyBand) * inv_c : mref + kLazyBand; };
+    float tA = lazy_thr(mA), tB = lazy_thr(mB);
+    float nA = (mA == kNegInf) ? 0.f : -mA, nB = (mB == kNegInf) ? 0.f : -mB;
     f32x16 aA[2], aB[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -408,43 +415,46 @@ void prefill_band_kernel(BandParams p) {
             }
           }
         }
-        xA = pair32_max(xA);
-        xB = pair32_max(xB);
-        if (FAST) {
-          xA = (xA == kNegInf) ? kNegInf : xA * p.c_logit;
-          xB = (xB == kNegInf) ? kNegInf : xB * p.c_logit;
-        }
-        if (__any(xA > mA + kLazyBand)) {
+        // xA, xB: this lane's half of the chunk's row max (the other half sits
+        // in lane ^ 32); the whole-row max is formed only when a reference moves.
+        if (__any(xA > tA)) {
+          xA = pair32_max(xA);
+          if (FAST) xA = (xA == kNegInf) ? kNegInf : xA * p.c_logit;
           const float mn = fmaxf(mA, xA);
           const float al = (mn == kNegInf) ? 1.f : fast_exp2(mA - mn);
           mA = mn;
+          tA = lazy_thr(mA);
+          nA = (mA == kNegInf) ? 0.f : -mA;
           lA *= al;
 #pragma unroll
           for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) aA[c][r] *= al;
         }
-        if (__any(xB > mB + kLazyBand)) {
+        if (__any(xB > tB)) {
+          xB = pair32_max(xB);
+          if (FAST) xB = (xB == kNegInf) ? kNegInf : xB * p.c_logit;
           const float mn = fmaxf(mB, xB);
           const float al = (mn == kNegInf) ? 1.f : fast_exp2(mB - mn);
           mB = mn;
+          tB = lazy_thr(mB);
+          nB = (mB == kNegInf) ? 0.f : -mB;
           lB *= al;
 #pragma unroll
           for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) aB[c][r] *= al;
         }
-        const float uA = (mA == kNegInf) ? 0.f : mA, uB = (mB == kNegInf) ? 0.f : mB;
 #pragma unroll
         for (int jj = 0; jj < CH; ++jj) {
           const int j = ck * CH + jj;
           if (j < nj) {
             const uint8_t* vt_s = slot_v(kb_lo + j);
-            float pa = 0.f, pb = 0.f;
+            float pa = -0.f, pb = -0.f;  // (-0 + x == x: the first additions fold away)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const float wa = FAST ? fast_exp2(__builtin_fmaf(sA[jj][r], p.c_logit, -uA)) : fast_exp2(sA[jj][r] - uA);
-              const float wb = FAST ? fast_exp2(__builtin_fmaf(sB[jj][r], p.c_logit, -uB)) : fast_exp2(sB[jj][r] - uB);
+              const float wa = FAST ? fast_exp2(__builtin_fmaf(sA[jj][r], p.c_logit, nA)) : fast_exp2(sA[jj][r] + nA);
+              const float wb = FAST ? fast_exp2(__builtin_fmaf(sB[jj][r], p.c_logit, nB)) : fast_exp2(sB[jj][r] + nB);
               sA[jj][r] = wa;
               sB[jj][r] = wb;
               pa += wa;
