@@ -165,6 +165,7 @@ void prefill_bf16_kernel(PrefillParams p) {
   constexpr int KCH = BN * ECH / NT;       // K chunks per thread (RBF register staging)
   static_assert(IPW * RPI * 4 == BN, "tile must split into whole 1 KB loads per wave");
   static_assert(KCH * NT == BN * ECH, "K staging must tile evenly");
+  static_assert(!FOLD || KCH % 2 == 0, "the norm split converts two rows at a time");
   static_assert(2 * 32 * OSTR * 2 <= 2 * TILEB, "epilogue staging of two waves must fit one tile buffer");
 
   // [buf][K tile | V tile], each tile row-major with swizzled 16-byte chunks.
@@ -288,6 +289,18 @@ void prefill_bf16_kernel(PrefillParams p) {
   }
 
   u32x4 kreg[KCH];  // RBF only: K chunks on their way to LDS
+  // RBF: LDS byte offset of each staged chunk (row (tid + NT*i) / ECH, swizzled),
+  // formed once; the empty asm keeps the compiler from recomputing it per tile.
+  uint32_t kwo[RBF ? KCH : 1];
+  if (RBF) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int id = tid + NT * i;
+      const int row = id / ECH, c = id % ECH;
+      kwo[i] = (uint32_t)(row * ROWB + ((c ^ tile_swz<E>(row)) * 16));
+      asm volatile("" : "+v"(kwo[i]));
+    }
+  }
 
   auto tile_keys = [&](int t, int& j0, int& kc) __attribute__((always_inline)) {
     if (t < n_reg_tiles) {
@@ -325,27 +338,40 @@ void prefill_bf16_kernel(PrefillParams p) {
   // LDS-direct requests have landed.
   auto finish_tile = [&](int buf) __attribute__((always_inline)) {
     if (RBF) {
+      // |k|^2 of each staged key row: its ECH chunks sit in ECH consecutive lanes.
+      float ss[KCH];
 #pragma unroll
       for (int i = 0; i < KCH; ++i) {
-        const int id = tid + NT * i;
-        const int row = id / ECH, c = id % ECH;
-        *reinterpret_cast<u32x4*>(k_tile(buf) + row * ROWB + ((c ^ tile_swz<E>(row)) * 16)) = kreg[i];
-        // |k|^2 of this key row: its ECH chunks sit in ECH consecutive lanes.
-        const float ss = group_sum<ECH>(sumsq8(kreg[i]));
+        *reinterpret_cast<u32x4*>(k_tile(buf) + kwo[i]) = kreg[i];
+        ss[i] = group_sum<ECH>(sumsq8(kreg[i]));
+      }
+      const int c = tid % ECH;  // the same chunk for every i (NT is a multiple of ECH)
+      if (c == 0) {
+        const int row0 = tid / ECH;
         if (FOLD) {
-          if (c == 0) {
-            // -|k|^2/2 = hi + mid + lo, each rounded to bf16 (nearest even) in turn
-            const float v0 = -0.5f * ss;
-            const __bf16 hi = (__bf16)v0;
-            const float v1 = v0 - (float)hi;
-            const __bf16 mid = (__bf16)v1;
-            const __bf16 lo = (__bf16)(v1 - (float)mid);
-            sKn[buf][row] = u32x2{(uint32_t)__builtin_bit_cast(uint16_t, hi) |
-                                      ((uint32_t)__builtin_bit_cast(uint16_t, mid) << 16),
-                                  (uint32_t)__builtin_bit_cast(uint16_t, lo)};
+          // -|k|^2/2 = hi + mid + lo, each rounded to bf16 (nearest even) in
+          // turn; two rows per conversion (v_cvt_pk_bf16_f32).
+          typedef float f32x2v __attribute__((ext_vector_type(2)));
+          typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+          auto widen = [](bf16x2v x) {
+            const uint32_t w = __builtin_bit_cast(uint32_t, x);
+            return f32x2v{bf16_lo(w), bf16_hi(w)};
+          };
+#pragma unroll
+          for (int i = 0; i < KCH; i += 2) {
+            const f32x2v v0 = {-0.5f * ss[i], -0.5f * ss[i + 1]};
+            const bf16x2v hi = __builtin_convertvector(v0, bf16x2v);
+            const f32x2v v1 = v0 - widen(hi);
+            const bf16x2v mid = __builtin_convertvector(v1, bf16x2v);
+            const bf16x2v lo = __builtin_convertvector(v1 - widen(mid), bf16x2v);
+            const uint32_t h = __builtin_bit_cast(uint32_t, hi), md = __builtin_bit_cast(uint32_t, mid),
+                           l = __builtin_bit_cast(uint32_t, lo);
+            sKn[buf][row0 + (NT / ECH) * i] = u32x2{__builtin_amdgcn_perm(md, h, 0x05040100u), l & 0xffffu};
+            sKn[buf][row0 + (NT / ECH) * (i + 1)] = u32x2{__builtin_amdgcn_perm(md, h, 0x07060302u), l >> 16};
           }
-        } else if (c == 0) {
-          sBias[buf][row] = p.c_bias * ss;
+        } else {
+#pragma unroll
+          for (int i = 0; i < KCH; ++i) sBias[buf][row0 + (NT / ECH) * i] = p.c_bias * ss[i];
         }
       }
     }
