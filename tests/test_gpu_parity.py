@@ -46,6 +46,12 @@ PREFILL_CASES = [
     W("dot_registers_window_sink_e128", Hq=4, Hkv=2, L=270, S_real=270, E=128, n_reg=40, window=100, sink=True),
     W("dot_noncausal_registers_e128", N=2, L=90, S_real=150, E=128, n_reg=3, causal=False),
     W("dot_negative_scale_registers_e128", L=100, S_real=130, E=128, n_reg=33, scale=-0.07),
+    # the lazy reference max: a large positive scale moves it on most tiles (the
+    # half-row max passing the raw-score threshold), a tiny one never after the
+    # first tile (threshold (m + 8) / c of order 1e5 against raw scores of order 10)
+    W("dot_large_scale_rescales_e128", Hq=4, Hkv=2, L=333, S_real=333, E=128, scale=0.9, sink=True),
+    W("dot_tiny_scale_e128", L=200, S_real=260, E=128, scale=1e-4),
+    W("dot_large_scale_rescales_e64", N=2, L=300, S_real=300, scale=1.5, n_reg=5),
     W("rbf_wide_window_sink_e128", L=650, S_real=650, E=128, mode="rbf", window=260, sink=True, gamma=0.05),
     W("dot_single_query", N=3, Hq=4, Hkv=1, L=1, S_real=999, E=128),
     W("rbf_causal_registers", L=300, S_real=300, mode="rbf", n_reg=4, k_dist="dir_lognormal"),
