@@ -168,7 +168,8 @@ size_t attn_bwd_workspace_bytes(int N, int Hq, int L);
  *   workspace, workspace_bytes  device scratch of at least
  *                    attn_decode_workspace_bytes(...) bytes, 16-byte aligned,
  *                    owned by the caller; its contents on entry do not matter.
- * Only bf16 is implemented (dt = ATTN_F32 returns ATTN_ERR_UNSUPPORTED).
+ * bf16 runs the split products on MFMA (P rounded to bf16, as in attn_fwd);
+ * f32 runs them on the vector ALUs in fp32 throughout.
  */
 int attn_decode(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E,
                 const void* q, const void* k, const void* v,
@@ -245,7 +246,8 @@ int attn_stream_append(attn_dtype dt, int N, int Hkv, int E, int n_sink, int win
  * o (N, Hq, 1, E), lse (N, Hq, 1).  The result equals attn_decode over the full
  * history of pos + 1 keys with n_reg = n_sink, window = window, causal = 1.
  * mode, scale, gamma, sink, num_splits, workspace: as for attn_decode, with
- * workspace size from attn_stream_decode_workspace_bytes.  bf16 only.
+ * workspace size from attn_stream_decode_workspace_bytes.  bf16 or f32 (the
+ * cache rows and q of element type dt, as written by attn_stream_append).
  */
 int attn_stream_decode(attn_dtype dt, int N, int Hq, int Hkv, int E, int n_sink, int window, long long pos,
                        const void* q, const void* k_cache, const void* v_cache,

@@ -139,6 +139,11 @@ long long stream_rows(int n_sink, int window, long long pos) {
   return pos + 1 < cap ? pos + 1 : cap;
 }
 
+// Split-K decode of either element type (bf16: MFMA kernel, f32: vector-ALU kernel).
+hipError_t launch_decode(attn_dtype dt, const attn_impl::DecodeArgs& d, hipStream_t stream) {
+  return dt == ATTN_BF16 ? attn_impl::launch_decode_bf16(d, stream) : attn_impl::launch_decode_f32(d, stream);
+}
+
 // Validation and launch set-up shared by attn_decode and attn_decode_noalloc:
 // everything but the partial-result buffers.  *need = their size in bytes.
 // Returns ATTN_OK (with *empty set when there is nothing to compute) or an error.
@@ -150,7 +155,6 @@ int decode_setup(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, con
   if (L != 1) return fail(ATTN_ERR_SHAPE, "decode takes exactly one query per sequence (L=%d)", L);
   int rc = check_args(dt, N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o, lse);
   if (rc != ATTN_OK) return rc;
-  if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode is implemented for bf16 only");
   if (num_splits < 0) return fail(ATTN_ERR_ARG, "num_splits=%d must be >= 0", num_splits);
   if (N == 0) {
     *empty = true;
@@ -419,7 +423,7 @@ int attn_decode(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, cons
   if (!aligned(workspace, 16)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
   d.part_o = static_cast<float*>(workspace);
   d.part_ml = d.part_o + (size_t)N * Hq * d.num_splits * E;
-  return hip_status(attn_impl::launch_decode_bf16(d, static_cast<hipStream_t>(stream)), "attn_decode launch");
+  return hip_status(launch_decode(dt, d, static_cast<hipStream_t>(stream)), "attn_decode launch");
 }
 
 int attn_decode_noalloc(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, const void* q, const void* k,
@@ -443,7 +447,7 @@ int attn_decode_noalloc(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int
   // so nothing left by an earlier call is read: no clearing is needed.
   d.part_o = scratch;
   d.part_ml = scratch + (size_t)N * Hq * d.num_splits * E;
-  return hip_status(attn_impl::launch_decode_bf16(d, static_cast<hipStream_t>(stream)), "attn_decode_noalloc launch");
+  return hip_status(launch_decode(dt, d, static_cast<hipStream_t>(stream)), "attn_decode_noalloc launch");
 }
 
 // ----------------------------------------------------------------------------- rolling cache
@@ -500,7 +504,6 @@ int attn_stream_decode(attn_dtype dt, int N, int Hq, int Hkv, int E, int n_sink,
   // any order: plain decode over rows [0, S) of slices that are `cap` rows apart.
   int rc = check_args(dt, N, Hq, Hkv, 1, (int)cap, E, q, k_cache, v_cache, mode, scale, gamma, 1, 0, 0, sink, o, lse);
   if (rc != ATTN_OK) return rc;
-  if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode is implemented for bf16 only");
   if (num_splits < 0) return fail(ATTN_ERR_ARG, "num_splits=%d must be >= 0", num_splits);
   if (N == 0) return ok();
   const int splits = resolve_splits(N, Hq, Hkv, S, 1, 0, 0, num_splits);
@@ -516,7 +519,7 @@ int attn_stream_decode(attn_dtype dt, int N, int Hq, int Hkv, int E, int n_sink,
   d.num_splits = splits;
   d.part_o = static_cast<float*>(workspace);
   d.part_ml = d.part_o + (size_t)N * Hq * splits * E;
-  return hip_status(attn_impl::launch_decode_bf16(d, static_cast<hipStream_t>(stream)), "attn_stream_decode launch");
+  return hip_status(launch_decode(dt, d, static_cast<hipStream_t>(stream)), "attn_stream_decode launch");
 }
 
 const char* attn_status_string(int status) {

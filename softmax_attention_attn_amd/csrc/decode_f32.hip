@@ -1,0 +1,327 @@
+// decode_f32.hip -- split-K decode for float32 inputs on gfx950.
+//
+// The same split-K scheme and partial format as the bf16 decode
+// (decode_bf16.hip): workgroup (split, kv head x query group, batch) streams
+// the keys of its split once for up to 16 query heads of the GQA group and
+// writes, per query head, the running max (log2 units), the running sum and
+// the unnormalised output; decode_f32_combine merges the splits with
+// log-sum-exp weights and adds the sink logit ("Attention Sink" section 4.2).
+// The arithmetic is fp32 throughout (no operand is rounded), so the products
+// run on the vector ALUs: a key row is spread over R = E/4 lanes, 16 bytes
+// each; every lane forms the partial dot products of its 4 dims with the
+// group's query heads and a butterfly over the R lanes (DPP row operations,
+// then v_permlane16_swap at E = 128) completes them.  Each R-lane row group
+// keeps its own online-softmax state (running max and sum, 4 output dims per
+// query head; "SDPA란 무엇인가?" section 2) over the keys it takes, and the row
+// groups of the 4 waves are merged through LDS at the end.  Decode is bound by
+// the K/V bytes (SOCKET summary, problem statement), which are read once, with
+// the non-temporal hint.
+#include "device_common.h"
+#include "kernels.h"
+
+using namespace attn_dev;
+
+namespace {
+
+constexpr int NT = 256;  // threads per workgroup
+constexpr int NWAVE = 4;
+
+struct DecodeF32Params {
+  const float* q;
+  const float* k;
+  const float* v;
+  float* part_o;
+  float* part_ml;
+  int N, Hq, Hkv, kv_rows, n_reg;
+  int first_real;  // keys n_reg .. n_reg+first_real-1 are outside the window
+  int nkeys;       // n_reg + visible real keys
+  int chunk;       // keys per split
+  int num_splits;
+  int qgroups;     // ceil(G / 16)
+  float c_logit, c_bias;
+};
+
+// Sum over the R lanes of a row group (R = 16: one DPP row; R = 32: two rows).
+template <int R>
+__device__ __forceinline__ float row_group_sum(float v) {
+  v = group_sum<16>(v);
+  if (R == 32) v = pair16_sum(v);
+  return v;
+}
+
+// NS: query slots per workgroup (a power of two, at least the group size when
+// G <= 16, else 16 per query group).
+template <int E, bool RBF, int NS>
+__global__ __launch_bounds__(NT, 2) void decode_split_f32_kernel(DecodeF32Params p) {
+  constexpr int R = E / 4;         // lanes per key row
+  constexpr int RG = 64 / R;       // row groups per wave
+  constexpr int KPS = NWAVE * RG;  // keys per workgroup step
+  __shared__ float sM[NWAVE * RG][NS];
+  __shared__ float sL[NWAVE * RG][NS];
+  __shared__ __attribute__((aligned(16))) float sO[NWAVE * RG][NS][E];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = lane / R, rl = lane % R;
+  const int grp = wave * RG + rg;  // this lane's row group in the workgroup
+  const int split = blockIdx.x;
+  const int n = blockIdx.z;
+  const int G = p.Hq / p.Hkv;
+  const int kvh = blockIdx.y / p.qgroups;
+  const int qg = blockIdx.y % p.qgroups;
+  const int nslots = min(NS, G - qg * 16);  // real query heads of this workgroup
+
+  // The query heads' 4 dims of this lane (zeros for slots past the group).
+  f32x4 qv[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int h = kvh * G + qg * 16 + min(s, nslots - 1);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(p.q + ((size_t)n * p.Hq + h) * E + 4 * rl);
+    qv[s] = s < nslots ? x : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const size_t kvoff = ((size_t)n * p.Hkv + kvh) * (size_t)p.kv_rows * E;
+  const float* kbase = p.k + kvoff;
+  const float* vbase = p.v + kvoff;
+  const int v0 = split * p.chunk;
+  const int v1 = min(v0 + p.chunk, p.nkeys);
+  const int steps = v1 > v0 ? (v1 - v0 + KPS - 1) / KPS : 0;
+  // Virtual key index -> key row: registers first, then the visible real keys.
+  auto key_row = [&](int vidx) { return vidx < p.n_reg ? vidx : vidx + p.first_real; };
+
+  float m[NS], l[NS];
+  f32x4 acc[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    m[s] = kNegInf;
+    l[s] = 0.f;
+    acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Step st: this row group's key is v0 + st*KPS + grp; past v1 it reads row
+  // v0 (every lane stays in bounds) and is masked.
+  auto load = [&](int st, f32x4& kr, f32x4& vr) {
+    const int vk = v0 + st * KPS + grp;
+    const size_t row = (size_t)key_row(vk < v1 ? vk : v0);
+    kr = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kbase + row * E + 4 * rl));
+    vr = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(vbase + row * E + 4 * rl));
+  };
+  auto compute = [&](int st, const f32x4& kr, const f32x4& vr) {
+    const bool live = v0 + st * KPS + grp < v1;
+    float nk = 0.f;
+    if (RBF) nk = row_group_sum<R>(kr[0] * kr[0] + kr[1] * kr[1] + kr[2] * kr[2] + kr[3] * kr[3]);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      float d = qv[s][0] * kr[0];
+      d = __builtin_fmaf(qv[s][1], kr[1], d);
+      d = __builtin_fmaf(qv[s][2], kr[2], d);
+      d = __builtin_fmaf(qv[s][3], kr[3], d);
+      d = row_group_sum<R>(d);
+      float x = d * p.c_logit;
+      if (RBF) x = __builtin_fmaf(p.c_bias, nk, x);
+      if (!live) x = kNegInf;
+      const float m_new = fmaxf(m[s], x);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = exp2f(m[s] - m_use);
+      const float w = exp2f(x - m_use);
+      m[s] = m_new;
+      l[s] = __builtin_fmaf(l[s], alpha, w);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[s][e] = __builtin_fmaf(acc[s][e], alpha, w * vr[e]);
+    }
+  };
+
+  // Step st + 1 is requested while step st is computed (unconditional requests:
+  // a step past the end reads row v0, masked).
+  if (steps > 0) {
+    f32x4 kA, vA;
+    load(0, kA, vA);
+    for (int st = 0; st < steps; ++st) {
+      f32x4 kB, vB;
+      load(st + 1, kB, vB);
+      compute(st, kA, vA);
+      kA = kB;
+      vA = vB;
+    }
+  }
+
+  // Merge the row groups: max, sum and output dims of every (row group, slot).
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (rl == 0) {
+      sM[grp][s] = m[s];
+      sL[grp][s] = l[s];
+    }
+    *reinterpret_cast<f32x4*>(&sO[grp][s][4 * rl]) = acc[s];
+  }
+  __syncthreads();
+  const size_t part_base = ((size_t)n * p.Hq + (size_t)kvh * G + qg * 16) * p.num_splits + split;
+  for (int idx = tid; idx < nslots * E; idx += NT) {
+    const int sl = idx / E, e = idx % E;
+    float M = kNegInf;
+#pragma unroll
+    for (int r = 0; r < NWAVE * RG; ++r) M = fmaxf(M, sM[r][sl]);
+    const float Mu = (M == kNegInf) ? 0.f : M;
+    float o = 0.f;
+#pragma unroll
+    for (int r = 0; r < NWAVE * RG; ++r) o += exp2f(sM[r][sl] - Mu) * sO[r][sl][e];
+    const size_t pi = part_base + (size_t)sl * p.num_splits;
+    p.part_o[pi * E + e] = o;
+    if (e == 0) {
+      float lt = 0.f;
+#pragma unroll
+      for (int r = 0; r < NWAVE * RG; ++r) lt += exp2f(sM[r][sl] - Mu) * sL[r][sl];
+      p.part_ml[pi * 2 + 0] = M;
+      p.part_ml[pi * 2 + 1] = lt;
+    }
+  }
+}
+
+struct CombineF32Params {
+  const float* q;
+  const float* part_o;
+  const float* part_ml;
+  const float* sink;
+  float* o;
+  float* lse;
+  int Hq, num_splits, rbf;
+  float gamma;
+};
+
+template <int E>
+__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
+  const int e = threadIdx.x;
+  red[e] = v;
+  __syncthreads();
+#pragma unroll
+  for (int s = E / 2; s > 0; s >>= 1) {
+    if (e < s) red[e] = is_max ? fmaxf(red[e], red[e + s]) : red[e] + red[e + s];
+    __syncthreads();
+  }
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
+// One workgroup per (batch, query head), one thread per output dim: the split
+// maxima are reduced first, then the weighted partial outputs summed in chunks
+// of splits whose weights sit in LDS (as in the bf16 combine).
+constexpr int kCombineChunk = 1024;
+
+template <int E>
+__global__ __launch_bounds__(E) void decode_f32_combine(CombineF32Params p) {
+  __shared__ float sRed[E];
+  __shared__ float sW[kCombineChunk];
+  const int nh = blockIdx.x;
+  const int h = nh % p.Hq;
+  const int e = threadIdx.x;
+
+  float qn2 = 0.f;
+  if (p.rbf) {
+    const float qe = p.q[(size_t)nh * E + e];
+    qn2 = block_reduce<E>(qe * qe, sRed, false);
+  }
+  const size_t base = (size_t)nh * p.num_splits;
+  float sink2 = kNegInf;
+  if (p.sink) sink2 = (p.sink[h] + (p.rbf ? p.gamma * qn2 : 0.f)) * kLog2e;
+  float mloc = kNegInf;
+  for (int s = e; s < p.num_splits; s += E) mloc = fmaxf(mloc, p.part_ml[(base + s) * 2]);
+  const float M = fmaxf(sink2, block_reduce<E>(mloc, sRed, true));
+  const float Mu = (M == kNegInf) ? 0.f : M;
+
+  float lloc = 0.f, acc = 0.f;
+  for (int c0 = 0; c0 < p.num_splits; c0 += kCombineChunk) {
+    const int cn = min(kCombineChunk, p.num_splits - c0);
+    for (int s = e; s < cn; s += E) {
+      const float w = exp2f(p.part_ml[(base + c0 + s) * 2] - Mu);
+      sW[s] = w;
+      lloc += w * p.part_ml[(base + c0 + s) * 2 + 1];
+    }
+    __syncthreads();
+    const float* po = p.part_o + (base + c0) * E + e;
+    for (int s = 0; s < cn; ++s) acc += sW[s] * po[(size_t)s * E];
+    __syncthreads();
+  }
+  float l = block_reduce<E>(lloc, sRed, false);
+  if (p.sink) l += exp2f(sink2 - Mu);
+  p.o[(size_t)nh * E + e] = l > 0.f ? acc / l : 0.f;
+  if (e == 0) {
+    float lv = kNegInf;
+    if (l > 0.f) {
+      lv = (M + log2f(l)) * kLn2;
+      if (p.rbf) lv -= p.gamma * qn2;
+    }
+    p.lse[nh] = lv;
+  }
+}
+
+template <int E, bool RBF, int NS>
+hipError_t launch_t(const DecodeF32Params& p, const CombineF32Params& c, int N, hipStream_t stream) {
+  dim3 grid((unsigned)p.num_splits, (unsigned)(p.Hkv * p.qgroups), (unsigned)N);
+  hipLaunchKernelGGL((decode_split_f32_kernel<E, RBF, NS>), grid, dim3(NT), 0, stream, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((decode_f32_combine<E>), dim3((unsigned)(N * p.Hq)), dim3(E), 0, stream, c);
+  return hipGetLastError();
+}
+
+template <int E, bool RBF>
+hipError_t launch_ns(const DecodeF32Params& p, const CombineF32Params& c, int N, int G, hipStream_t stream) {
+  if (G <= 1) return launch_t<E, RBF, 1>(p, c, N, stream);
+  if (G <= 2) return launch_t<E, RBF, 2>(p, c, N, stream);
+  if (G <= 4) return launch_t<E, RBF, 4>(p, c, N, stream);
+  if (G <= 8) return launch_t<E, RBF, 8>(p, c, N, stream);
+  return launch_t<E, RBF, 16>(p, c, N, stream);
+}
+
+}  // namespace
+
+namespace attn_impl {
+
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream) {
+  const FwdArgs& f = a.f;
+  if (a.key_index) return hipErrorInvalidValue;  // indexed (sparse) decode is bf16 only
+  const DecodeKeys dk = decode_keys(f.S, f.n_reg, f.causal, f.window);
+  DecodeF32Params p;
+  p.q = static_cast<const float*>(f.q);
+  p.k = static_cast<const float*>(f.k);
+  p.v = static_cast<const float*>(f.v);
+  p.part_o = a.part_o;
+  p.part_ml = a.part_ml;
+  p.N = f.N;
+  p.Hq = f.Hq;
+  p.Hkv = f.Hkv;
+  p.kv_rows = f.kv_rows;
+  p.n_reg = f.n_reg;
+  p.first_real = dk.first_real;
+  p.nkeys = dk.count;
+  p.num_splits = a.num_splits;
+  p.chunk = (p.nkeys + a.num_splits - 1) / a.num_splits;
+  if (p.chunk == 0) p.chunk = 1;
+  const int G = f.Hq / f.Hkv;
+  p.qgroups = (G + 15) / 16;
+  if (f.rbf) {
+    p.c_logit = 2.f * f.gamma * 1.4426950408889634f;
+    p.c_bias = -f.gamma * 1.4426950408889634f;
+  } else {
+    p.c_logit = f.scale * 1.4426950408889634f;
+    p.c_bias = 0.f;
+  }
+  CombineF32Params c;
+  c.q = p.q;
+  c.part_o = a.part_o;
+  c.part_ml = a.part_ml;
+  c.sink = f.sink;
+  c.o = static_cast<float*>(f.o);
+  c.lse = f.lse;
+  c.Hq = f.Hq;
+  c.num_splits = a.num_splits;
+  c.rbf = f.rbf;
+  c.gamma = f.gamma;
+  if (f.E == 128)
+    return f.rbf ? launch_ns<128, true>(p, c, f.N, G, stream) : launch_ns<128, false>(p, c, f.N, G, stream);
+  return f.rbf ? launch_ns<64, true>(p, c, f.N, G, stream) : launch_ns<64, false>(p, c, f.N, G, stream);
+}
+
+}  // namespace attn_impl

@@ -57,6 +57,8 @@ bool prefill_band_fits(const FwdArgs& a);
 hipError_t launch_prefill_bf16_band(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+// fp32 inputs: the same split-K scheme and partials on the vector ALUs (no key_index).
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 
 // Device scratch for the no-allocation decode (decode_bf16.hip): a static
 // device array of kDecodeScratchBytes per GPU.  decode_scratch() returns its

@@ -99,7 +99,7 @@ def test_fwd_empty_is_a_no_op(lib):
 @pytest.mark.parametrize("kw,code", [
     (dict(L=2), -2),
     (dict(L=0), -2),
-    (dict(dt=1), -4),
+    (dict(dt=5), -3),
     (dict(splits=-1), -8),
     (dict(ws=None), -6),
     (dict(wsb=16), -6),
@@ -216,7 +216,7 @@ def test_stream_append_empty_is_a_no_op(lib):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dt=1), -4),
+    (dict(dt=5), -3),
     (dict(window=0), -8),
     (dict(n_sink=-4), -8),
     (dict(pos=-1), -8),
@@ -321,12 +321,12 @@ def test_missing_library_fails_loudly(monkeypatch):
 
 
 def test_decode_noalloc_rejects_before_any_hip_call(lib):
-    # partials beyond the static scratch, L != 1, bad dtype: all refused on the host
+    # partials beyond the static scratch, L != 1, unknown dtype: all refused on the host
     big = lib.attn_decode_noalloc(0, 64, 64, 8, 1, 1 << 20, 128, A, A, A, 0, 0.1, 0.0, 1, 0, 0, None, A, A, 4096,
                                   None)
     assert big == -6 and b"static scratch" in lib.attn_last_error()
     assert lib.attn_decode_noalloc(0, 1, 4, 2, 2, 64, 64, A, A, A, 0, 0.1, 0.0, 1, 0, 0, None, A, A, 0, None) == -2
-    assert lib.attn_decode_noalloc(1, 1, 4, 2, 1, 64, 64, A, A, A, 0, 0.1, 0.0, 1, 0, 0, None, A, A, 0, None) == -4
+    assert lib.attn_decode_noalloc(5, 1, 4, 2, 1, 64, 64, A, A, A, 0, 0.1, 0.0, 1, 0, 0, None, A, A, 0, None) == -3
     assert lib.attn_decode_noalloc(0, 1, 4, 3, 1, 64, 64, A, A, A, 0, 0.1, 0.0, 1, 0, 0, None, A, A, 0, None) == -2
     # nothing to compute: no HIP call either
     assert lib.attn_decode_noalloc(0, 0, 4, 2, 1, 64, 64, None, None, None, 0, 0.1, 0.0, 1, 0, 0, None, None, None,
