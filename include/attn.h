@@ -264,8 +264,8 @@ size_t attn_stream_decode_workspace_bytes(int N, int Hq, int Hkv, int E, int n_s
  * steps 1-4).  proj: (tables*bits, E) float32 random hyperplanes, drawn by the
  * caller (the method is data-independent: any fixed random draw).
  *
- * attn_socket_hash -- prefill step: for every key row of k (N, Hkv, S, E, bf16)
- * and table t, bit b of the code of (key j, table t) is set iff the float32
+ * attn_socket_hash -- prefill step: for every key row of k (N, Hkv, S, E; bf16
+ * or f32 as dt says, v likewise) and table t, bit b of the code of (key j, table t) is set iff the float32
  * projection proj[t*bits + b] . k_j (fused multiply-adds in element order) is
  * > 0.  buckets: (N, Hkv, S, C) bytes with C = attn_socket_code_bytes(tables,
  * bits): with bits <= 4 two codes share a byte (table t in the low nibble of
@@ -295,7 +295,8 @@ int attn_socket_code_bytes(int tables, int bits);
  * num_splits: 0 = choose; a split takes at most 4096 selected keys, so a count
  * below ceil(top_k / 4096) is raised to it.
  * workspace: attn_socket_decode_workspace_bytes(...) bytes, 256-byte aligned.
- * bf16 only.
+ * bf16 or f32 (q, k, v and o of element type dt; the exact attention over the
+ * chosen keys runs as attn_decode does for that type).
  */
 int attn_socket_decode(attn_dtype dt, int N, int Hq, int Hkv, int S, int E, int tables, int bits, float tau,
                        int top_k, const void* q, const void* k, const void* v, const float* proj,

@@ -11,7 +11,7 @@ or a call is rejected, an exception is raised.
     stream_append(k_new, v_new, k_cache, v_cache, n_sink=4, window=W, pos=p)
     o, lse = stream_decode(q, k_cache, v_cache, n_sink=4, window=W, pos=p, ...)
 
-q (N, Hq, L, E), k and v (N, Hkv, S, E), all bf16 (or all float32 for fwd),
+q (N, Hq, L, E), k and v (N, Hkv, S, E), all bf16 or all float32 (bwd: bf16),
 contiguous, on one GPU; sink (Hq,) float32.  Returns o like q and lse
 (N, Hq, L) float32.
 """
@@ -412,7 +412,7 @@ def socket_hash(k: torch.Tensor, v: torch.Tensor, proj: torch.Tensor, *, tables:
                 stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """SOCKET prefill hashing through attn_socket_hash: bucket codes (N, Hkv, S, C) uint8 with
     C = socket_code_bytes(tables, bits) (codes of at most 4 bits packed two per byte, see
-    unpack_codes) and value norms (N, Hkv, S) float32 of a bf16 key/value cache; proj
+    unpack_codes) and value norms (N, Hkv, S) float32 of a bf16 or float32 key/value cache; proj
     (tables*bits, E) float32."""
     for name, t in (("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or t.dim() != 4 or not t.is_contiguous() or \

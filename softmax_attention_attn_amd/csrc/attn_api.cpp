@@ -291,7 +291,7 @@ int attn_socket_code_bytes(int tables, int bits) {
 
 int attn_socket_hash(attn_dtype dt, int N, int Hkv, int S, int E, int tables, int bits, const void* k, const void* v,
                      const float* proj, unsigned char* buckets, float* vnorm, void* stream) {
-  if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "SOCKET hashing is implemented for bf16 keys only");
+  if (dt != ATTN_BF16 && dt != ATTN_F32) return fail(ATTN_ERR_DTYPE, "unknown dtype %d", (int)dt);
   int rc = socket_check(N, Hkv, Hkv, S, E, tables, bits);
   if (rc != ATTN_OK) return rc;
   if ((long long)N * S == 0) return ok();
@@ -299,8 +299,8 @@ int attn_socket_hash(attn_dtype dt, int N, int Hkv, int S, int E, int tables, in
   if (!aligned(k, 16) || (v && !aligned(v, 16)) || !aligned(proj, 4) || (vnorm && !aligned(vnorm, 4)))
     return fail(ATTN_ERR_ALIGN, "k and v must be 16-byte aligned, proj and vnorm 4-byte aligned");
   if (((long long)N * Hkv * S + 255) / 256 > kMaxGrid) return fail(ATTN_ERR_SHAPE, "grid too large");
-  attn_impl::SocketHashArgs a{k, v, proj, buckets, vnorm, N, Hkv, S, E, tables, bits};
-  return hip_status(attn_impl::launch_socket_hash_bf16(a, static_cast<hipStream_t>(stream)), "attn_socket_hash launch");
+  attn_impl::SocketHashArgs a{k, v, proj, buckets, vnorm, N, Hkv, S, E, tables, bits, dt == ATTN_F32};
+  return hip_status(attn_impl::launch_socket_hash(a, static_cast<hipStream_t>(stream)), "attn_socket_hash launch");
 }
 
 // Workspace layout: bucket probabilities, scores, selected rows, decode partials.
@@ -340,7 +340,6 @@ int attn_socket_decode(attn_dtype dt, int N, int Hq, int Hkv, int S, int E, int 
                        void* stream) {
   int rc = check_args(dt, N, Hq, Hkv, 1, S, E, q, k, v, mode, scale, gamma, 1, 0, 0, sink, o, lse);
   if (rc != ATTN_OK) return rc;
-  if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "SOCKET decode is implemented for bf16 only");
   rc = socket_check(N, Hq, Hkv, S, E, tables, bits);
   if (rc != ATTN_OK) return rc;
   if (!(std::isfinite(tau) && tau > 0.f)) return fail(ATTN_ERR_ARG, "tau must be finite and > 0");
@@ -377,8 +376,9 @@ int attn_socket_decode(attn_dtype dt, int N, int Hq, int Hkv, int S, int E, int 
   s.bits = bits;
   s.top_k = top_k;
   s.tau = tau;
+  s.f32 = dt == ATTN_F32;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  rc = hip_status(attn_impl::launch_socket_select_bf16(s, st), "attn_socket_decode select launch");
+  rc = hip_status(attn_impl::launch_socket_select(s, st), "attn_socket_decode select launch");
   if (rc != ATTN_OK) return rc;
   attn_impl::DecodeArgs d;
   d.f = make_args(N, Hq, Hkv, 1, S, E, q, k, v, mode, scale, gamma, 1, 0, 0, sink, o, lse);
@@ -387,7 +387,7 @@ int attn_socket_decode(attn_dtype dt, int N, int Hq, int Hkv, int S, int E, int 
   d.part_ml = d.part_o + (size_t)N * Hq * l.splits * E;
   d.key_index = s.selected;
   d.index_count = top_k;
-  return hip_status(attn_impl::launch_decode_bf16(d, st), "attn_socket_decode launch");
+  return hip_status(launch_decode(dt, d, st), "attn_socket_decode launch");
 }
 
 int attn_decode_num_splits(int N, int Hq, int Hkv, int S, int E, int causal, int window, int n_reg) {

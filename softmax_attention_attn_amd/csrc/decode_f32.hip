@@ -39,7 +39,12 @@ struct DecodeF32Params {
   int num_splits;
   int qgroups;     // ceil(G / 16)
   float c_logit, c_bias;
+  // Indexed mode: every query head has its own list of nkeys key rows at
+  // key_index[(n*Hq + h)*nkeys ..]; one query head per workgroup.
+  const int* key_index;
 };
+
+constexpr int kIdxMax = attn_impl::kDecodeIndexMax;  // indexed mode: longest key list of one split
 
 // Sum over the R lanes of a row group (R = 16: one DPP row; R = 32: two rows).
 template <int R>
@@ -50,15 +55,18 @@ __device__ __forceinline__ float row_group_sum(float v) {
 }
 
 // NS: query slots per workgroup (a power of two, at least the group size when
-// G <= 16, else 16 per query group).
-template <int E, bool RBF, int NS>
+// G <= 16, else 16 per query group; 1 in indexed mode).  PF: key steps whose
+// loads are in flight.  IDX: indexed mode.
+template <int E, bool RBF, int NS, int PF, bool IDX>
 __global__ __launch_bounds__(NT, 2) void decode_split_f32_kernel(DecodeF32Params p) {
+  static_assert(!IDX || NS == 1, "indexed mode takes one query head per workgroup");
   constexpr int R = E / 4;         // lanes per key row
   constexpr int RG = 64 / R;       // row groups per wave
   constexpr int KPS = NWAVE * RG;  // keys per workgroup step
   __shared__ float sM[NWAVE * RG][NS];
   __shared__ float sL[NWAVE * RG][NS];
   __shared__ __attribute__((aligned(16))) float sO[NWAVE * RG][NS][E];
+  __shared__ int sIdx[IDX ? kIdxMax : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -68,15 +76,16 @@ __global__ __launch_bounds__(NT, 2) void decode_split_f32_kernel(DecodeF32Params
   const int split = blockIdx.x;
   const int n = blockIdx.z;
   const int G = p.Hq / p.Hkv;
-  const int kvh = blockIdx.y / p.qgroups;
-  const int qg = blockIdx.y % p.qgroups;
-  const int nslots = min(NS, G - qg * 16);  // real query heads of this workgroup
+  // The workgroup's query heads are hbase .. hbase + nslots - 1.
+  const int kvh = IDX ? (int)blockIdx.y / G : (int)blockIdx.y / p.qgroups;
+  const int hbase = IDX ? (int)blockIdx.y : kvh * G + ((int)blockIdx.y % p.qgroups) * 16;
+  const int nslots = IDX ? 1 : min(NS, kvh * G + G - hbase);
 
   // The query heads' 4 dims of this lane (zeros for slots past the group).
   f32x4 qv[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const int h = kvh * G + qg * 16 + min(s, nslots - 1);
+    const int h = hbase + min(s, nslots - 1);
     const f32x4 x = *reinterpret_cast<const f32x4*>(p.q + ((size_t)n * p.Hq + h) * E + 4 * rl);
     qv[s] = s < nslots ? x : f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -87,8 +96,17 @@ __global__ __launch_bounds__(NT, 2) void decode_split_f32_kernel(DecodeF32Params
   const int v0 = split * p.chunk;
   const int v1 = min(v0 + p.chunk, p.nkeys);
   const int steps = v1 > v0 ? (v1 - v0 + KPS - 1) / KPS : 0;
-  // Virtual key index -> key row: registers first, then the visible real keys.
-  auto key_row = [&](int vidx) { return vidx < p.n_reg ? vidx : vidx + p.first_real; };
+  if (IDX) {  // the split's key rows, read once (chunk <= kIdxMax)
+    const int* kidx = p.key_index + ((size_t)n * p.Hq + hbase) * p.nkeys;
+    for (int i = tid; i < v1 - v0; i += NT) sIdx[i] = kidx[v0 + i];
+    __syncthreads();
+  }
+  // Key index -> key row: the split's list in indexed mode; else registers
+  // first, then the visible real keys.
+  auto key_row = [&](int vidx) {
+    if (IDX) return sIdx[vidx - v0];
+    return vidx < p.n_reg ? vidx : vidx + p.first_real;
+  };
 
   float m[NS], l[NS];
   f32x4 acc[NS];
@@ -132,17 +150,21 @@ __global__ __launch_bounds__(NT, 2) void decode_split_f32_kernel(DecodeF32Params
     }
   };
 
-  // Step st + 1 is requested while step st is computed (unconditional requests:
-  // a step past the end reads row v0, masked).
+  // A ring of PF steps in flight: once step st is computed, its registers take
+  // the request for step st + PF (unconditional requests: a step past the end
+  // reads row v0, masked).  The ring index is a compile-time constant.
   if (steps > 0) {
-    f32x4 kA, vA;
-    load(0, kA, vA);
-    for (int st = 0; st < steps; ++st) {
-      f32x4 kB, vB;
-      load(st + 1, kB, vB);
-      compute(st, kA, vA);
-      kA = kB;
-      vA = vB;
+    f32x4 kb[PF], vb[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) load(i, kb[i], vb[i]);
+    for (int st = 0; st < steps; st += PF) {
+#pragma unroll
+      for (int i = 0; i < PF; ++i) {
+        if (st + i < steps) {
+          compute(st + i, kb[i], vb[i]);
+          load(st + i + PF, kb[i], vb[i]);
+        }
+      }
     }
   }
 
@@ -156,7 +178,7 @@ __global__ __launch_bounds__(NT, 2) void decode_split_f32_kernel(DecodeF32Params
     *reinterpret_cast<f32x4*>(&sO[grp][s][4 * rl]) = acc[s];
   }
   __syncthreads();
-  const size_t part_base = ((size_t)n * p.Hq + (size_t)kvh * G + qg * 16) * p.num_splits + split;
+  const size_t part_base = ((size_t)n * p.Hq + hbase) * p.num_splits + split;
   for (int idx = tid; idx < nslots * E; idx += NT) {
     const int sl = idx / E, e = idx % E;
     float M = kNegInf;
@@ -256,10 +278,11 @@ __global__ __launch_bounds__(E) void decode_f32_combine(CombineF32Params p) {
   }
 }
 
-template <int E, bool RBF, int NS>
+template <int E, bool RBF, int NS, bool IDX = false>
 hipError_t launch_t(const DecodeF32Params& p, const CombineF32Params& c, int N, hipStream_t stream) {
-  dim3 grid((unsigned)p.num_splits, (unsigned)(p.Hkv * p.qgroups), (unsigned)N);
-  hipLaunchKernelGGL((decode_split_f32_kernel<E, RBF, NS>), grid, dim3(NT), 0, stream, p);
+  dim3 grid((unsigned)p.num_splits, (unsigned)(IDX ? p.Hq : p.Hkv * p.qgroups), (unsigned)N);
+  constexpr int PF = NS >= 16 ? 2 : 4;
+  hipLaunchKernelGGL((decode_split_f32_kernel<E, RBF, NS, PF, IDX>), grid, dim3(NT), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((decode_f32_combine<E>), dim3((unsigned)(N * p.Hq)), dim3(E), 0, stream, c);
@@ -268,6 +291,7 @@ hipError_t launch_t(const DecodeF32Params& p, const CombineF32Params& c, int N, 
 
 template <int E, bool RBF>
 hipError_t launch_ns(const DecodeF32Params& p, const CombineF32Params& c, int N, int G, hipStream_t stream) {
+  if (p.key_index) return launch_t<E, RBF, 1, true>(p, c, N, stream);
   if (G <= 1) return launch_t<E, RBF, 1>(p, c, N, stream);
   if (G <= 2) return launch_t<E, RBF, 2>(p, c, N, stream);
   if (G <= 4) return launch_t<E, RBF, 4>(p, c, N, stream);
@@ -281,7 +305,6 @@ namespace attn_impl {
 
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream) {
   const FwdArgs& f = a.f;
-  if (a.key_index) return hipErrorInvalidValue;  // indexed (sparse) decode is bf16 only
   const DecodeKeys dk = decode_keys(f.S, f.n_reg, f.causal, f.window);
   DecodeF32Params p;
   p.q = static_cast<const float*>(f.q);
@@ -295,10 +318,12 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream) {
   p.kv_rows = f.kv_rows;
   p.n_reg = f.n_reg;
   p.first_real = dk.first_real;
-  p.nkeys = dk.count;
+  p.nkeys = a.key_index ? a.index_count : dk.count;
+  p.key_index = a.key_index;
   p.num_splits = a.num_splits;
   p.chunk = (p.nkeys + a.num_splits - 1) / a.num_splits;
   if (p.chunk == 0) p.chunk = 1;
+  if (p.key_index && p.chunk > kIdxMax) return hipErrorInvalidValue;
   const int G = f.Hq / f.Hkv;
   p.qgroups = (G + 15) / 16;
   if (f.rbf) {

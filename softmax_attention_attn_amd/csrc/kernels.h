@@ -57,7 +57,7 @@ bool prefill_band_fits(const FwdArgs& a);
 hipError_t launch_prefill_bf16_band(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
-// fp32 inputs: the same split-K scheme and partials on the vector ALUs (no key_index).
+// fp32 inputs: the same split-K scheme, partials and indexed mode on the vector ALUs.
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 
 // Device scratch for the no-allocation decode (decode_bf16.hip): a static
@@ -99,8 +99,9 @@ struct SocketHashArgs {
   uint8_t* buckets;        // (N, Hkv, S, socket_code_bytes(tables, bits))
   float* vnorm;            // (N, Hkv, S)
   int N, Hkv, S, E, tables, bits;
+  bool f32 = false;        // k and v are float32 (else bf16)
 };
-hipError_t launch_socket_hash_bf16(const SocketHashArgs& a, hipStream_t stream);
+hipError_t launch_socket_hash(const SocketHashArgs& a, hipStream_t stream);
 
 struct SocketSelectArgs {
   const void* q;           // (N, Hq, 1, E)
@@ -112,8 +113,9 @@ struct SocketSelectArgs {
   int* selected;           // [N*Hq][top_k] ascending key rows
   int N, Hq, Hkv, S, E, tables, bits, top_k;
   float tau;
+  bool f32 = false;        // q is float32 (else bf16)
 };
-hipError_t launch_socket_select_bf16(const SocketSelectArgs& a, hipStream_t stream);
+hipError_t launch_socket_select(const SocketSelectArgs& a, hipStream_t stream);
 size_t socket_lds_bytes(int G, int tables, int bits);
 
 // Rolling key/value cache append: tokens at positions pos .. pos+T-1 from

@@ -13,7 +13,9 @@
 //  - socket_hash_kernel: one thread per key; the `bits` projections of each
 //    table are float32 fused multiply-add chains over the key's elements in
 //    element order (the same float32 decision an fp32 reference makes), bit
-//    set iff > 0; hyperplanes staged in LDS.  Also writes |v|.
+//    set iff > 0; hyperplanes staged in LDS.  Also writes |v|.  Keys and
+//    values are bf16 or float32 (the key row is held as 32-bit words either
+//    way: two bf16 elements or one float32 element per word).
 //  - socket_prob_kernel: per query head, y = W q and, per table, the
 //    probability of every bucket: the softmax over the 2^bits sign patterns of
 //    sum_b s_b y_b / tau factorises into prod_b sigmoid(2 s_b y_b / tau).
@@ -45,29 +47,38 @@ constexpr int SEL_T = 1024;    // threads of the selection workgroup
 // multiply-add chain over the elements in order, starting from zero.
 constexpr int HASH_LDS = 32 * 1024;
 
-template <int E, int BP>
+template <int E, int BP, bool F32>
 __global__ __launch_bounds__(256) void socket_hash_kernel(attn_impl::SocketHashArgs a) {
   extern __shared__ float sW[];
   constexpr int TG = HASH_LDS / (E * BP * 4);  // tables per LDS stage
+  constexpr int KW = F32 ? E : E / 2;          // 32-bit words of one key row
   typedef float wvec __attribute__((ext_vector_type(BP)));
   const long long nkeys = (long long)a.N * a.Hkv * a.S;
   const long long j = (long long)blockIdx.x * 256 + threadIdx.x;
   const bool ok = j < nkeys;
-  uint32_t kw[E / 2];
+  uint32_t kw[KW];
   {
-    const uint16_t* krow = static_cast<const uint16_t*>(a.k) + (size_t)(ok ? j : 0) * E;
+    const uint32_t* krow = static_cast<const uint32_t*>(a.k) + (size_t)(ok ? j : 0) * KW;
 #pragma unroll
-    for (int c = 0; c < E / 8; ++c) {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(krow + 8 * c);
+    for (int c = 0; c < KW / 4; ++c) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(krow + 4 * c);
 #pragma unroll
       for (int w = 0; w < 4; ++w) kw[4 * c + w] = x[w];
     }
   }
   if (ok && a.vnorm) {
-    const uint16_t* vrow = static_cast<const uint16_t*>(a.v) + (size_t)j * E;
+    const uint32_t* vrow = static_cast<const uint32_t*>(a.v) + (size_t)j * KW;
     float ss = 0.f;
 #pragma unroll
-    for (int c = 0; c < E / 8; ++c) ss += sumsq8(*reinterpret_cast<const u32x4*>(vrow + 8 * c));
+    for (int c = 0; c < KW / 4; ++c) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(vrow + 4 * c);
+      if (F32) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) ss = __builtin_fmaf(__uint_as_float(x[w]), __uint_as_float(x[w]), ss);
+      } else {
+        ss += sumsq8(x);
+      }
+    }
     a.vnorm[j] = sqrtf(ss);
   }
   // Codes are gathered into 32-bit words (8 four-bit or 4 eight-bit codes),
@@ -93,7 +104,8 @@ __global__ __launch_bounds__(256) void socket_hash_kernel(attn_impl::SocketHashA
       for (int b = 0; b < BP; ++b) x[b] = 0.f;
 #pragma unroll
       for (int e2 = 0; e2 < E / 2; ++e2) {
-        const float k0 = bf16_lo(kw[e2]), k1 = bf16_hi(kw[e2]);
+        const float k0 = F32 ? __uint_as_float(kw[2 * e2]) : bf16_lo(kw[e2]);
+        const float k1 = F32 ? __uint_as_float(kw[2 * e2 + 1]) : bf16_hi(kw[e2]);
         const wvec w0 = *reinterpret_cast<const wvec*>(w + (2 * e2) * BP);
         const wvec w1 = *reinterpret_cast<const wvec*>(w + (2 * e2 + 1) * BP);
 #pragma unroll
@@ -124,20 +136,28 @@ __global__ __launch_bounds__(256) void socket_hash_kernel(attn_impl::SocketHashA
   }
 }
 
-template <int E>
+template <int E, bool F32>
 __global__ __launch_bounds__(256) void socket_prob_kernel(attn_impl::SocketSelectArgs a) {
   __shared__ float sY[kMaxProj];
   const int nh = blockIdx.x;
   const int tid = threadIdx.x;
   const int nproj = a.tables * a.bits;
-  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (size_t)nh * E;
+  constexpr int QW = F32 ? E : E / 2;  // 32-bit words of the query row
+  const uint32_t* qrow = static_cast<const uint32_t*>(a.q) + (size_t)nh * QW;
   for (int i = tid; i < nproj; i += 256) {
     const float* w = a.proj + (size_t)i * E;
     float y = 0.f;
     for (int e2 = 0; e2 < E / 2; ++e2) {
-      const uint32_t qq = *reinterpret_cast<const uint32_t*>(qrow + 2 * e2);
-      y = __builtin_fmaf(bf16_lo(qq), w[2 * e2], y);
-      y = __builtin_fmaf(bf16_hi(qq), w[2 * e2 + 1], y);
+      float q0, q1;
+      if (F32) {
+        q0 = __uint_as_float(qrow[2 * e2]);
+        q1 = __uint_as_float(qrow[2 * e2 + 1]);
+      } else {
+        q0 = bf16_lo(qrow[e2]);
+        q1 = bf16_hi(qrow[e2]);
+      }
+      y = __builtin_fmaf(q0, w[2 * e2], y);
+      y = __builtin_fmaf(q1, w[2 * e2 + 1], y);
     }
     sY[i] = y;
   }
@@ -812,33 +832,49 @@ __global__ __launch_bounds__(SEL_T) void socket_select_kernel(attn_impl::SocketS
   }
 }
 
+template <bool F32>
+void launch_hash_t(const attn_impl::SocketHashArgs& a, dim3 grid, hipStream_t stream) {
+  if (a.E == 128) {
+    if (a.bits <= 4)
+      hipLaunchKernelGGL((socket_hash_kernel<128, 4, F32>), grid, dim3(256), HASH_LDS, stream, a);
+    else
+      hipLaunchKernelGGL((socket_hash_kernel<128, 8, F32>), grid, dim3(256), HASH_LDS, stream, a);
+  } else {
+    if (a.bits <= 4)
+      hipLaunchKernelGGL((socket_hash_kernel<64, 4, F32>), grid, dim3(256), HASH_LDS, stream, a);
+    else
+      hipLaunchKernelGGL((socket_hash_kernel<64, 8, F32>), grid, dim3(256), HASH_LDS, stream, a);
+  }
+}
+
+template <bool F32>
+void launch_prob_t(const attn_impl::SocketSelectArgs& a, hipStream_t stream) {
+  if (a.E == 128)
+    hipLaunchKernelGGL((socket_prob_kernel<128, F32>), dim3((unsigned)(a.N * a.Hq)), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((socket_prob_kernel<64, F32>), dim3((unsigned)(a.N * a.Hq)), dim3(256), 0, stream, a);
+}
+
 }  // namespace
 
 namespace attn_impl {
 
-hipError_t launch_socket_hash_bf16(const SocketHashArgs& a, hipStream_t stream) {
+hipError_t launch_socket_hash(const SocketHashArgs& a, hipStream_t stream) {
   const long long keys = (long long)a.N * a.Hkv * a.S;
   if (keys == 0) return hipSuccess;
   const dim3 grid((unsigned)((keys + 255) / 256));
-  if (a.E == 128) {
-    if (a.bits <= 4)
-      hipLaunchKernelGGL((socket_hash_kernel<128, 4>), grid, dim3(256), HASH_LDS, stream, a);
-    else
-      hipLaunchKernelGGL((socket_hash_kernel<128, 8>), grid, dim3(256), HASH_LDS, stream, a);
-  } else {
-    if (a.bits <= 4)
-      hipLaunchKernelGGL((socket_hash_kernel<64, 4>), grid, dim3(256), HASH_LDS, stream, a);
-    else
-      hipLaunchKernelGGL((socket_hash_kernel<64, 8>), grid, dim3(256), HASH_LDS, stream, a);
-  }
+  if (a.f32)
+    launch_hash_t<true>(a, grid, stream);
+  else
+    launch_hash_t<false>(a, grid, stream);
   return hipGetLastError();
 }
 
-hipError_t launch_socket_select_bf16(const SocketSelectArgs& a, hipStream_t stream) {
-  if (a.E == 128)
-    hipLaunchKernelGGL((socket_prob_kernel<128>), dim3((unsigned)(a.N * a.Hq)), dim3(256), 0, stream, a);
+hipError_t launch_socket_select(const SocketSelectArgs& a, hipStream_t stream) {
+  if (a.f32)
+    launch_prob_t<true>(a, stream);
   else
-    hipLaunchKernelGGL((socket_prob_kernel<64>), dim3((unsigned)(a.N * a.Hq)), dim3(256), 0, stream, a);
+    launch_prob_t<false>(a, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int G = a.Hq / a.Hkv;

@@ -103,9 +103,11 @@ def check_socket_heads(w: Workload, inp: gen.Inputs, top_k: int, sc_ref, sel_ref
     is unique (no other key within that band) it must equal the oracle's.  Several
     selections are correct only when scores tie within the band; for every head, unique or
     not, the output must then be exact attention (oracle) over the keys the GPU chose,
-    within 2e-2 (O) / 1e-3 (LSE), and for unique heads the oracle's own sparse output too.
+    within the element type's O bar (2e-2 bf16, 1e-4 fp32) and 1e-3 on the LSE, and for
+    unique heads the oracle's own sparse output too.
     """
     G = w.Hq // w.Hkv
+    tol_o = TOL_O[w.dtype]
     unique = 0
     heads = heads if heads is not None else [(n, h) for n in range(w.N) for h in range(w.Hq)]
     for n, h in heads:
@@ -121,8 +123,8 @@ def check_socket_heads(w: Workload, inp: gen.Inputs, top_k: int, sc_ref, sel_ref
         if np.sum(sc >= lo) == top_k:  # the top-k set is unique
             unique += 1
             assert np.array_equal(sg[n, h], sel_ref[n, h]), f"head {(n, h)}: selection differs"
-            assert np.max(np.abs(og[n, h] - o_ref[n, h])) <= 2e-2
-            assert abs(lg[n, h, 0] - l_ref[n, h, 0]) <= 1e-3
+            assert np.max(np.abs(og[n, h] - o_ref[n, h])) <= tol_o
+            assert abs(lg[n, h, 0] - l_ref[n, h, 0]) <= TOL_LSE
         kh = h // G
         idx = np.asarray(sg[n, h], dtype=np.int64)
         kk = np.ascontiguousarray(inp.k[n:n + 1, kh:kh + 1, idx])
@@ -132,5 +134,6 @@ def check_socket_heads(w: Workload, inp: gen.Inputs, top_k: int, sc_ref, sel_ref
                                    scale=w.scale, gamma=w.gamma, sink=sk_h)
         eo = float(np.max(np.abs(og[n, h] - o_sel[0, 0])))
         el = float(abs(lg[n, h, 0] - l_sel[0, 0, 0]))
-        assert eo <= 2e-2 and el <= 1e-3, f"head {(n, h)}: attention over the chosen keys off by {eo:.3e} / {el:.3e}"
+        assert eo <= tol_o and el <= TOL_LSE, \
+            f"head {(n, h)}: attention over the chosen keys off by {eo:.3e} / {el:.3e}"
     return unique

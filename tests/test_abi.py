@@ -157,7 +157,7 @@ def bwd(lib, dt=0, N=1, Hq=4, Hkv=2, L=8, S=8, E=64, q=A, k=A, v=A, o=A, lse=A, 
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dt=1), -4),
+    (dict(dt=5), -3),
     (dict(E=96), -4),
     (dict(window=3, causal=0), -4),
     (dict(Hq=3), -2),
@@ -278,7 +278,7 @@ def sdecs(lib, dt=0, N=1, Hq=4, Hkv=2, S=64, E=64, tables=4, bits=4, tau=0.5, to
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dt=1), -4),
+    (dict(dt=5), -3),
     (dict(E=96), -4),
     (dict(bits=9), -8),
     (dict(bits=0), -8),
@@ -291,7 +291,7 @@ def test_socket_hash_rejects(lib, kw, code):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dt=1), -4),
+    (dict(dt=5), -3),
     (dict(top_k=0), -8),
     (dict(top_k=65), -8),
     (dict(tau=0.0), -8),
