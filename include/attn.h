@@ -142,7 +142,8 @@ int attn_fwd_biased(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E,
  *   dsink     Hq float32 values, or NULL; 0 when sink is NULL
  *   workspace device scratch of attn_bwd_workspace_bytes(N, Hq, L) bytes,
  *             16-byte aligned, caller-owned; contents on entry do not matter
- * bf16 only (ATTN_ERR_UNSUPPORTED for f32).  Results are deterministic (no
+ * bf16 (P and dS rounded to bf16 as MFMA operands, as P in attn_fwd) or f32
+ * (fp32 throughout, on the vector ALUs).  Results are deterministic (no
  * atomics).  The general bias of attn_fwd_biased has no backward here.
  */
 int attn_bwd(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E,

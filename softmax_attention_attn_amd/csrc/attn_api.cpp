@@ -242,7 +242,6 @@ int attn_bwd(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, const v
              size_t workspace_bytes, void* stream) {
   int rc = check_args(dt, N, Hq, Hkv, L, S, E, q, k, v, mode, scale, gamma, causal, window, n_reg, sink, o, lse);
   if (rc != ATTN_OK) return rc;
-  if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "the backward pass is implemented for bf16 only");
   if ((long long)N * Hq * L == 0 && (long long)N * Hkv * S == 0) return ok();
   if ((long long)N * Hq * L == 0 || (long long)N * Hkv * S == 0)
     return fail(ATTN_ERR_UNSUPPORTED, "backward with an empty query or key side (L=%d, S=%d)", L, S);
@@ -254,7 +253,7 @@ int attn_bwd(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, const v
   if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
   if (workspace_bytes < need) return fail(ATTN_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, need);
   if (!aligned(workspace, 16)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
-  if (((long long)S + 64) * E * 2 > 0x7fffffffLL || ((long long)L + 64) * E * 2 > 0x7fffffffLL)
+  if (dt == ATTN_BF16 && (((long long)S + 64) * E * 2 > 0x7fffffffLL || ((long long)L + 64) * E * 2 > 0x7fffffffLL))
     return fail(ATTN_ERR_UNSUPPORTED, "a (batch, head) slice near or above 2 GiB (L=%d, S=%d, E=%d)", L, S, E);
   if ((long long)((L + 127) / 128) * N * Hq > kMaxGrid || (long long)((S + 127) / 128) * N * Hkv > kMaxGrid ||
       (long long)N * Hq > 65535LL)
@@ -269,7 +268,9 @@ int attn_bwd(attn_dtype dt, int N, int Hq, int Hkv, int L, int S, int E, const v
   a.dv = dv;
   a.dsink = dsink;
   a.workspace = static_cast<float*>(workspace);
-  return hip_status(attn_impl::launch_backward_bf16(a, static_cast<hipStream_t>(stream)), "attn_bwd launch");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(dt == ATTN_BF16 ? attn_impl::launch_backward_bf16(a, st) : attn_impl::launch_backward_f32(a, st),
+                    "attn_bwd launch");
 }
 
 // ----------------------------------------------------------------------------- SOCKET

@@ -81,6 +81,8 @@ struct BwdArgs {
   float* workspace;
 };
 hipError_t launch_backward_bf16(const BwdArgs& a, hipStream_t stream);
+// fp32 inputs: the same gradients, workspace layout and conventions on the vector ALUs.
+hipError_t launch_backward_f32(const BwdArgs& a, hipStream_t stream);
 size_t backward_workspace_bytes(int N, int Hq, int L);
 
 // SOCKET soft-LSH sparse decode (socket_bf16.hip).
