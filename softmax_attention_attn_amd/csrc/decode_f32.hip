@@ -6,16 +6,19 @@
 // writes, per query head, the running max (log2 units), the running sum and
 // the unnormalised output; decode_f32_combine merges the splits with
 // log-sum-exp weights and adds the sink logit ("Attention Sink" section 4.2).
-// The arithmetic is fp32 throughout (no operand is rounded), so the products
-// run on the vector ALUs: a key row is spread over R = E/4 lanes, 16 bytes
-// each; every lane forms the partial dot products of its 4 dims with the
-// group's query heads and a butterfly over the R lanes (DPP row operations,
-// then v_permlane16_swap at E = 128) completes them.  Each R-lane row group
-// keeps its own online-softmax state (running max and sum, 4 output dims per
-// query head; "SDPA란 무엇인가?" section 2) over the keys it takes, and the row
-// groups of the 4 waves are merged through LDS at the end.  Decode is bound by
-// the K/V bytes (SOCKET summary, problem statement), which are read once, with
-// the non-temporal hint.
+// The arithmetic is fp32 throughout (no operand is rounded).  With one or two
+// query heads per kv head (and in indexed mode) the products run on the vector
+// ALUs: a key row is spread over R = E/4 lanes, 16 bytes each; every lane
+// forms the partial dot products of its 4 dims with the group's query heads
+// and a butterfly over the R lanes (DPP row operations, then
+// v_permlane16_swap at E = 128) completes them.  Each R-lane row group keeps
+// its own online-softmax state (running max and sum, 4 output dims per query
+// head; "SDPA란 무엇인가?" section 2) over the keys it takes, and the row
+// groups of the 4 waves are merged through LDS at the end.  With more heads
+// that per-head work would bound the kernel, so the products run on
+// v_mfma_f32_16x16x4_f32 instead (decode_split_f32_mfma_kernel).  Decode is
+// bound by the K/V bytes (SOCKET summary, problem statement), which are read
+// once, with the non-temporal hint.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -200,6 +203,180 @@ __global__ __launch_bounds__(NT, 2) void decode_split_f32_kernel(DecodeF32Params
   }
 }
 
+// GQA groups of more than two query heads: the same split, partials and merge
+// with the products on v_mfma_f32_16x16x4_f32 (fp32 operands, fp32
+// accumulation), so the per-head cross-lane sums of the kernel above go away.
+// A wave step is 16 keys x 16 query slots (the group's heads, padded):
+//   S^T = K Q^T: E/4 MFMAs; lane (l16, g) holds, for every 16-dim chunk c of a
+//     row, dims 16c + 4g .. +3 of key l16 (A) and of query slot l16 (B), so one
+//     load takes 64 contiguous bytes of each of 16 key rows;
+//   O^T += V^T P^T: 4 x E/16 MFMAs; lane (l16, g) holds dims 64u + 4 l16 .. +3
+//     (u < E/64) of keys 4g .. 4g+3 (A: 256 contiguous bytes of each of 4 rows
+//     per load) and the weights of those keys for slot l16 (B: its own scores).
+// Accumulator element r of the scores is key 4g + r for slot l16; element r of
+// output block b = 4u + i is dim 64u + 4(4g + r) + i of slot l16.  The 4 waves take
+// every 4th step, step st + 4 requested while step st is computed.
+template <int E, bool RBF>
+__global__ __launch_bounds__(NT, 2) void decode_split_f32_mfma_kernel(DecodeF32Params p) {
+  constexpr int QC = E / 16;  // 16-dim chunks of a row
+  constexpr int VB = E / 16;  // value dims per lane per key, and output blocks
+  constexpr int KST = 16;     // keys per wave step
+  __shared__ float sM[NWAVE][16];
+  __shared__ float sL[NWAVE][64];
+  __shared__ __attribute__((aligned(16))) float sO[NWAVE][16][E];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int split = blockIdx.x;
+  const int n = blockIdx.z;
+  const int G = p.Hq / p.Hkv;
+  const int kvh = blockIdx.y / p.qgroups;
+  const int qg = blockIdx.y % p.qgroups;
+  const int hbase = kvh * G + qg * 16;
+  const int nslots = min(16, G - qg * 16);
+  const bool qvalid = l16 < nslots;
+
+  f32x4 qf[QC];
+  {
+    const float* qrow = p.q + ((size_t)n * p.Hq + hbase + (qvalid ? l16 : 0)) * E;
+#pragma unroll
+    for (int c = 0; c < QC; ++c) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(qrow + 16 * c + 4 * g);
+      qf[c] = qvalid ? x : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  const size_t kvoff = ((size_t)n * p.Hkv + kvh) * (size_t)p.kv_rows * E;
+  const float* kbase = p.k + kvoff;
+  const float* vbase = p.v + kvoff;
+  const int v0 = split * p.chunk;
+  const int v1 = min(v0 + p.chunk, p.nkeys);
+  const int steps = v1 > v0 ? (v1 - v0 + KST - 1) / KST : 0;
+  auto key_row = [&](int vidx) { return vidx < p.n_reg ? vidx : vidx + p.first_real; };
+
+  float m = kNegInf, lsum = 0.f;
+  f32x4 acc[VB];
+#pragma unroll
+  for (int b = 0; b < VB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Keys past v1 read row v0 (in bounds) and are masked.
+  auto load = [&](int st, f32x4 (&kr)[QC], f32x4 (&vr)[4][VB / 4]) {
+    const int vb = v0 + st * KST;
+    {
+      const int vk = vb + l16;
+      const float* row = kbase + (size_t)key_row(vk < v1 ? vk : v0) * E;
+#pragma unroll
+      for (int c = 0; c < QC; ++c)
+        kr[c] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 16 * c + 4 * g));
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int vk = vb + 4 * g + r;
+      const float* row = vbase + (size_t)key_row(vk < v1 ? vk : v0) * E + 4 * l16;
+#pragma unroll
+      for (int u = 0; u < VB / 4; ++u) vr[r][u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 64 * u));
+    }
+  };
+
+  auto compute = [&](int st, const f32x4 (&kr)[QC], const f32x4 (&vr)[4][VB / 4]) {
+    const int vb = v0 + st * KST;
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < QC; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[c][i], qf[c][i], sc, 0, 0, 0);
+    float nk = 0.f;
+    if (RBF) {  // |k|^2 of key l16 (its four quarters sit in lanes l16 + 16g), then of keys 4g + r
+#pragma unroll
+      for (int c = 0; c < QC; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nk = __builtin_fmaf(kr[c][i], kr[c][i], nk);
+      nk = pair32_sum(pair16_sum(nk));
+    }
+    float x[4];
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float xv = sc[r] * p.c_logit;
+      if (RBF) xv = __builtin_fmaf(p.c_bias, __shfl(nk, 4 * g + r, 64), xv);
+      if (vb + 4 * g + r >= v1) xv = kNegInf;
+      x[r] = xv;
+      mx = fmaxf(mx, xv);
+    }
+    mx = pair32_max(pair16_max(mx));  // over the step's 16 keys, for slot l16
+    const float m_new = fmaxf(m, mx);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    if (__any(m_new > m)) {  // the running max moved for some slot: rescale
+      const float alpha = exp2f(m - m_use);
+      lsum *= alpha;
+#pragma unroll
+      for (int b = 0; b < VB; ++b) acc[b] *= alpha;
+    }
+    m = m_new;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x[r] = exp2f(x[r] - m_use);
+      lsum += x[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int b = 0; b < VB; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[r][b >> 2][b & 3], x[r], acc[b], 0, 0, 0);
+  };
+
+  if (steps > 0) {
+    f32x4 kA[QC], vA[4][VB / 4];
+    int st = wave;
+    load(st, kA, vA);
+    for (; st < steps; st += NWAVE) {
+      f32x4 kB[QC], vB[4][VB / 4];
+      load(st + NWAVE, kB, vB);
+      compute(st, kA, vA);
+#pragma unroll
+      for (int c = 0; c < QC; ++c) kA[c] = kB[c];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int u = 0; u < VB / 4; ++u) vA[r][u] = vB[r][u];
+    }
+  }
+
+  // Merge the 4 waves: running max per slot, sums per lane, outputs per (slot, dim).
+  if (g == 0) sM[wave][l16] = m;
+  sL[wave][lane] = lsum;
+#pragma unroll
+  for (int b = 0; b < VB; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sO[wave][l16][64 * (b >> 2) + 4 * (4 * g + r) + (b & 3)] = acc[b][r];
+  __syncthreads();
+  const size_t part_base = ((size_t)n * p.Hq + hbase) * p.num_splits + split;
+  for (int idx = tid; idx < nslots * E; idx += NT) {
+    const int sl = idx / E, e = idx % E;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, sM[w][sl]);
+    const float Mu = (M == kNegInf) ? 0.f : M;
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) o += exp2f(sM[w][sl] - Mu) * sO[w][sl][e];
+    const size_t pi = part_base + (size_t)sl * p.num_splits;
+    p.part_o[pi * E + e] = o;
+    if (e == 0) {
+      float lt = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWAVE; ++w) {
+        const float lw = (sL[w][sl] + sL[w][sl + 16]) + (sL[w][sl + 32] + sL[w][sl + 48]);
+        lt += exp2f(sM[w][sl] - Mu) * lw;
+      }
+      p.part_ml[pi * 2 + 0] = M;
+      p.part_ml[pi * 2 + 1] = lt;
+    }
+  }
+}
+
 struct CombineF32Params {
   const float* q;
   const float* part_o;
@@ -290,13 +467,23 @@ hipError_t launch_t(const DecodeF32Params& p, const CombineF32Params& c, int N, 
 }
 
 template <int E, bool RBF>
+hipError_t launch_mfma(const DecodeF32Params& p, const CombineF32Params& c, int N, hipStream_t stream) {
+  dim3 grid((unsigned)p.num_splits, (unsigned)(p.Hkv * p.qgroups), (unsigned)N);
+  hipLaunchKernelGGL((decode_split_f32_mfma_kernel<E, RBF>), grid, dim3(NT), 0, stream, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((decode_f32_combine<E>), dim3((unsigned)(N * p.Hq)), dim3(E), 0, stream, c);
+  return hipGetLastError();
+}
+
+// One or two heads per kv head: the vector-ALU kernel streams at the HBM rate;
+// more: the MFMA kernel (the vector one becomes bound by its per-head work).
+template <int E, bool RBF>
 hipError_t launch_ns(const DecodeF32Params& p, const CombineF32Params& c, int N, int G, hipStream_t stream) {
   if (p.key_index) return launch_t<E, RBF, 1, true>(p, c, N, stream);
   if (G <= 1) return launch_t<E, RBF, 1>(p, c, N, stream);
   if (G <= 2) return launch_t<E, RBF, 2>(p, c, N, stream);
-  if (G <= 4) return launch_t<E, RBF, 4>(p, c, N, stream);
-  if (G <= 8) return launch_t<E, RBF, 8>(p, c, N, stream);
-  return launch_t<E, RBF, 16>(p, c, N, stream);
+  return launch_mfma<E, RBF>(p, c, N, stream);
 }
 
 }  // namespace

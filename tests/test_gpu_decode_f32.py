@@ -1,10 +1,11 @@
 """GPU parity of the float32 split-K decode (attn_decode, attn_stream_decode with
 dt = f32) against the fp64 oracle.
 
-The fp32 decode keeps every operand in fp32 (products on the vector ALUs), so
-it is held to the fp32 bars: max-abs error 1e-4 on O and 1e-3 on the LSE.
-Cases cover each query-slot width of the kernel (GQA group sizes 1, 2, 3, 5,
-16 and 20, the last over two query groups), both head dimensions, both score
+The fp32 decode keeps every operand in fp32 (products on the vector ALUs for
+one or two query heads per kv head, on fp32 MFMA for more), so it is held to
+the fp32 bars: max-abs error 1e-4 on O and 1e-3 on the LSE.  Cases cover both
+kernels and each query-slot width (GQA group sizes 1, 2, 3, 5, 16 and 20, the
+last over two query groups), both head dimensions, both score
 modes, sinks, windows and register rows, forced split counts (one split, odd
 counts, more splits than keys so that some splits are empty), caches with no
 key at all, and the rolling cache.
@@ -42,6 +43,10 @@ CASES = [
     (D("f32_window_registers_sink_e128", Hq=4, Hkv=1, S=4000, E=128, window=700, n_reg=4, sink=True), [0, 2]),
     (D("f32_large_scale_e64", Hq=8, Hkv=4, S=1200, scale=1.5), [0, 3]),
     (D("f32_tiny_cache_more_splits_than_keys", Hq=4, Hkv=2, S=5, E=128), [0, 3, 16]),
+    # the MFMA kernel with the RBF fold over log-normal keys and registers, and with a large scale
+    (D("f32_gqa8_rbf_registers_lognormal_e64", Hq=16, Hkv=2, S=2500, mode="rbf", n_reg=5, k_dist="dir_lognormal"),
+     [0, 5]),
+    (D("f32_gqa4_large_scale_e128", N=2, Hq=8, Hkv=2, S=1700, E=128, scale=1.2, sink=True), [0, 3]),
 ]
 
 
