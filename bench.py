@@ -25,8 +25,9 @@ workload is warmed up for at least 200 ms before its K timed calls, so that no
 timing falls in the clock ramp of the first calls.  The long-context decode
 figure is repeated at top level under "decode" (the metric's second half).
 "probe_peaks" holds what this GPU sustains on a bf16 GEMM, a device copy and a
-read-only sum (vendor library work), and each roofline entry gives its fraction
-of the probe peak of its bound beside the fraction of the published one.
+read-only sum (vendor library work) and on the library's own streaming read and
+copy probes, and each roofline entry gives its fraction of the probe peak of
+its bound beside the fraction of the published one.
 
 Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits with a
 message.
@@ -180,12 +181,13 @@ def warm(call, warmup: int, torch):
     return i
 
 
-def probe_peaks(torch, n: int = 8192, nbytes: int = 1 << 30, device: str = "cuda:0"):
-    """What this GPU sustains on plain library work, beside the published peaks:
-    a bf16 GEMM 8192 x 8192 x 8192 (torch.matmul, i.e. the vendor BLAS) in
-    TFLOP/s, a 1 GiB device-to-device copy in GB/s (bytes read + written) and a
-    sum over 1 GiB of bf16 (bytes read).  Each is warmed up for WARM_MS, then
-    timed over back-to-back calls."""
+def probe_peaks(torch, attn, n: int = 8192, nbytes: int = 1 << 30, device: str = "cuda:0"):
+    """What this GPU sustains on plain work, beside the published peaks: a bf16
+    GEMM 8192 x 8192 x 8192 (torch.matmul, i.e. the vendor BLAS) in TFLOP/s; a
+    1 GiB device-to-device copy (torch) and a sum over 1 GiB of bf16 in GB/s;
+    and the library's own streaming read and copy of 1 GiB (attn_probe_read,
+    attn_probe_copy: the access pattern of the HBM-bound kernels).  Each is
+    warmed up for WARM_MS, then timed over back-to-back calls."""
     dev = torch.device(device)
     stream = torch.cuda.current_stream(dev)
     out = {}
@@ -220,18 +222,29 @@ def probe_peaks(torch, n: int = 8192, nbytes: int = 1 << 30, device: str = "cuda
     ms = rate_of(lambda: torch.sum(xs, dim=0, dtype=torch.float32, out=acc), 20)
     out["hbm_read"] = {"value": nb / (ms * 1e-3) / 1e9, "unit": "GB/s",
                        "what": f"torch.sum over {nb >> 20} MiB of bf16, bytes read", "ms": ms}
-    del src, xs, acc
+    del xs, acc
+    # The library's own probes: the 16-byte non-temporal access pattern of the
+    # HBM-bound kernels (include/attn_probe.h).
+    sink = attn.probe_read(src)
+    ms = rate_of(lambda: attn.probe_read(src, sink=sink), 20)
+    out["hbm_read_kernel"] = {"value": nb / (ms * 1e-3) / 1e9, "unit": "GB/s",
+                              "what": f"attn_probe_read over {nb >> 20} MiB, bytes read", "ms": ms}
+    dst = torch.empty_like(src)
+    ms = rate_of(lambda: attn.probe_copy(src, dst), 20)
+    out["hbm_copy_kernel"] = {"value": 2.0 * nb / (ms * 1e-3) / 1e9, "unit": "GB/s",
+                              "what": f"attn_probe_copy of {nb >> 20} MiB, bytes read + written", "ms": ms}
+    del src, dst, sink
     torch.cuda.empty_cache()
     return out
 
 
 def attach_probe(entry: dict, probes) -> None:
     """Adds the probe peak of the entry's bound and the fraction of it reached (for
-    HBM the better of the copy and the read-only sum)."""
+    HBM the best of the device copies and streaming reads)."""
     if not probes:
         return
-    hbm = max((p for p in (probes.get("hbm_copy"), probes.get("hbm_read")) if p), key=lambda p: p["value"],
-              default=None)
+    hbm = max((p for p in (probes.get(k) for k in ("hbm_copy", "hbm_read", "hbm_read_kernel", "hbm_copy_kernel"))
+               if p), key=lambda p: p["value"], default=None)
     p = {"mfma": probes.get("bf16_gemm"), "hbm": hbm}.get(entry.get("bound"))
     if p is None or p["unit"] != entry.get("unit"):
         return
@@ -554,7 +567,7 @@ def main() -> int:
     probes = None
     if not args.no_probe:
         log("[bench] probe peaks: bf16 GEMM and device copy")
-        probes = probe_peaks(torch)
+        probes = probe_peaks(torch, attn)
         result["probe_peaks"] = probes
         attach_probe(result["roofline"], probes)
     if not args.no_cpu_baseline:

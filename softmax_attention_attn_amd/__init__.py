@@ -37,7 +37,8 @@ EXPORTS = ("attn_fwd", "attn_fwd_biased", "attn_bwd", "attn_bwd_workspace_bytes"
            "attn_decode_noalloc",
            "attn_stream_append", "attn_stream_decode", "attn_stream_decode_workspace_bytes",
            "attn_socket_hash", "attn_socket_code_bytes", "attn_socket_decode", "attn_socket_decode_workspace_bytes",
-           "attn_status_string", "attn_last_error")
+           "attn_status_string", "attn_last_error",
+           "attn_probe_sink_words", "attn_probe_read", "attn_probe_copy")
 
 
 class AttnError(RuntimeError):
@@ -94,6 +95,12 @@ def load() -> ctypes.CDLL:
         lib.attn_status_string.argtypes = [I]
         lib.attn_last_error.restype = ctypes.c_char_p
         lib.attn_last_error.argtypes = []
+        lib.attn_probe_sink_words.restype = Z
+        lib.attn_probe_sink_words.argtypes = [Z]
+        lib.attn_probe_read.restype = I
+        lib.attn_probe_read.argtypes = [P, Z, P, P]
+        lib.attn_probe_copy.restype = I
+        lib.attn_probe_copy.argtypes = [P, P, Z, P]
         _lib = lib
     return _lib
 
@@ -462,3 +469,30 @@ def socket_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, proj: torch
                                 _stream(q.device, stream))
     _check(rc)
     return out, lse, sel
+
+
+# ----------------------------------------------------------------------------- bandwidth probes
+
+
+def _probe_buffer(name: str, t: torch.Tensor) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_contiguous() or t.device.type != _DEVICE_TYPE:
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    return t.numel() * t.element_size()
+
+
+def probe_read(src: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Stream src once through attn_probe_read (include/attn_probe.h); returns the sink words."""
+    nbytes = _probe_buffer("src", src)
+    lib = load()
+    if sink is None:
+        sink = torch.empty(max(int(lib.attn_probe_sink_words(nbytes)), 1), dtype=torch.int32, device=src.device)
+    _check(lib.attn_probe_read(_ptr(src), nbytes, _ptr(sink), _stream(src.device, stream)))
+    return sink
+
+
+def probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Copy src into dst (same byte size) through attn_probe_copy."""
+    nbytes = _probe_buffer("src", src)
+    if _probe_buffer("dst", dst) != nbytes or dst.device != src.device:
+        raise ValueError("dst must be a GPU tensor of src's byte size on src's device")
+    _check(load().attn_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(src.device, stream)))

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["attn_api.cpp", "prefill_bf16.hip", "prefill_bf16_band.hip", "prefill_f32.hip", "decode_bf16.hip", "decode_f32.hip", "stream_cache.hip", "backward_bf16.hip", "backward_f32.hip", "socket_bf16.hip"]
+SOURCES = ["attn_api.cpp", "prefill_bf16.hip", "prefill_bf16_band.hip", "prefill_f32.hip", "decode_bf16.hip", "decode_f32.hip", "stream_cache.hip", "backward_bf16.hip", "backward_f32.hip", "socket_bf16.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

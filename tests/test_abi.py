@@ -1,4 +1,5 @@
-"""The C ABI: library loads, exports what include/attn.h declares, and rejects
+"""The C ABI: library loads, exports what include/attn.h (and the bandwidth
+probes of include/attn_probe.h) declare, and rejects
 misuse before any HIP call (CPU only: every call here fails validation or has
 nothing to compute, so no GPU is touched)."""
 import ctypes
@@ -12,13 +13,13 @@ import torch
 import softmax_attention_attn_amd as attn
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "attn.h")
+HEADERS = [os.path.join(ROOT, "include", "attn.h"), os.path.join(ROOT, "include", "attn_probe.h")]
 
 A = 0x100000  # a 16-byte aligned fake device address; validation never dereferences it
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+[\s\*]+(attn_\w+)\s*\(", text, re.M)))
 
 
@@ -333,3 +334,16 @@ def test_decode_noalloc_rejects_before_any_hip_call(lib):
                                    0, None) == 0
     # the bytes the scratch holds, as the header states
     assert attn.DECODE_NOALLOC_SCRATCH_BYTES == 8 << 20
+
+
+def test_probes_reject_bad_arguments_before_any_hip_call(lib):
+    assert lib.attn_probe_read(A, 0, A, None) == 0  # nothing to do
+    assert lib.attn_probe_read(None, 64, A, None) == -1
+    assert lib.attn_probe_read(A + 4, 64, A, None) == -5
+    assert lib.attn_probe_read(A, 60, A, None) == -2
+    assert lib.attn_probe_copy(A, None, 64, None) == -1
+    assert lib.attn_probe_copy(A, A + 8, 64, None) == -5
+    assert lib.attn_probe_copy(A, A + 4096, 100, None) == -2
+    # one word per wave of the grid: 4 per 256-thread workgroup, at most 4096 workgroups
+    assert lib.attn_probe_sink_words(16 * 256) == 4
+    assert lib.attn_probe_sink_words(1 << 30) == 4096 * 4

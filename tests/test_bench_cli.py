@@ -84,9 +84,12 @@ def test_probe_peaks_runs_on_small_sizes():
     shim.cuda = cuda
     saved = bench.WARM_MS
     bench.WARM_MS = 0.0
+    # the library's probes stand in as host-side no-ops (they need a GPU)
+    probes = types.SimpleNamespace(probe_read=lambda src, sink=None: torch.zeros(4, dtype=torch.int32),
+                                   probe_copy=lambda src, dst: None)
     try:
-        out = bench.probe_peaks(shim, n=32, nbytes=1 << 16, device="cpu")
+        out = bench.probe_peaks(shim, probes, n=32, nbytes=1 << 16, device="cpu")
     finally:
         bench.WARM_MS = saved
-    assert set(out) == {"bf16_gemm", "hbm_copy", "hbm_read"}
+    assert set(out) == {"bf16_gemm", "hbm_copy", "hbm_read", "hbm_read_kernel", "hbm_copy_kernel"}
     assert all(v["value"] > 0 for v in out.values())
