@@ -43,7 +43,9 @@
 // moves lazily: the accumulator is rescaled only when a row max grows by more
 // than 2^8 over the reference (O = acc / l does not depend on the reference;
 // it only bounds p by 256).  With a positive scale the dot-mode max is taken on
-// the raw scores and each weight costs one fma + exp2.  In folded RBF mode no
+// the raw scores and each weight costs one fma + exp2; the tile max itself is
+// skipped when each lane's sum of weights formed against the current reference
+// shows that no weight exceeds 256.  In folded RBF mode no
 // logit of a row exceeds c|q|^2/2, and the tile max is skipped once the
 // reference is within 2^16 of that bound.  Row sums are compensated (Kahan)
 // where a register allows it.
@@ -61,6 +63,7 @@ namespace {
 constexpr int BM = 128;  // query rows per workgroup
 constexpr int NT = 256;  // threads per workgroup
 constexpr float kLazy = 8.f;  // rescale when a row max grows by more than this (log2 units)
+constexpr float kSumCap = 256.f;  // 2^kLazy: bound on a lane's weight sum that needs no tile max
 constexpr float kLazyBound = 16.f;  // RBF: skip the tile max once the reference is this close to the bound
 
 struct PrefillParams {
@@ -148,6 +151,9 @@ void prefill_bf16_kernel(PrefillParams p) {
   constexpr bool RBF = MODE == kRbf || MODE == kRbfFold;  // K staged through registers, |k|^2 on chip
   constexpr bool FOLD = MODE == kRbfFold;
   constexpr bool FAST = MODE == kDotPos || FOLD;
+  // Dot mode with a positive scale: weights against the current reference first,
+  // the tile max only when their sums say the reference must move.
+  constexpr bool SUMCHK = MODE == kDotPos;
   static_assert(UB == kBiasNone || !FAST, "a user bias needs the logits formed before the max");
   constexpr int BN = TileShape<E, MODE, UB>::kKeys;  // keys per staged tile
   // Epilogue O staging: padded rows, or (32-key tiles, where padded rows of two
@@ -447,8 +453,15 @@ void prefill_bf16_kernel(PrefillParams p) {
     }
 
     // S^T = K * Q^T for NB blocks of 32 keys; the NB accumulation chains are
-    // interleaved so that consecutive MFMAs never depend on each other.
+    // interleaved so that consecutive MFMAs never depend on each other.  The
+    // scores are then made logits (unless FAST) and masked; a second pass forms
+    // them again, from the same K tile, when the sum-checked weights of SUMCHK
+    // fail their check.
     f32x16 st[NB];
+    float ps = -0.f;  // (-0 + x == x: the first addition folds away)
+    bool general = true;
+#pragma unroll
+    for (int pass = 0; pass < (SUMCHK ? 2 : 1); ++pass) {
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -515,6 +528,31 @@ void prefill_bf16_kernel(PrefillParams p) {
           st[b][r] = vis ? st[b][r] : kNegInf;
         }
     }
+
+    // SUMCHK: once every row of the wave has a reference, the weights are formed
+    // against it without the tile max.  A lane's sum of its 16 (or 32) weights
+    // bounds each of them, so a sum at most 2^kLazy shows that no weight passed
+    // 2^kLazy: the bound the lazy rule below keeps, met without moving the
+    // reference.  Otherwise (rare: the row max jumped, or many weights near the
+    // reference) the scores are formed again and go the general way.
+    if (SUMCHK && pass == 0 && !__any(m == kNegInf)) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = fast_exp2(__builtin_fmaf(st[b][r], p.c_logit, negm));
+          st[b][r] = pv;
+          ps += pv;
+        }
+      general = __any(!(ps <= kSumCap));
+      if (general) {
+        ps = -0.f;
+        continue;
+      }
+    }
+    break;
+    }
+    if (general) {
     // RBF: no logit of this row exceeds qbound (the logit of a key equal to q),
     // so once every row's reference is within kLazyBound of it no weight can
     // pass 2^kLazyBound and the tile's max is not needed.
@@ -546,7 +584,6 @@ void prefill_bf16_kernel(PrefillParams p) {
     }
     }
 
-    float ps = -0.f;  // (-0 + x == x: the first addition folds away)
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -556,6 +593,7 @@ void prefill_bf16_kernel(PrefillParams p) {
         st[b][r] = pv;
         ps += pv;
       }
+    }
     if (KSUM) {
       const float y = ps - lcomp;
       const float t = lsum + y;

@@ -151,6 +151,34 @@ def test_decode_small(w, splits):
         check(w, inp, o, lse)
 
 
+@pytest.mark.parametrize("E", [64, 128])
+def test_prefill_constructed_logit_jumps(E):
+    """Logits laid out per key so that every way out of the dot-mode weight check is
+    taken: a run of keys about 6 log2 units above the first keys (weight sums of a tile
+    past 2^8 while no row max passes the reference by more than 8: no rescale), one
+    key 150 units up (weights against the old reference overflow: scores formed again,
+    reference moved), then a ramp rising from there by 0.2 units per key (6.4 per
+    32-key tile: weight sums fail the check on most tiles, the reference moves on some).  q_i = u + noise, k_j = a_j u + noise, a_j set from the target logit."""
+    w = W(f"dot_logit_jumps_e{E}", Hq=2, Hkv=1, L=600, S_real=600, E=E, scale=0.9 / np.sqrt(E))
+    inp = gen.generate(w)
+    r = np.random.default_rng(5)
+    u = np.where(r.random(E) < 0.5, -1.0, 1.0).astype(np.float32)
+    c = w.scale * np.log2(np.e) * float(u @ u)  # log2-unit logit per unit of a_j for q = u
+    t = np.zeros(w.S_real)
+    t[96:200] = 6.0
+    t[333] = 150.0
+    t[334:] = 150.0 + 0.2 * np.arange(1, w.S_real - 333)
+    a = (t / c).astype(np.float32)
+    q = u[None, None, None, :] + 0.05 * r.standard_normal((1, w.Hq, w.L, E)).astype(np.float32)
+    k = a[None, None, :, None] * u + 0.05 * r.standard_normal((1, 1, w.S_real, E)).astype(np.float32)
+    inp.q = gen.bf16_bits_from_f32(q)
+    inp.k = gen.bf16_bits_from_f32(k)
+    qd, kd, vd, sink = to_device(inp)
+    o, lse = run_gpu(w, qd, kd, vd, sink)
+    torch.cuda.synchronize()
+    check(w, inp, o, lse)
+
+
 def test_decode_matches_prefill_single_query():
     w = W("dec_vs_prefill", N=2, Hq=8, Hkv=2, L=1, S_real=2000, E=128, sink=True, decode=True)
     inp = gen.generate(w)
