@@ -158,7 +158,8 @@ def test_prefill_constructed_logit_jumps(E):
     past 2^8 while no row max passes the reference by more than 8: no rescale), one
     key 150 units up (weights against the old reference overflow: scores formed again,
     reference moved), then a ramp rising from there by 0.2 units per key (6.4 per
-    32-key tile: weight sums fail the check on most tiles, the reference moves on some).  q_i = u + noise, k_j = a_j u + noise, a_j set from the target logit."""
+    32-key tile: weight sums fail the check on most tiles, the reference moves on some).
+    q_i = u + noise, k_j = a_j u + noise, a_j set from the target logit."""
     w = W(f"dot_logit_jumps_e{E}", Hq=2, Hkv=1, L=600, S_real=600, E=E, scale=0.9 / np.sqrt(E))
     inp = gen.generate(w)
     r = np.random.default_rng(5)
