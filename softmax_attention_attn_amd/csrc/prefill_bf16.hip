@@ -119,7 +119,8 @@ __device__ __forceinline__ void map_block(int bid, const PrefillParams& p, int& 
 //   kDotAny:  dot mode, any finite scale -- x = c*s first;
 //   kRbf:     x = c*s + bias_k with bias_k = -gamma*log2(e)*|k|^2 from the staged tile;
 //   kRbfFold: RBF with gamma > 0 -- the key term goes into the matrix product instead:
-//             one more 16-wide K step whose A operand holds -|k|^2/2 split into three
+//             one more K step (a 32x32x8 MFMA, half the K width of the others: the
+//             three terms fit one 4-wide K group) whose A operand holds -|k|^2/2 split into three
 //             bf16 parts (hi + mid + lo, ~24 significant bits, summed exactly in the
 //             fp32 accumulator) against ones in Q^T, so s' = q.k - |k|^2/2 and the
 //             weights are formed as in kDotPos: exp2(fma(s', c, -m)), c = 2*gamma*log2(e).
@@ -213,9 +214,9 @@ void prefill_bf16_kernel(PrefillParams p) {
     if (RBF) qn2 += sumsq8(c);
   }
   if (RBF) qn2 = pair32_sum(qn2);
-  // kRbfFold: Q^T fragment of the extra K step, ones in K-dims 0..2 (lanes g = 0).
-  const u32x4 qone_w = (FOLD && g == 0) ? u32x4{0x3f803f80u, 0x00003f80u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
-  const bf16x8 qone = as_bf16x8(qone_w);
+  // kRbfFold: Q^T fragment of the extra K step (a 32x32x8 operand), bf16 ones in
+  // K-dims 0..2 (lanes g = 0).
+  const u32x2 qone = (FOLD && g == 0) ? u32x2{0x3f803f80u, 0x00003f80u} : u32x2{0u, 0u};
 
   // Running state in log2 units: m is the reference max, lsum this lane's share
   // of the row sum (its 16 keys per block); the halves are added at the end.
@@ -480,12 +481,15 @@ void prefill_bf16_kernel(PrefillParams p) {
     }
     if (FOLD) {
       // The extra K step: key row l32 of block b contributes its three parts of
-      // -|k|^2/2 in K-dims 0..2 (lanes g = 0), the query side ones there.
+      // -|k|^2/2 in K-dims 0..2 (lanes g = 0 hold K-dims 0..3 of the 32x32x8
+      // operands, lanes g = 1 K-dims 4..7), the query side ones there.
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const u32x2 kn = sKn[buf][32 * b + l32];
-        const u32x4 av = g == 0 ? u32x4{kn[0], kn[1], 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
-        st[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), qone, st[b], 0, 0, 0);
+        typedef short short4v __attribute__((ext_vector_type(4)));
+        const u32x2 av = g == 0 ? kn : u32x2{0u, 0u};
+        st[b] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(short4v, av),
+                                                          __builtin_bit_cast(short4v, qone), st[b], 0, 0, 0);
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -551,7 +555,7 @@ void prefill_bf16_kernel(PrefillParams p) {
       }
     }
     break;
-    }
+    }  // pass
     if (general) {
     // RBF: no logit of this row exceeds qbound (the logit of a key equal to q),
     // so once every row's reference is within kLazyBound of it no weight can
@@ -593,7 +597,7 @@ void prefill_bf16_kernel(PrefillParams p) {
         st[b][r] = pv;
         ps += pv;
       }
-    }
+    }  // general
     if (KSUM) {
       const float y = ps - lcomp;
       const float t = lsum + y;
