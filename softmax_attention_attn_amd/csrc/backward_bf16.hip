@@ -86,8 +86,33 @@ __global__ __launch_bounds__(64) void bwd_sink_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------- shared pieces
 
 // Logit frames (log2 units), as in the forward: dot x = c_logit*s; rbf
-// x = c_logit*s + c_bias*|k|^2 (the -gamma|q|^2 part is folded into mref).
+// x = c_logit*s + c_bias*|k|^2 = c_logit*(s - |k|^2/2) (c_bias = -c_logit/2; the
+// -gamma|q|^2 part is folded into mref).  In RBF mode both kernels add -|k|^2/2
+// to the scores inside the matrix product, as the forward does: one 32x32x8
+// MFMA per 32x32 block whose key-side operand holds -|k|^2/2 as three bf16
+// parts in K-dims 0..2 (lanes 0..31) against ones on the query side, so that a
+// logit costs one multiply by c_logit.
 enum { kDot = 0, kRbf = 1 };
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+// v as hi + mid + lo, each rounded to bf16 (nearest even) in turn (about 24
+// significant bits; the residuals are exact in fp32), packed as K-dims 0..3 of
+// a 32x32x8 bf16 operand: {hi | mid << 16, lo}.
+__device__ __forceinline__ u32x2 split3_bf16(float v) {
+  const __bf16 hi = (__bf16)v;
+  const float r1 = v - (float)hi;
+  const __bf16 mid = (__bf16)r1;
+  const __bf16 lo = (__bf16)(r1 - (float)mid);
+  const uint32_t h = __builtin_bit_cast(uint16_t, hi), m = __builtin_bit_cast(uint16_t, mid),
+                 l = __builtin_bit_cast(uint16_t, lo);
+  return u32x2{h | (m << 16), l};
+}
+
+// bf16 ones in K-dims 0..2 of a 32x32x8 operand (lanes 0..31; zero elsewhere).
+__device__ __forceinline__ u32x2 ones3_bf16(int g) {
+  return g == 0 ? u32x2{0x3f803f80u, 0x00003f80u} : u32x2{0u, 0u};
+}
 
 template <int E, int R = BT>
 struct TileGeom {
@@ -196,7 +221,7 @@ void bwd_dq_kernel(BwdParams p, int num_q_tiles) {
   // the reads of one buffer from the LDS-direct loads in flight into the other.
   __shared__ __attribute__((aligned(16))) uint8_t sKV0[2 * TILEB];
   __shared__ __attribute__((aligned(16))) uint8_t sKV1[2 * TILEB];
-  __shared__ __attribute__((aligned(16))) float sBias[2][BT];
+  __shared__ __attribute__((aligned(16))) u32x2 sKn[RBF ? 2 : 1][RBF ? BT : 1];  // RBF: -|k|^2/2 as 3 bf16
   auto k_tile = [&](int buf) { return buf ? sKV1 : sKV0; };
   auto v_tile = [&](int buf) { return (buf ? sKV1 : sKV0) + TILEB; };
 
@@ -215,6 +240,7 @@ void bwd_dq_kernel(BwdParams p, int num_q_tiles) {
   const int i0 = qt * BR;
   const int qa = i0 + wave * 32;
   const int qi = qa + l32;
+  const u32x2 qone = ones3_bf16(RBF ? g : 1);  // RBF: query side of the -|k|^2/2 fold
   const int qb = min(qa + 31, p.L - 1);
   const size_t row = (size_t)nh * p.L + min(qi, p.L - 1);
 
@@ -327,7 +353,7 @@ void bwd_dq_kernel(BwdParams p, int num_q_tiles) {
         const int rr = id / ECH, c = id % ECH;
         *reinterpret_cast<u32x4*>(k_tile(buf) + rr * ROWB + ((c ^ tile_swz<E>(rr)) * 16)) = kreg[i];
         const float ss = group_sum<ECH>(sumsq8(kreg[i]));
-        if (c == 0) sBias[buf][rr] = p.c_bias * ss;
+        if (c == 0) sKn[buf][rr] = split3_bf16(-0.5f * ss);
       }
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
@@ -371,6 +397,15 @@ void bwd_dq_kernel(BwdParams p, int num_q_tiles) {
         dp[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[b], gf[s], dp[b], 0, 0, 0);
       }
     }
+    if (RBF) {
+      // -|k|^2/2 of key row l32 of block b (lanes g = 0) against ones.
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const u32x2 kn = g == 0 ? sKn[buf][32 * b + l32] : u32x2{0u, 0u};
+        st[b] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(short4v, kn),
+                                                          __builtin_bit_cast(short4v, qone), st[b], 0, 0, 0);
+      }
+    }
     // Visible keys of this lane's row: one interval [lo, hi] of tile offsets.
     int lo = 0, hi = BT - 1;
     if (MASKED) {
@@ -391,8 +426,7 @@ void bwd_dq_kernel(BwdParams p, int num_q_tiles) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ko = 32 * b + 8 * (r >> 2) + (r & 3);
-        float x = st[b][r] * p.c_logit;
-        if (RBF) x += sBias[buf][ko + 4 * g];
+        const float x = st[b][r] * p.c_logit;
         const float pw = (!MASKED || ((ko >= lo) & (ko <= hi))) ? fast_exp2(x - mr) : 0.f;
         if (RBF) {
           const float pd = pw * dp[b][r];
@@ -559,7 +593,12 @@ void bwd_dkdv_kernel(BwdParams p, int num_k_tiles) {
       *reinterpret_cast<u32x4*>(sV + r * ROWB + ((c ^ tile_swz<E>(r)) * 16)) = x;
     }
   }
-  const float kbias = RBF ? p.c_bias * pair32_sum(nk2) : 0.f;
+  // RBF: this lane's key's -|k|^2/2 as the key-side operand of the fold (lanes g = 0).
+  // The halves' sum is a cross-lane exchange: every lane takes part, the lane
+  // test comes after it.
+  const u32x2 ksplit = split3_bf16(-0.5f * (RBF ? pair32_sum(nk2) : 0.f));
+  const u32x2 kfold = (RBF && g == 0) ? ksplit : u32x2{0u, 0u};
+  const u32x2 qone = ones3_bf16(RBF ? g : 1);
   float csum = 0.f;  // RBF: this lane's share of sum_i dS_ij
   f32x16 accv[EB], acck[EB];
 #pragma unroll
@@ -666,6 +705,9 @@ void bwd_dkdv_kernel(BwdParams p, int num_k_tiles) {
         s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[s], s_acc, 0, 0, 0);
         d_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vs, d_acc, 0, 0, 0);
       }
+      if (RBF)
+        s_acc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(short4v, qone),
+                                                          __builtin_bit_cast(short4v, kfold), s_acc, 0, 0, 0);
       // Register r holds query row ib + 8(r/4) + 4g + r%4 for this lane's key.
       const int lo = qlo - ib - 4 * g, hi = qhi - ib - 4 * g;
       f32x16 pw, ds;
@@ -677,7 +719,7 @@ void bwd_dkdv_kernel(BwdParams p, int num_k_tiles) {
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rq + e;
           const int ro = 8 * rq + e;
-          const float x = __builtin_fmaf(s_acc[r], p.c_logit, kbias);
+          const float x = s_acc[r] * p.c_logit;
           const float w = (!MASKED || ((ro >= lo) & (ro <= hi))) ? fast_exp2(x - m4[e]) : 0.f;
           pw[r] = w;
           ds[r] = w * (d_acc[r] - d4[e]);
